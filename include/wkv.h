@@ -1,0 +1,199 @@
+/*
+ * wkv.h — C ABI of the MI355X (gfx950) WKV time-mixing library (libwkv.so).
+ *
+ * The library computes the RWKV WKV recurrence in three forms:
+ *
+ *   v4  channel-wise exponential-decay weighted average with a bonus on the
+ *       current token, carried as a numerically stable running-max state
+ *       (a, b, p) per channel.  The call shape follows the RWKV-v4
+ *       walk-through page ("代码连连看——RWKV", RWKV_TimeMix.forward, the
+ *       RUN_CUDA(B, T, C, time_decay, time_first, k, v) call, whose result is
+ *       gated by sigmoid(r)).
+ *   v5  multi-head form with an N x N fp32 state per head and a static decay
+ *       per head-channel.
+ *   v6  the same with a per-token, per-channel decay.  Arguments follow the
+ *       rwkv_ops page ("rwkv6op 使用方法": r, k, v, w of shape
+ *       (batch, seq, hidden); u of shape (heads, head_size) or (hidden,);
+ *       init_state (n_state, heads, head_size, head_size); state_map int32
+ *       (batch,); y_state (batch, heads, head_size, head_size)).
+ *
+ * and a varlen entry point for batched serving where each slot consumes its
+ * own number of tokens per call and keeps its state on the device between
+ * calls (the web-rwkv page, batched inference section: slots of a model
+ * state, a per-call token budget `token_chunk_size`, empty slots skipped).
+ *
+ * Definitions (no page prints them; these are the standard RWKV-4/5/6
+ * recurrences).  Channel c = h*N + i; key index i (row of S), value index j
+ * (column of S).
+ *
+ *   v4:   lambda_c = -exp(time_decay[c]); with A = a*e^p, B = b*e^p
+ *         wkv_t = (A + e^(u_c + k_t) v_t) / (B + e^(u_c + k_t))
+ *         y_t   = sigmoid(r_t) * wkv_t  (r given)  or  wkv_t  (r == NULL)
+ *         A <- e^lambda_c A + e^(k_t) v_t ;  B <- e^lambda_c B + e^(k_t)
+ *   v5/v6: d_t[i] = exp(-exp(w_t[i]))   (w constant over t for v5)
+ *         y_t[j] = sum_i r_t[i] (S[i][j] + u[i] k_t[i] v_t[j])
+ *         S[i][j] <- d_t[i] S[i][j] + k_t[i] v_t[j]
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller, row-major
+ *     and contiguous, aligned to at least 16 bytes.  The library never
+ *     allocates, frees or copies caller memory between host and device.
+ *   - Token arrays are [B, T, C] (C = H*N, not head-first).  y is always fp32.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
+ *     and return before it completes.  Results are valid once the stream has
+ *     been synchronised.
+ *   - Errors are status codes; the library never aborts.  Host-checkable
+ *     problems return before anything is enqueued.  Data problems that only
+ *     the device can see set bits in *dev_status (if given) and skip the
+ *     affected unit of work.
+ *   - Functions are stateless and reentrant; identical inputs give bitwise
+ *     identical outputs (no floating-point atomics).
+ */
+#ifndef WKV_H
+#define WKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define WKV_API __attribute__((visibility("default")))
+#else
+#define WKV_API
+#endif
+
+typedef int32_t wkv_status;
+#define WKV_OK               0  /* success (work enqueued)                        */
+#define WKV_ERR_INVALID_ARG  1  /* bad dimension, NULL or misaligned pointer, ... */
+#define WKV_ERR_UNSUPPORTED  2  /* head size other than 64, unknown dtype / algo  */
+#define WKV_ERR_DEVICE       3  /* a HIP launch failed; see wkv_last_error()      */
+
+typedef int32_t wkv_dtype;
+#define WKV_F32   0             /* 32-bit IEEE float inputs                       */
+#define WKV_BF16  1             /* bfloat16 inputs (upper half of an fp32)        */
+
+typedef int32_t wkv_algo;
+#define WKV_ALGO_AUTO     0     /* library picks                                  */
+#define WKV_ALGO_SCAN     1     /* token-sequential scan on the vector ALUs       */
+#define WKV_ALGO_CHUNKED  2     /* 64-token chunks, contractions on MFMA          */
+
+/* Bits OR-ed into *dev_status by the device (never cleared by the library). */
+#define WKV_DEV_BAD_STATE_MAP  1  /* state_map entry outside [0, n_state)         */
+#define WKV_DEV_BAD_LENGTH     2  /* varlen length < 0 or > max_len               */
+#define WKV_DEV_TOKEN_OVERFLOW 4  /* varlen: sum of lengths exceeds total_tokens  */
+#define WKV_DEV_DUPLICATE_ROW  8  /* varlen: two slots map to the same state row  */
+#define WKV_DEV_DECAY_RANGE   16  /* chunked: a chunk's accumulated log-decay
+                                     exceeds the kernel's exponent range; that
+                                     head's outputs are not valid — rerun with
+                                     WKV_ALGO_SCAN                                */
+
+/*
+ * v4 forward (prefill over T tokens, or T = 1 decode).
+ *   time_decay [C] fp32   raw parameter; per-step decay exp(-exp(time_decay))
+ *   time_first [C] fp32   bonus u of the current token
+ *   k, v       [B,T,C]    in_dtype
+ *   r          [B,T,C]    in_dtype, optional: output gated by sigmoid(r)
+ *   y          [B,T,C]    fp32 output
+ *   state_in   [B,3,C]    fp32 planes (a, b, p), NULL = fresh sequence
+ *                         (a = b = 0, p = -1e38)
+ *   state_out  [B,3,C]    fp32 final state, NULL = not returned; may equal
+ *                         state_in (in place)
+ * T = 0 is a valid no-op (state_out, if given, receives state_in).
+ */
+WKV_API wkv_status wkv4_forward(int B, int T, int C,
+                        const float *time_decay, const float *time_first,
+                        const void *k, const void *v, const void *r,
+                        wkv_dtype in_dtype, float *y,
+                        const float *state_in, float *state_out,
+                        void *stream);
+
+/*
+ * v5 forward (static decay).
+ *   r, k, v    [B,T,H*N]  in_dtype
+ *   w          [H*N] fp32 raw decay parameter; decay exp(-exp(w))
+ *   u          [H*N] fp32 bonus
+ *   y          [B,T,H*N]  fp32 output
+ *   state_in   [n_state,H,N,N] fp32 or NULL (zero initial state)
+ *   state_map  [B] int32 or NULL: batch row b starts from
+ *              state_in[state_map[b]]; with NULL, n_state must be 1 (shared)
+ *              or B (one per row)
+ *   state_out  [B,H,N,N] fp32 or NULL; may equal state_in only when
+ *              state_map is NULL and n_state == B
+ *   dev_status int32 device word or NULL (WKV_DEV_* bits)
+ * N must be 64.
+ */
+WKV_API wkv_status wkv5_forward(int B, int T, int H, int N,
+                        const void *r, const void *k, const void *v,
+                        wkv_dtype in_dtype,
+                        const float *w, const float *u, float *y,
+                        const float *state_in, const int32_t *state_map, int n_state,
+                        float *state_out, wkv_algo algo, int32_t *dev_status,
+                        void *stream);
+
+/*
+ * v6 forward (per-token decay).  As wkv5_forward, except
+ *   w          [B,T,H*N]  in_dtype raw decay parameter per token and channel
+ */
+WKV_API wkv_status wkv6_forward(int B, int T, int H, int N,
+                        const void *r, const void *k, const void *v, const void *w,
+                        wkv_dtype in_dtype, const float *u, float *y,
+                        const float *state_in, const int32_t *state_map, int n_state,
+                        float *state_out, wkv_algo algo, int32_t *dev_status,
+                        void *stream);
+
+/*
+ * v6 varlen forward for batched serving.
+ *   lengths      [num_slots] int32 DEVICE: tokens slot s consumes this call
+ *                (0 = empty slot: no work, its state row is untouched, or
+ *                copied when state_out != state_in)
+ *   max_len      host upper bound on every length (a length above it is a
+ *                data error)
+ *   total_tokens number of packed token rows in r, k, v, w, y
+ *   r, k, v, w   [total_tokens, H*N] in_dtype; slot s owns rows
+ *                [off_s, off_s + lengths[s]), off = exclusive prefix sum
+ *   u            [H*N] fp32
+ *   y            [total_tokens, H*N] fp32 (rows past sum(lengths) untouched)
+ *   state_in     [n_state,H,N,N] fp32: slot s reads row state_map[s]
+ *   state_out    [n_state,H,N,N] fp32: slot s writes row state_map[s];
+ *                may equal state_in (the usual in-place serving loop)
+ *   state_map    [num_slots] int32 DEVICE or NULL (identity; then
+ *                n_state >= num_slots).  Entries must be distinct.
+ * N must be 64.
+ */
+WKV_API wkv_status wkv6_forward_varlen(int num_slots, int H, int N,
+                               const int32_t *lengths, int max_len, int total_tokens,
+                               const void *r, const void *k, const void *v, const void *w,
+                               wkv_dtype in_dtype, const float *u, float *y,
+                               const float *state_in, float *state_out,
+                               const int32_t *state_map, int n_state,
+                               int32_t *dev_status, void *stream);
+
+/*
+ * Host-side token-budget split for the varlen serving loop (HOST arrays).
+ * Hands one token at a time to every slot with tokens left, in slot order,
+ * until `budget` tokens are given out or no slot has tokens left.
+ *   remaining [num_slots] int32 >= 0   tokens each slot still has to consume
+ *   take      [num_slots] int32 output tokens each slot consumes this call
+ *   *total    receives sum(take)
+ */
+WKV_API wkv_status wkv_schedule_round_robin(int num_slots, const int32_t *remaining,
+                                    int budget, int32_t *take, int32_t *total);
+
+/* Algorithm WKV_ALGO_AUTO resolves to for a v5 (version 5) or v6 (version 6)
+ * call of this shape.  Pure host function. */
+WKV_API wkv_algo wkv_resolve_algo(int version, int B, int T, int H, int N, wkv_algo requested);
+
+WKV_API const char *wkv_status_string(wkv_status s);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+WKV_API const char *wkv_last_error(void);
+WKV_API int wkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV_H */

@@ -1,0 +1,207 @@
+"""MI355X (gfx950) RWKV WKV time-mixing kernels — thin PyTorch binding.
+
+Every function here only checks and marshals arguments (shapes, dtypes,
+device pointers, the current HIP stream) and calls the C ABI of libwkv.so
+(include/wkv.h).  All arithmetic runs in the library's HIP kernels; there is
+no CPU or PyTorch fallback, and importing the package fails if the library
+has not been built.
+
+Tensors are row-major and contiguous, token arrays [B, T, C] with C = H*N
+(varlen: packed [total_tokens, C]); inputs are torch.bfloat16 or
+torch.float32; outputs and states are float32.  Calls are asynchronous on
+torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native
+from ._native import (WKV_ALGO_AUTO, WKV_ALGO_CHUNKED, WKV_ALGO_SCAN, WKV_DEV_BAD_LENGTH,  # noqa: F401
+                      WKV_DEV_BAD_STATE_MAP, WKV_DEV_DECAY_RANGE, WKV_DEV_DUPLICATE_ROW,
+                      WKV_DEV_TOKEN_OVERFLOW, WkvError, check)
+
+_lib = _native.load()
+
+_ALGOS = {"auto": WKV_ALGO_AUTO, "scan": WKV_ALGO_SCAN, "chunked": WKV_ALGO_CHUNKED}
+
+__all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_forward_varlen",
+           "schedule_round_robin", "resolve_algo", "WkvError", "library"]
+
+
+def library():
+    """The loaded ctypes handle of libwkv.so."""
+    return _lib
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return _native.WKV_BF16
+    if t.dtype == torch.float32:
+        return _native.WKV_F32
+    raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(ref):
+    return ctypes.c_void_p(torch.cuda.current_stream(ref.device).cuda_stream)
+
+
+def _same_dtype(name_tensors):
+    dts = {t.dtype for _, t in name_tensors if t is not None}
+    if len(dts) != 1:
+        raise TypeError("token inputs must share one dtype: " +
+                        ", ".join(f"{n}={t.dtype}" for n, t in name_tensors if t is not None))
+
+
+def wkv4_forward(time_decay, time_first, k, v, r=None, state=None, *, y=None, state_out=None,
+                 return_state=True):
+    """v4 WKV.  k, v, r: [B, T, C]; time_decay, time_first: [C] fp32; state: [B, 3, C] fp32 (a, b, p).
+
+    Returns ``(y, state_out)`` (``state_out`` None unless ``return_state``).
+    """
+    B, T, C = k.shape
+    _same_dtype([("k", k), ("v", v), ("r", r)])
+    _dev(k, "k", shape=(B, T, C)); _dev(v, "v", shape=(B, T, C)); _dev(r, "r", shape=(B, T, C))
+    _dev(time_decay, "time_decay", torch.float32, (C,)); _dev(time_first, "time_first", torch.float32, (C,))
+    _dev(state, "state", torch.float32, (B, 3, C))
+    if y is None:
+        y = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
+    _dev(y, "y", torch.float32, (B, T, C))
+    if return_state and state_out is None:
+        state_out = torch.empty((B, 3, C), dtype=torch.float32, device=k.device)
+    _dev(state_out, "state_out", torch.float32, (B, 3, C))
+    check(_lib.wkv4_forward(B, T, C, _ptr(time_decay), _ptr(time_first), _ptr(k), _ptr(v), _ptr(r),
+                            _dtype_code(k), _ptr(y), _ptr(state), _ptr(state_out), _stream(k)))
+    return y, state_out
+
+
+def _dense56(version, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status):
+    B, T, C = r.shape
+    if C % H:
+        raise ValueError(f"C={C} is not a multiple of H={H}")
+    N = C // H
+    _same_dtype([("r", r), ("k", k), ("v", v)] + ([("w", w)] if version == 6 else []))
+    for name, t in (("r", r), ("k", k), ("v", v)):
+        _dev(t, name, shape=(B, T, C))
+    if version == 6:
+        _dev(w, "w", shape=(B, T, C))
+    else:
+        _dev(w, "w", torch.float32, (C,))
+    _dev(u.reshape(-1) if u.dim() == 2 else u, "u", torch.float32, (C,))
+    n_state = 0
+    if state is not None:
+        _dev(state, "state", torch.float32)
+        if state.dim() != 4 or tuple(state.shape[1:]) != (H, N, N):
+            raise ValueError(f"state must be [n_state, {H}, {N}, {N}], got {tuple(state.shape)}")
+        n_state = state.shape[0]
+    _dev(state_map, "state_map", torch.int32, (B,))
+    if y is None:
+        y = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
+    _dev(y, "y", torch.float32, (B, T, C))
+    if return_state and state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    _dev(state_out, "state_out", torch.float32, (B, H, N, N))
+    _dev(dev_status, "dev_status", torch.int32, (1,))
+    fn = _lib.wkv5_forward if version == 5 else _lib.wkv6_forward
+    a = _ALGOS[algo] if isinstance(algo, str) else int(algo)
+    common = (_ptr(u), _ptr(y), _ptr(state), _ptr(state_map), n_state, _ptr(state_out), a,
+              _ptr(dev_status), _stream(r))
+    if version == 5:
+        check(fn(B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _dtype_code(r), _ptr(w), *common))
+    else:
+        check(fn(B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r), *common))
+    return y, state_out
+
+
+def wkv5_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y=None, state_out=None,
+                 return_state=True, dev_status=None):
+    """v5 WKV (static decay).  r, k, v: [B, T, H*N]; w, u: [H*N] fp32 (w = raw decay parameter).
+
+    ``state``: [n_state, H, N, N] fp32 initial states; ``state_map``: [B] int32.
+    Returns ``(y [B, T, H*N] fp32, state_out [B, H, N, N] fp32 or None)``.
+    """
+    return _dense56(5, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status)
+
+
+def wkv6_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y=None, state_out=None,
+                 return_state=True, dev_status=None):
+    """v6 WKV (per-token decay).  r, k, v, w: [B, T, H*N] (same dtype); u: [H*N] or [H, N] fp32.
+
+    Returns ``(y [B, T, H*N] fp32, state_out [B, H, N, N] fp32 or None)``.
+    """
+    return _dense56(6, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status)
+
+
+def wkv6_forward_varlen(lengths, r, k, v, w, u, H, state, *, max_len, state_out=None, state_map=None,
+                        y=None, dev_status=None):
+    """Varlen v6 over packed token rows; updates ``state_out`` (default: ``state`` in place).
+
+    ``lengths``: [S] int32 device tensor (tokens each slot consumes); ``r, k, v, w``:
+    [total_tokens, H*N]; ``state``: [n_state, H, N, N] fp32; ``state_map``: [S] int32.
+    Returns ``y`` [total_tokens, H*N] fp32.
+    """
+    S = lengths.shape[0]
+    total, C = r.shape
+    if C % H:
+        raise ValueError(f"C={C} is not a multiple of H={H}")
+    N = C // H
+    _dev(lengths, "lengths", torch.int32, (S,))
+    _same_dtype([("r", r), ("k", k), ("v", v), ("w", w)])
+    for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
+        _dev(t, name, shape=(total, C))
+    _dev(u.reshape(-1) if u.dim() == 2 else u, "u", torch.float32, (C,))
+    _dev(state, "state", torch.float32)
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, N, N):
+        raise ValueError(f"state must be [n_state, {H}, {N}, {N}], got {tuple(state.shape)}")
+    if state_out is None:
+        state_out = state
+    _dev(state_out, "state_out", torch.float32, tuple(state.shape))
+    _dev(state_map, "state_map", torch.int32, (S,))
+    if y is None:
+        y = torch.empty((total, C), dtype=torch.float32, device=r.device)
+    _dev(y, "y", torch.float32, (total, C))
+    _dev(dev_status, "dev_status", torch.int32, (1,))
+    check(_lib.wkv6_forward_varlen(S, H, N, _ptr(lengths), int(max_len), total, _ptr(r), _ptr(k), _ptr(v),
+                                   _ptr(w), _dtype_code(r), _ptr(u), _ptr(y), _ptr(state), _ptr(state_out),
+                                   _ptr(state_map), state.shape[0], _ptr(dev_status), _stream(r)))
+    return y
+
+
+def schedule_round_robin(remaining, budget):
+    """Per-slot token counts for one serving call (host lists / arrays of int)."""
+    import numpy as np
+    rem = np.ascontiguousarray(remaining, dtype=np.int32)
+    take = np.zeros_like(rem)
+    total = ctypes.c_int32(0)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    check(_lib.wkv_schedule_round_robin(rem.size, rem.ctypes.data_as(i32p), int(budget),
+                                        take.ctypes.data_as(i32p), ctypes.byref(total)))
+    return take
+
+
+def resolve_algo(version, B, T, H, N, algo="auto"):
+    """Name of the algorithm the library runs for a v5/v6 call of this shape."""
+    a = _ALGOS[algo] if isinstance(algo, str) else int(algo)
+    code = _lib.wkv_resolve_algo(version, B, T, H, N, a)
+    return {v: k for k, v in _ALGOS.items()}[code]

@@ -1,0 +1,49 @@
+// Host-side launchers of the WKV kernels (internal to libwkv.so).
+// Arguments have been validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv {
+
+constexpr int kHeadSize = 64;  // the only head size the kernels are built for
+
+// v5 / v6 token-sequential scan.  Dense form: unit = batch row (tokens
+// [b*T, b*T+T)); varlen form: unit = slot (tokens at the slot's packed offset).
+struct ScanParams {
+  int units;        // B (dense) or num_slots (varlen)
+  int T;            // tokens per row (dense)
+  int H;
+  const void *r, *k, *v, *w;  // w: [H*N] fp32 (v5) or token array (v6)
+  const float *u;
+  float *y;
+  const float *state_in;
+  const int32_t *state_map;
+  int n_state;
+  float *state_out;
+  int32_t *dev_status;
+  // varlen only
+  const int32_t *lengths;
+  int max_len;
+  int total_tokens;
+};
+
+hipError_t launch_wkv56_scan(const ScanParams &p, bool v6, bool bf16, bool varlen, hipStream_t s);
+
+// v5 / v6 64-token chunked form with MFMA contractions (dense rows only).
+hipError_t launch_wkv56_chunked(const ScanParams &p, bool v6, bool bf16, hipStream_t s);
+
+// v4 channel-wise scan.
+struct V4Params {
+  int B, T, C;
+  const float *tau, *u;
+  const void *k, *v, *r;
+  float *y;
+  const float *state_in;
+  float *state_out;
+};
+
+hipError_t launch_wkv4(const V4Params &p, bool bf16, hipStream_t s);
+
+}  // namespace wkv

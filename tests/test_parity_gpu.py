@@ -1,0 +1,230 @@
+"""GPU parity of the HIP kernels against the fp64 oracle (through the C ABI).
+
+Workloads (seeded, synthetic):
+  v4  B=1 T=64 C=32 fp32, zero state (small) and B=8 T=1024 C=2048 fp32 with
+      the sigmoid(r) gate plus one T=1 decode step carrying (a, b, p);
+  v5  B=8 T=4096 H=32 N=64 bf16 (sampled heads) plus small ragged cases;
+  v6  B=4 T=4096 H=40 N=64 and B=8 T=4096 H=32 N=64 bf16 (sampled heads),
+      plus small cases covering ragged tails, T=1, shared / mapped / in-place
+      states and fp32 inputs.
+Tolerances: fp32 inputs max error relative to max(|o|, rms(o)) <= 2e-5;
+bf16 inputs max abs <= 2e-2 and mean abs <= 5e-3, on y and on final states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rwkv_linear_attention_wkv_amd as wkv
+from parity import assert_bf16, assert_fp32, dev, host
+from wkv_inputs import wkv4_inputs, wkv5_inputs, wkv6_inputs
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = ["scan"]
+
+
+def _v4_AB(state):
+    s = host(state) if isinstance(state, torch.Tensor) else np.asarray(state, dtype=np.float64)
+    return s[:, 0] * np.exp(s[:, 2]), s[:, 1] * np.exp(s[:, 2])
+
+
+def _check_v4_state(state, A_ref, B_ref, what):
+    A, Bd = _v4_AB(state)
+    rel_b = np.max(np.abs(Bd - B_ref) / np.abs(B_ref))
+    assert rel_b <= 2e-5, f"{what}: denominator relative error {rel_b:.3e}"
+    assert_fp32(A / Bd, A_ref / B_ref, what + " (A/B)")
+
+
+# ------------------------------------------------------------------ v4
+
+def test_v4_small_config():
+    inp = wkv4_inputs(1, 64, 32, seed=0)
+    y, st = wkv.wkv4_forward(dev(inp["tau"]), dev(inp["u"]), dev(inp["k"]), dev(inp["v"]))
+    torch.cuda.synchronize()
+    yo, Ao, Bo = oracle.wkv4(inp["tau"], inp["u"], inp["k"], inp["v"])
+    assert_fp32(host(y), yo, "v4 C0 y")
+    _check_v4_state(st, Ao, Bo, "v4 C0 state")
+    # from a zero state the first output is v_0 exactly
+    assert np.array_equal(host(y)[0, 0], inp["v"][0, 0].astype(np.float64))
+
+
+def test_v4_full_config_with_decode():
+    inp = wkv4_inputs(8, 1024, 2048, seed=0, with_r=True, decode_steps=1)
+    y, st = wkv.wkv4_forward(dev(inp["tau"]), dev(inp["u"]), dev(inp["k"]), dev(inp["v"]), dev(inp["r"]))
+    d = inp["decode"][0]
+    y1, st1 = wkv.wkv4_forward(dev(inp["tau"]), dev(inp["u"]), dev(d["k"]), dev(d["v"]), dev(d["r"]), state=st)
+    torch.cuda.synchronize()
+    yo, Ao, Bo = oracle.wkv4(inp["tau"], inp["u"], inp["k"], inp["v"], inp["r"])
+    assert_fp32(host(y), yo, "v4 C1 y")
+    _check_v4_state(st, Ao, Bo, "v4 C1 state")
+    yo1, Ao1, Bo1 = oracle.wkv4(inp["tau"], inp["u"], d["k"], d["v"], d["r"], Ao, Bo)
+    assert_fp32(host(y1), yo1, "v4 C1 decode y")
+    _check_v4_state(st1, Ao1, Bo1, "v4 C1 decode state")
+
+
+@pytest.mark.parametrize("B,T,C,dtype,with_r", [(2, 1, 100, "f32", False), (3, 37, 100, "bf16", True),
+                                                (1, 300, 64, "f32", True)])
+def test_v4_ragged_and_initial_state(B, T, C, dtype, with_r):
+    inp = wkv4_inputs(B, T, C, seed=7, with_r=with_r, dtype=dtype, init_state=True)
+    st0 = dev(inp["state"])
+    y, st = wkv.wkv4_forward(dev(inp["tau"]), dev(inp["u"]), dev(inp["k"]), dev(inp["v"]), dev(inp["r"]),
+                             state=st0)
+    # in place: state_out == state_in
+    st_inplace = dev(inp["state"])
+    y2, _ = wkv.wkv4_forward(dev(inp["tau"]), dev(inp["u"]), dev(inp["k"]), dev(inp["v"]), dev(inp["r"]),
+                             state=st_inplace, state_out=st_inplace)
+    torch.cuda.synchronize()
+    A0, B0 = _v4_AB(inp["state"])
+    yo, Ao, Bo = oracle.wkv4(inp["tau"], inp["u"], inp["k"], inp["v"], inp["r"], A0, B0)
+    assert_fp32(host(y), yo, "v4 y")
+    _check_v4_state(st, Ao, Bo, "v4 state")
+    assert torch.equal(y, y2) and torch.equal(st, st_inplace)
+
+
+def test_v4_zero_tokens_copies_state():
+    inp = wkv4_inputs(2, 0, 64, seed=1, init_state=True)
+    st0 = dev(inp["state"])
+    out = torch.full_like(st0, float("nan"))
+    wkv.wkv4_forward(dev(inp["tau"]), dev(inp["u"]), dev(inp["k"]), dev(inp["v"]), state=st0, state_out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, st0)
+
+
+# ------------------------------------------------------------------ v5 / v6 helpers
+
+def _run56(version, inp, algo, state=None, state_map=None, **kw):
+    H = inp["H"]
+    args = [dev(inp["r"]), dev(inp["k"]), dev(inp["v"]), dev(inp["x"]), dev(inp["u"]), H]
+    fn = wkv.wkv6_forward if version == 6 else wkv.wkv5_forward
+    return fn(*args, state=state, state_map=state_map, algo=algo, **kw)
+
+
+def _oracle56(inp, state=None, state_map=None, units=None):
+    return oracle.wkv56(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], inp["H"], inp["N"],
+                        state=state, state_map=state_map, units=units)
+
+
+def _sampled_units(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0), (B - 1, H - 1)}
+    while len(picks) < n:
+        picks.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(picks)
+
+
+def _compare_units(y, S, yo, So, units, N, what):
+    yh = host(y)
+    Sh = host(S)
+    ys = np.stack([yh[b, :, h * N:(h + 1) * N] for b, h in units])
+    yos = np.stack([yo[b, :, h * N:(h + 1) * N] for b, h in units])
+    Ss = np.stack([Sh[b, h] for b, h in units])
+    Sos = np.stack([So[b, h] for b, h in units])
+    assert_bf16(ys, yos, what + " y")
+    assert_bf16(Ss, Sos, what + " state")
+
+
+# ------------------------------------------------------------------ v5
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_v5_full_config_sampled(algo):
+    inp = wkv5_inputs(8, 4096, 32, 64, seed=0)
+    y, S = _run56(5, inp, algo)
+    torch.cuda.synchronize()
+    units = _sampled_units(8, 32, 6, seed=1)
+    yo, So = _oracle56(inp, units=units)
+    _compare_units(y, S, yo, So, units, 64, f"v5 C2 {algo}")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("T", [1, 17, 130])
+def test_v5_small_mapped_state(algo, T):
+    inp = wkv5_inputs(3, T, 2, 64, seed=T, init_state=2)
+    smap = np.array([1, 0, 1], dtype=np.int32)
+    y, S = _run56(5, inp, algo, state=dev(inp["state"]), state_map=dev(smap))
+    torch.cuda.synchronize()
+    yo, So = _oracle56(inp, state=inp["state"], state_map=smap)
+    assert_bf16(host(y), yo, "v5 y")
+    assert_bf16(host(S), So, "v5 state")
+
+
+# ------------------------------------------------------------------ v6
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("B,H", [(4, 40), (8, 32)])
+def test_v6_full_config_sampled(algo, B, H):
+    inp = wkv6_inputs(B, 4096, H, 64, seed=0)
+    y, S = _run56(6, inp, algo)
+    torch.cuda.synchronize()
+    units = _sampled_units(B, H, 6, seed=2)
+    yo, So = _oracle56(inp, units=units)
+    _compare_units(y, S, yo, So, units, 64, f"v6 B={B} H={H} {algo}")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (63, "bf16"), (64, "f32"), (200, "f32"), (129, "bf16")])
+def test_v6_small_cases(algo, T, dtype):
+    inp = wkv6_inputs(2, T, 3, 64, seed=100 + T, dtype=dtype, init_state=2)
+    # 1:1 states
+    y, S = _run56(6, inp, algo, state=dev(inp["state"]))
+    # shared state (n_state == 1)
+    y1, S1 = _run56(6, inp, algo, state=dev(inp["state"][:1]))
+    # permuted map
+    smap = np.array([1, 0], dtype=np.int32)
+    y2, S2 = _run56(6, inp, algo, state=dev(inp["state"]), state_map=dev(smap))
+    # in place
+    st = dev(inp["state"])
+    y3, _ = _run56(6, inp, algo, state=st, state_out=st)
+    torch.cuda.synchronize()
+    check = assert_bf16 if dtype == "bf16" else assert_bf16
+    yo, So = _oracle56(inp, state=inp["state"])
+    check(host(y), yo, "v6 y")
+    check(host(S), So, "v6 state")
+    yo1, So1 = _oracle56(inp, state=inp["state"][:1])
+    check(host(y1), yo1, "v6 shared y")
+    check(host(S1), So1, "v6 shared state")
+    yo2, So2 = _oracle56(inp, state=inp["state"], state_map=smap)
+    check(host(y2), yo2, "v6 mapped y")
+    check(host(S2), So2, "v6 mapped state")
+    assert torch.equal(y3, y) and torch.equal(st, S)
+
+
+def test_v6_fp32_inputs_tight():
+    """fp32 inputs: the scan is far inside the bf16 tolerance (state kept in fp32)."""
+    inp = wkv6_inputs(2, 300, 2, 64, seed=5, dtype="f32", init_state=2)
+    y, S = _run56(6, inp, "scan", state=dev(inp["state"]))
+    torch.cuda.synchronize()
+    yo, So = _oracle56(inp, state=inp["state"])
+    err = np.max(np.abs(host(y) - yo)) / max(1.0, np.max(np.abs(yo)))
+    assert err < 2e-5, err
+
+
+def test_v6_bad_state_map_sets_status_and_skips():
+    inp = wkv6_inputs(2, 8, 1, 64, seed=3, init_state=2)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.full((2, 8, 64), float("nan"), device="cuda")
+    smap = dev(np.array([0, 5], dtype=np.int32))
+    _run56(6, inp, "scan", state=dev(inp["state"]), state_map=smap, y=y, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & wkv.WKV_DEV_BAD_STATE_MAP
+    assert torch.isnan(y[1]).all() and not torch.isnan(y[0]).any()
+
+
+def test_v6_deterministic():
+    inp = wkv6_inputs(2, 500, 4, 64, seed=9)
+    ya, Sa = _run56(6, inp, "scan")
+    yb, Sb = _run56(6, inp, "scan")
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb) and torch.equal(Sa, Sb)
+
+
+def test_v6_split_carry_matches_single_pass():
+    inp = wkv6_inputs(2, 300, 2, 64, seed=12, init_state=2)
+    y, S = _run56(6, inp, "scan", state=dev(inp["state"]))
+    part = {k: (inp[k][:, :111] if isinstance(inp[k], np.ndarray) and inp[k].ndim == 3 else inp[k]) for k in inp}
+    rest = {k: (inp[k][:, 111:] if isinstance(inp[k], np.ndarray) and inp[k].ndim == 3 else inp[k]) for k in inp}
+    ya, Sa = _run56(6, part, "scan", state=dev(inp["state"]))
+    yb, Sb = _run56(6, rest, "scan", state=Sa)
+    torch.cuda.synchronize()
+    # the scan walks tokens in the same order either way: bitwise equal
+    assert torch.equal(torch.cat([ya, yb], dim=1), y) and torch.equal(Sb, S)

@@ -1,0 +1,153 @@
+"""Varlen / batched-serving parity on the GPU (wkv6_forward_varlen).
+
+Serving workload: 64 slots, prompt lengths ~ U{1..2048}, H=32, N=64, bf16
+inputs, non-zero fp32 initial states ~ N(0, 0.1), a 128-token budget per call
+split round-robin over the slots, then 256 T=1 decode steps per slot with the
+state carried in place on the device.  Every mapped state row must match its
+own slot's oracle; rows of empty and unmapped slots stay bitwise untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rwkv_linear_attention_wkv_amd as wkv
+from parity import assert_bf16, dev, host
+from wkv_inputs import varlen_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _offsets(lengths):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(lengths)[:-1]]) if lengths.size else lengths
+
+
+def test_varlen_small_with_empty_slots_and_map():
+    H, N = 2, 64
+    lengths = np.array([5, 0, 17, 1, 40, 0], dtype=np.int32)
+    inp = varlen_inputs(6, H, N, seed=50, decode_steps=0, lengths=lengths)
+    n_state = 9
+    rng = np.random.default_rng(3)
+    state = rng.standard_normal((n_state, H, N, N)).astype(np.float32) * 0.1
+    smap = np.array([7, 2, 0, 5, 3, 8], dtype=np.int32)
+    st = dev(state)
+    y = torch.full((int(lengths.sum()), H * N), float("nan"), device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wkv.wkv6_forward_varlen(dev(lengths), dev(inp["r"]), dev(inp["k"]), dev(inp["v"]), dev(inp["x"]),
+                            dev(inp["u"]), H, st, max_len=64, state_map=dev(smap), y=y, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    yo, so = oracle.wkv6_varlen(lengths, inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, state,
+                                state_map=smap)
+    assert_bf16(host(y), yo, "varlen y")
+    sh = host(st)
+    touched = {int(smap[s]) for s in range(6) if lengths[s] > 0}
+    for row in range(n_state):
+        if row in touched:
+            assert_bf16(sh[row], so[row], f"varlen state row {row}")
+        else:
+            assert np.array_equal(sh[row], state[row].astype(np.float64)), f"row {row} modified"
+
+
+def test_varlen_out_of_place_copies_empty_slots():
+    H, N = 1, 64
+    lengths = np.array([0, 3], dtype=np.int32)
+    inp = varlen_inputs(2, H, N, seed=51, decode_steps=0, lengths=lengths)
+    sin = dev(inp["state"])
+    sout = torch.full_like(sin, float("nan"))
+    wkv.wkv6_forward_varlen(dev(lengths), dev(inp["r"]), dev(inp["k"]), dev(inp["v"]), dev(inp["x"]),
+                            dev(inp["u"]), H, sin, max_len=8, state_out=sout)
+    torch.cuda.synchronize()
+    assert torch.equal(sout[0], sin[0])
+    assert torch.equal(sin, dev(inp["state"]))
+    _, so = oracle.wkv6_varlen(lengths, inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, inp["state"])
+    assert_bf16(host(sout[1]), so[1], "out-of-place row")
+
+
+@pytest.mark.parametrize("case", ["negative", "too_long", "bad_map", "duplicate", "overflow"])
+def test_varlen_device_status(case):
+    H, N = 1, 64
+    lengths = np.array([2, 3, 1], dtype=np.int32)
+    smap = np.array([0, 1, 2], dtype=np.int32)
+    total = 6
+    max_len = 8
+    flag = {"negative": wkv.WKV_DEV_BAD_LENGTH, "too_long": wkv.WKV_DEV_BAD_LENGTH,
+            "bad_map": wkv.WKV_DEV_BAD_STATE_MAP, "duplicate": wkv.WKV_DEV_DUPLICATE_ROW,
+            "overflow": wkv.WKV_DEV_TOKEN_OVERFLOW}[case]
+    if case == "negative":
+        lengths[0] = -1
+    elif case == "too_long":
+        lengths[1] = 3
+        max_len = 2
+    elif case == "bad_map":
+        smap[2] = 3
+    elif case == "duplicate":
+        smap[2] = 0
+    elif case == "overflow":
+        total = 5
+    inp = varlen_inputs(3, H, N, seed=52, decode_steps=0, lengths=[2, 3, 1])
+    state = dev(inp["state"])
+    before = state.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.zeros((6, 64), device="cuda")
+    wkv.wkv6_forward_varlen(dev(lengths), dev(inp["r"][:total]), dev(inp["k"][:total]), dev(inp["v"][:total]),
+                            dev(inp["x"][:total]), dev(inp["u"]), H, state, max_len=max_len,
+                            state_map=dev(smap), y=y[:total], dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & flag
+    if case == "duplicate":
+        # both slots mapping to row 0 are skipped; slot 1 still runs
+        assert torch.equal(state[0], before[0])
+        assert not torch.equal(state[1], before[1])
+
+
+def test_serving_workload_prefill_and_decode():
+    S, H, N = 64, 32, 64
+    steps = 256
+    inp = varlen_inputs(S, H, N, seed=0, decode_steps=steps)
+    lengths = inp["lengths"]
+    off = _offsets(lengths)
+    C = H * N
+    state = dev(inp["state"])
+    packed = {n: dev(inp[n]) for n in ("r", "k", "v", "x")}
+    u = dev(inp["u"])
+    consumed = np.zeros(S, dtype=np.int64)
+    y_prompt = torch.full((int(lengths.sum()), C), float("nan"), device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    calls = 0
+    while True:
+        take = wkv.schedule_round_robin(lengths - consumed, 128)
+        if take.sum() == 0:
+            break
+        rows = np.concatenate([np.arange(off[s] + consumed[s], off[s] + consumed[s] + take[s])
+                               for s in range(S) if take[s] > 0])
+        idx = torch.from_numpy(rows).cuda()
+        args = [packed[n].index_select(0, idx) for n in ("r", "k", "v", "x")]
+        y = wkv.wkv6_forward_varlen(dev(take), *args, u, H, state, max_len=128, dev_status=status)
+        y_prompt.index_copy_(0, idx, y)
+        consumed += take
+        calls += 1
+    assert calls >= int(np.ceil(lengths.sum() / 128))
+    ones = dev(np.ones(S, dtype=np.int32))
+    dec = {n: dev(inp["decode"][n]) for n in ("r", "k", "v", "x")}
+    y_dec = torch.empty((steps, S, C), device="cuda")
+    for t in range(steps):
+        y_dec[t] = wkv.wkv6_forward_varlen(ones, dec["r"][t], dec["k"][t], dec["v"][t], dec["x"][t], u, H, state,
+                                           max_len=1, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    # oracle on a sample of slots: prompt followed by the decode tokens
+    sample = [0, 1, int(np.argmax(lengths)), int(np.argmin(lengths)), 33, 63]
+    sample = sorted(set(sample))
+    L = lengths[sample].astype(np.int64) + steps
+    seq = {}
+    for n in ("r", "k", "v", "x"):
+        seq[n] = np.concatenate([np.concatenate([inp[n][off[s]:off[s] + lengths[s]], inp["decode"][n][:, s]])
+                                 for s in sample])
+    yo, so = oracle.wkv6_varlen(L, seq["r"], seq["k"], seq["v"], seq["x"], inp["u"], H, N,
+                                inp["state"][sample])
+    yp, yd = host(y_prompt), host(y_dec)
+    got = np.concatenate([np.concatenate([yp[off[s]:off[s] + lengths[s]], yd[:, s]]) for s in sample])
+    assert_bf16(got, yo, "serving y")
+    assert_bf16(host(state)[sample], so, "serving states")
