@@ -183,9 +183,12 @@ WKV_API wkv_status wkv6_forward_varlen(int num_slots, int H, int N,
 WKV_API wkv_status wkv_schedule_round_robin(int num_slots, const int32_t *remaining,
                                     int budget, int32_t *take, int32_t *total);
 
-/* Algorithm WKV_ALGO_AUTO resolves to for a v5 (version 5) or v6 (version 6)
- * call of this shape.  Pure host function. */
-WKV_API wkv_algo wkv_resolve_algo(int version, int B, int T, int H, int N, wkv_algo requested);
+/* Algorithm a v5 (version 5) or v6 (version 6) call of this shape and input
+ * dtype runs when it requests `requested` (WKV_ALGO_AUTO: chunked for bf16
+ * inputs with T >= 64, else the scan; the chunked form needs bf16 inputs).
+ * Pure host function. */
+WKV_API wkv_algo wkv_resolve_algo(int version, int B, int T, int H, int N, wkv_dtype in_dtype,
+                                  wkv_algo requested);
 
 WKV_API const char *wkv_status_string(wkv_status s);
 /* Detail of the last non-OK return on the calling thread ("" if none). */

@@ -200,8 +200,9 @@ def schedule_round_robin(remaining, budget):
     return take
 
 
-def resolve_algo(version, B, T, H, N, algo="auto"):
-    """Name of the algorithm the library runs for a v5/v6 call of this shape."""
+def resolve_algo(version, B, T, H, N, algo="auto", dtype=torch.bfloat16):
+    """Name of the algorithm the library runs for a v5/v6 call of this shape and input dtype."""
     a = _ALGOS[algo] if isinstance(algo, str) else int(algo)
-    code = _lib.wkv_resolve_algo(version, B, T, H, N, a)
+    d = _native.WKV_BF16 if dtype == torch.bfloat16 else _native.WKV_F32
+    code = _lib.wkv_resolve_algo(version, B, T, H, N, d, a)
     return {v: k for k, v in _ALGOS.items()}[code]

@@ -28,7 +28,7 @@ SIGNATURES = {
     "wkv6_forward_varlen": (_i, [_i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i,
                                  _vp, _vp]),
     "wkv_schedule_round_robin": (_i, [_i, _i32p, _i, _i32p, _i32p]),
-    "wkv_resolve_algo": (_i, [_i, _i, _i, _i, _i, _i]),
+    "wkv_resolve_algo": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "wkv_status_string": (ctypes.c_char_p, [_i]),
     "wkv_last_error": (ctypes.c_char_p, []),
     "wkv_abi_version": (_i, []),

@@ -38,7 +38,6 @@ wkv_status launched(hipError_t e, const char *what) {
 
 constexpr int kMaxGridY = 65535;
 constexpr int kChunk = 64;
-constexpr bool kHaveChunked = false;
 
 #define REQUIRE(cond, ...)                                        \
   do {                                                            \
@@ -55,8 +54,8 @@ wkv_status check_dense56(const char *fn, int B, int T, int H, int N, const void 
   if (!dtype_ok(in_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown input dtype %d", fn, in_dtype);
   if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SCAN && algo != WKV_ALGO_CHUNKED)
     return fail(WKV_ERR_UNSUPPORTED, "%s: unknown algorithm %d", fn, algo);
-  if (algo == WKV_ALGO_CHUNKED && !kHaveChunked)
-    return fail(WKV_ERR_UNSUPPORTED, "%s: the chunked algorithm is not built", fn);
+  if (algo == WKV_ALGO_CHUNKED && in_dtype != WKV_BF16)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: the chunked algorithm needs bf16 inputs", fn);
   REQUIRE(B <= kMaxGridY, "%s: B=%d exceeds %d", fn, B, kMaxGridY);
   REQUIRE((int64_t)H * N <= (int64_t)1 << 30, "%s: H*N too large", fn);
   if (T > 0) {
@@ -102,10 +101,10 @@ const char *wkv_status_string(wkv_status s) {
   }
 }
 
-wkv_algo wkv_resolve_algo(int version, int B, int T, int H, int N, wkv_algo requested) {
+wkv_algo wkv_resolve_algo(int version, int B, int T, int H, int N, wkv_dtype in_dtype, wkv_algo requested) {
   (void)B; (void)H; (void)N;
   if (requested == WKV_ALGO_SCAN || requested == WKV_ALGO_CHUNKED) return requested;
-  if ((version != 5 && version != 6) || !kHaveChunked) return WKV_ALGO_SCAN;
+  if ((version != 5 && version != 6) || in_dtype != WKV_BF16) return WKV_ALGO_SCAN;
   // Chunks only pay off once a row holds at least one full chunk.
   return T >= kChunk ? WKV_ALGO_CHUNKED : WKV_ALGO_SCAN;
 }
@@ -155,7 +154,7 @@ static wkv_status dense56(int version, int B, int T, int H, int N, const void *r
   p.dev_status = dev_status;
   const bool bf16 = in_dtype == WKV_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const wkv_algo a = wkv_resolve_algo(version, B, T, H, N, algo);
+  const wkv_algo a = wkv_resolve_algo(version, B, T, H, N, in_dtype, algo);
   if (a == WKV_ALGO_CHUNKED && T > 0)
     return launched(wkv::launch_wkv56_chunked(p, version == 6, bf16, s), fn);
   return launched(wkv::launch_wkv56_scan(p, version == 6, bf16, false, s), fn);

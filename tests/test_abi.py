@@ -167,8 +167,17 @@ def test_round_robin_rejects_negative(lib):
 
 def test_resolve_algo(lib):
     A, S, C = nat.WKV_ALGO_AUTO, nat.WKV_ALGO_SCAN, nat.WKV_ALGO_CHUNKED
-    assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, S) == S
-    assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, C) == C
-    assert lib.wkv_resolve_algo(6, 8, 1, 32, 64, A) == S          # decode stays on the scan
-    assert lib.wkv_resolve_algo(4, 8, 4096, 32, 64, A) == S
-    assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, A) in (S, C)
+    bf, f32 = nat.WKV_BF16, nat.WKV_F32
+    assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, bf, S) == S
+    assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, bf, C) == C
+    assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, bf, A) == C
+    assert lib.wkv_resolve_algo(5, 8, 4096, 32, 64, bf, A) == C
+    assert lib.wkv_resolve_algo(6, 8, 63, 32, 64, bf, A) == S          # no full chunk
+    assert lib.wkv_resolve_algo(6, 8, 1, 32, 64, bf, A) == S           # decode stays on the scan
+    assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, f32, A) == S       # fp32 inputs: scan
+    assert lib.wkv_resolve_algo(4, 8, 4096, 32, 64, bf, A) == S
+
+
+def test_chunked_needs_bf16(lib):
+    assert v6(lib, dt=nat.WKV_F32, algo=nat.WKV_ALGO_CHUNKED) == nat.WKV_ERR_UNSUPPORTED
+    assert b"bf16" in lib.wkv_last_error()
