@@ -44,7 +44,29 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the WKV step, time a plain device-to-device copy of this many bytes "
+                         "(the reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration(args):
+    """A plain copy of known size: the rocprofv3 byte counters of this run, divided by the bytes it must
+    move, give the factor that turns the same counters into HBM bytes for the WKV kernels."""
+    import torch
+    n = args.copy_bytes // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "steps": args.steps,
+                      "ms_per_copy": dt * 1e3, "GBs": 2 * 4 * n / dt / 1e9}))
 
 
 def kernel_digest(algo):
@@ -111,6 +133,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the WKV path here runs on a "
               "single MI355X and has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_calibration(args)
+        return
     import numpy as np
     import torch
 

@@ -4,39 +4,48 @@
 // r, k, v, w, u, init_state, state_map -> y, y_state; S indexed [key i][value j]):
 //   y_t[j] = sum_i r_t[i] (S[i][j] + u[i] k_t[i] v_t[j]),  S[i][j] <- d_t[i] S[i][j] + k_t[i] v_t[j]
 // rewritten exactly, chunk by chunk.  Inside a chunk of L = 64 tokens let
-// Lam_t[i] = sum_{m<=t} log d_m[i] (inclusive, from the chunk start).  Then
-//   rbar_t = r_t * exp(Lam_{t-1}),  ktil_s = k_s * exp(-Lam_s),  khat_s = k_s * exp(Lam_{L-1} - Lam_s)
-//   A[t][s] = rbar_t . ktil_s  (s < t),  A[t][t] = sum_i r_t[i] u[i] k_t[i],  A[t][s] = 0 (s > t)
-//   Y = A V + rbar S0                  (S0 = state at the chunk start)
-//   S1 = diag(exp(Lam_{L-1})) S0 + khat^T V
-// which equals the token recurrence in exact arithmetic.
+// Lam_t[i] = sum_{m<=t} log d_m[i] (inclusive, from the chunk start) and
+//   rbar_t = r_t * exp(Lam_{t-1}),  ktil_s = k_s * exp(-Lam_s).
+// Then, with S0 the state at the chunk start,
+//   A[t][s] = rbar_t . ktil_s (s < t),  A[t][t] = sum_i r_t[i] u[i] k_t[i],  A[t][s] = 0 (s > t)
+//   Y  = A V + rbar S0
+//   S1 = diag(exp(Lam_{L-1})) (S0 + ktil^T V)
+// which equals the token recurrence in exact arithmetic.  The last line adds
+// the chunk's keys in the frame of the chunk start and rescales once; fp32
+// rounding of that sum is relative to its larger term, so the rescale keeps
+// the usual relative accuracy.
 //
 // Precision.  Every MFMA runs on bf16 operands with fp32 accumulation.  V is
-// the exact bf16 input; every other operand (rbar, ktil, khat, A, S) is split
-// into hi = bf16(x) and lo = bf16(x - hi), and each product is formed as
-// hi*hi + hi*lo + lo*hi (v only needs hi*v + lo*v), which keeps about 16
-// significant bits per term.  All products that survive the mask are bounded
-// by |r k| because exp(Lam_{t-1} - Lam_s) <= 1 for s < t.
+// the exact bf16 input; every other operand (rbar, ktil, A, S) is split into
+// hi = bf16(x) and lo = bf16(x - hi) (both round-to-nearest-even) and each
+// product is formed as hi*hi + hi*lo + lo*hi (v only needs hi*v + lo*v),
+// about 16 significant bits per term.  Every product that survives the causal
+// mask is bounded by |r k|, since exp(Lam_{t-1} - Lam_s) <= 1 for s < t.
 //
 // Range.  ktil carries exp(-Lam_s) >= 1.  A chunk whose accumulated log2
 // decay in some channel is below -kMaxLog2 sets WKV_DEV_DECAY_RANGE (its
-// outputs are not trustworthy; the token-sequential scan has no such limit).
-// Per-step decays exp(-exp(x)) with x <= 0 stay far inside this range.
+// outputs are then not trustworthy; the token-sequential scan has no such
+// limit).  Per-step decays exp(-exp(x)) with x <= 0 stay far inside it.
 //
-// Work decomposition.  One 512-thread workgroup (8 waves) per (batch row,
-// head) walks the chunks in order with the fp32 state in MFMA accumulators.
-//   precompute: thread (channel i, token group g of 8) loads its 8 tokens,
-//     forms the log-decay prefix (group totals exchanged through LDS) and
-//     writes rbar, ktil (row-major [token][channel]), khat and V transposed
-//     ([channel][token]) as bf16 to LDS, plus the bonus diagonal.
-//   MFMA: wave (jb, part) owns value columns 16jb..16jb+15; part 0 computes
-//     output token blocks {0, 3}, part 1 blocks {1, 2} (equal MFMA counts),
-//     and key-row blocks {0,1} / {2,3} of the state update.  Each wave forms
-//     the A^T tiles it needs (v_mfma_f32_16x16x32_bf16), keeps them in
-//     registers and feeds them straight back as the A operand of A V (the K
-//     order of an accumulator tile is a permutation that the V operand
-//     reads in the same order).  The state is exchanged between waves as
-//     bf16 hi/lo S^T in a ping-pong LDS buffer.
+// Work decomposition: one 1024-thread workgroup (16 waves) per (batch row,
+// head) walks the chunks in order as a two-stage pipeline, so that the
+// vector-ALU work of one chunk overlaps the matrix-core work of the previous
+// one.  Every operand the producers write is double-buffered in LDS.
+//   producers (waves 0-7), chunk c+1: thread (channel pair cp, token group tg
+//     of 4) consumes its inputs (4-byte loads issued one chunk ahead), forms
+//     the log2-decay prefix (wave totals exchanged through LDS), and writes
+//     rbar, ktil row-major and V transposed as bf16 hi / lo; the bonus
+//     diagonal is reduced across the lanes of a half-wave.
+//   consumers (waves 8-15), chunk c:
+//     M1: the ten causal 16x16 tiles of A^T (v_mfma_f32_16x16x32_bf16),
+//       masked and stored to LDS as A hi / lo;
+//     M2: four waves own the 32x32 output tiles (v_mfma_f32_32x32x16_bf16:
+//       rbar S0 + A V); four waves own the 32x32 state tiles in fp32
+//       accumulators.  They transpose ktil on the matrix core (a product with
+//       the identity is exact for bf16 values) and reuse the accumulator
+//       layout as the A operand of ktil^T V by reading V in the matching
+//       permuted token order.  The state goes to the output waves as bf16
+//       hi / lo S^T in a ping-pong buffer.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "wkv.h"
@@ -46,50 +55,67 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int L = 64;          // tokens per chunk
-constexpr int kThreads = 512;  // 8 waves
-constexpr int RS = 72;         // LDS row stride in bf16 elements (144 bytes: conflict-free 16-lane b128 reads)
-constexpr int BS = kHead + 4;  // row stride of the fp32 bonus partials
+constexpr int L = 64;           // tokens per chunk
+constexpr int kThreads = 1024;  // 16 waves: 8 producers, 8 consumers
+constexpr int RS = 72;          // LDS row stride in bf16 elements (144 bytes)
 constexpr float kMaxLog2 = 100.f;
 
-struct Smem {
-  uint16_t rb_hi[L][RS], rb_lo[L][RS];            // rbar   [token][channel]
-  uint16_t kt_hi[L][RS], kt_lo[L][RS];            // ktil   [token][channel]
-  uint16_t kh_hi[kHead][RS], kh_lo[kHead][RS];    // khat^T [channel][token]
-  uint16_t vt[kHead][RS];                         // V^T    [value col][token]
-  uint16_t st_hi[2][kHead][RS], st_lo[2][kHead][RS];  // S^T [value col][key row], ping-pong
-  float bp[L][BS];                                // bonus partials r*u*k [token][channel]
-  float tot[8][kHead];                            // log2-decay total of each 8-token group
+struct Ops {                      // one chunk's operands, written by the producers
+  uint16_t rb_hi[L][RS], rb_lo[L][RS];  // rbar [token][key row]
+  uint16_t kt_hi[L][RS], kt_lo[L][RS];  // ktil [token][key row]
+  uint16_t vt[kHead][RS];               // V^T  [value col][token]
   float bonus[L];
-  float pl[kHead];                                // exp(Lam_{L-1}) per key row
+  float pl[kHead];                      // exp(Lam_{L-1}) per key row
+};
+
+struct Smem {
+  Ops ops[2];
+  uint16_t a_hi[L][RS], a_lo[L][RS];                  // A   [query token][key token]
+  uint16_t st_hi[2][kHead][RS], st_lo[2][kHead][RS];  // S^T [value col][key row], ping-pong
+  float2 wtot[8][32];                                 // log2-decay total of each producer wave, per channel pair
   int range_bad;
 };
 
-__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// hi = bf16(f), lo = bf16(f - hi), both round-to-nearest-even.
-__device__ __forceinline__ void split(float f, uint16_t &hi, uint16_t &lo) {
-  hi = bf16_bits_rne(f);
-  lo = bf16_bits_rne(f - bf16_bits_to_f32(hi));
+// Two floats -> packed bf16 pair (round to nearest even): low half = a.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(a);
+  v[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Split two floats into packed hi and lo bf16 pairs.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16(a, b);
+  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
-// two runs of 4 consecutive bf16 (8-byte aligned) as one operand
 __device__ __forceinline__ bf16x8 ld4x2(const uint16_t *p0, const uint16_t *p1) {
   const uint2 a = *reinterpret_cast<const uint2 *>(p0);
   const uint2 b = *reinterpret_cast<const uint2 *>(p1);
   return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
 }
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
+}
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Keeps the compiler from moving work on a prefetched register above this
+// point, so the wait for the load lands here.
+__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
 template <bool V6>
 __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
@@ -100,10 +126,13 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int hh = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform role selector
+  const bool producer = wave_u < 8;
   const long C = (long)p.H * kHead;
   const int T = p.T;
   const long tok0 = (long)b * T;
+  const int nchunks = (T + L - 1) / L;
 
   int row_in = -1;
   if (p.state_in) {
@@ -114,266 +143,320 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     }
   }
 
-  // ---- MFMA-phase roles
-  const int jb = wave & 3;    // value columns 16jb .. 16jb+15
-  const int part = wave >> 2;  // token blocks {0,3} / {1,2}; key-row blocks {0,1} / {2,3}
-  const int g = lane >> 4;    // operand k-group / accumulator row group
+  // ---------------- producer roles: channels 2cp, 2cp+1; tokens 4tg .. 4tg+3 of a chunk
+  const int cp = tid & 31;
+  const int tg = (tid >> 5) & 15;
+  const int pwave = (tid >> 6) & 7;
+  // ---------------- consumer roles
+  const int cw = (tid >> 6) & 7;         // consumer wave 0..7
+  const bool y_wave = cw < 4;            // M2: output tile / state tile
+  const int tile_r = (cw & 3) >> 1;      // token block (output) / key-row block (state)
+  const int tile_c = cw & 1;             // value-column block
+  const int l32 = lane & 31;
+  const int jcol = 32 * tile_c + l32;
   const int l16 = lane & 15;
-  const int jcol = 16 * jb + l16;
+  const int g4 = lane >> 4;
 
-  // state tiles owned: key rows 16*ib + 4g + e, ib = 2*part + q; column jcol
-  f32x4 Sacc[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int ib = 2 * part + q;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * ib + 4 * g + e;
-      Sacc[q][e] = row_in >= 0 ? p.state_in[(((long)row_in * p.H + h) * kHead + i) * kHead + jcol] : 0.f;
-    }
-  }
+  f32x16 S = {};  // state waves: rows 32*tile_r + 8*(e/4) + 4*hh + e%4, column jcol
   auto publish_state = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int ib = 2 * part + q;
-      uint16_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split(Sacc[q][e], hi[e], lo[e]);
-      *reinterpret_cast<uint2 *>(&sm.st_hi[buf][jcol][16 * ib + 4 * g]) =
-          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *reinterpret_cast<uint2 *>(&sm.st_lo[buf][jcol][16 * ib + 4 * g]) =
-          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    for (int q = 0; q < 4; ++q) {
+      uint32_t h0, l0, h1, l1;
+      split2(S[4 * q], S[4 * q + 1], h0, l0);
+      split2(S[4 * q + 2], S[4 * q + 3], h1, l1);
+      const int i0 = 32 * tile_r + 8 * q + 4 * hh;
+      *reinterpret_cast<uint2 *>(&sm.st_hi[buf][jcol][i0]) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(&sm.st_lo[buf][jcol][i0]) = make_uint2(l0, l1);
     }
   };
-  publish_state(0);
-  if (tid == 0) sm.range_bad = 0;
 
-  // ---- precompute roles: channel ci, tokens 8*cg .. 8*cg+7 of the chunk
-  const int ci = tid & 63;
-  const int cg = tid >> 6;
-  const float u_ci = p.u[h * kHead + ci];
-  const float xs_ci = V6 ? 0.f : static_cast<const float *>(p.w)[h * kHead + ci];
-  const uint16_t *R = static_cast<const uint16_t *>(p.r);
-  const uint16_t *K = static_cast<const uint16_t *>(p.k);
-  const uint16_t *Vv = static_cast<const uint16_t *>(p.v);
-  const uint16_t *W = static_cast<const uint16_t *>(p.w);
+  if (!producer) {
+    if (!y_wave && row_in >= 0) {
+      const float *sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[e] = sp[(32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3)) * kHead + jcol];
+    }
+    if (!y_wave) publish_state(0);
+    // A tiles that the causal mask zeroes but the 32-wide K steps of A V read
+    // (rows 0-15 x cols 16-31 and rows 32-47 x cols 48-63): zero them once.
+    const int ct = tid - 512;
+    if (ct < 128) {
+      const int region = ct >> 6, rem = ct & 63;
+      const int row = 32 * region + (rem >> 2), col = 16 + 32 * region + 4 * (rem & 3);
+      *reinterpret_cast<uint2 *>(&sm.a_hi[row][col]) = make_uint2(0u, 0u);
+      *reinterpret_cast<uint2 *>(&sm.a_lo[row][col]) = make_uint2(0u, 0u);
+    }
+  } else if (tid == 0) {
+    sm.range_bad = 0;
+  }
 
-  uint16_t nr[8], nk[8], nv[8], nx[8];
+  // ---------------- producer state carried between its two phases
+  float2 u2 = make_float2(0.f, 0.f), xs = make_float2(0.f, 0.f);
+  if (producer) {
+    u2 = *reinterpret_cast<const float2 *>(p.u + h * kHead + 2 * cp);
+    if (!V6) xs = *reinterpret_cast<const float2 *>(static_cast<const float *>(p.w) + h * kHead + 2 * cp);
+  }
+  const long thr_off = (long)(4 * tg) * C + h * kHead + 2 * cp;  // element offset of this thread's first row
+  uint32_t nr[4], nk[4], nv[4], nx[4];
   auto prefetch = [&](int c) {
-    const int t0 = c * L;
+    const long base = (tok0 + (long)c * L) * C;
+    const int last = T - 1 - c * L - 4 * tg;  // rows past the end: read the last row, zeroed on use
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int tau = 8 * cg + t;
-      if (t0 + tau < T) {
-        const long e = (tok0 + t0 + tau) * C + h * kHead + ci;
-        nr[t] = R[e];
-        nk[t] = K[e];
-        nv[t] = Vv[e];
-        if (V6) nx[t] = W[e];
-      } else {
-        nr[t] = 0; nk[t] = 0; nv[t] = 0; nx[t] = 0;
-      }
+    for (int t = 0; t < 4; ++t) {
+      const long e = base + thr_off + (long)min(t, last) * C;
+      nr[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.r) + e);
+      nk[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.k) + e);
+      nv[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.v) + e);
+      if (V6) nx[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.w) + e);
     }
   };
+  uint32_t rkeep[4], kkeep[4];  // this chunk's r and k words, carried to phase 2
+  float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f;
 
-  const int nchunks = (T + L - 1) / L;
-  prefetch(0);
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0 = c * L;
-    const int nvalid = min(L, T - t0);
-    const int buf = c & 1;
-
-    // ================= precompute (vector ALU)
-    float rr[8], kk[8], cum[8];
-    float run = 0.f;
+  // producer phase 1 of chunk c: decay, in-thread prefix, bonus, V^T, wave totals
+  auto produce1 = [&](int c) {
+    Ops &o = sm.ops[c & 1];
+    const int nvalid = min(L, T - c * L);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int tau = 8 * cg + t;
-      const bool valid = tau < nvalid;
-      rr[t] = bf16_bits_to_f32(nr[t]);
-      kk[t] = bf16_bits_to_f32(nk[t]);
-      const float x = V6 ? bf16_bits_to_f32(nx[t]) : xs_ci;
+    for (int t = 0; t < 4; ++t) {
+      pin(nr[t]); pin(nk[t]); pin(nv[t]);
+      if (V6) pin(nx[t]);
+    }
+    float bon[4];
+    uint32_t vraw[4];
+    float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bool valid = 4 * tg + t < nvalid;
+      const uint32_t rw = valid ? nr[t] : 0u, kw = valid ? nk[t] : 0u;
+      vraw[t] = valid ? nv[t] : 0u;
+      rkeep[t] = rw;
+      kkeep[t] = kw;
+      const float r0 = bf16_bits_to_f32(rw & 0xffffu), r1 = __uint_as_float(rw & 0xffff0000u);
+      const float k0 = bf16_bits_to_f32(kw & 0xffffu), k1 = __uint_as_float(kw & 0xffff0000u);
+      float x0 = xs.x, x1 = xs.y;
+      if (V6) {
+        x0 = bf16_bits_to_f32(nx[t] & 0xffffu);
+        x1 = __uint_as_float(nx[t] & 0xffff0000u);
+      }
       // log2 of the decay exp(-exp(x)) is -exp(x) * log2(e)
-      const float l2 = valid ? -fast_exp(x) * 1.4426950408889634f : 0.f;
-      run += l2;
-      cum[t] = run;
-      sm.bp[tau][ci] = rr[t] * u_ci * kk[t];
-    }
-    *reinterpret_cast<uint4 *>(&sm.vt[ci][8 * cg]) =
-        make_uint4(nv[0] | ((uint32_t)nv[1] << 16), nv[2] | ((uint32_t)nv[3] << 16),
-                   nv[4] | ((uint32_t)nv[5] << 16), nv[6] | ((uint32_t)nv[7] << 16));
-    sm.tot[cg][ci] = run;
-    __syncthreads();
-
-    float prefix = 0.f, total = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float tq = sm.tot[q][ci];
-      if (q < cg) prefix += tq;
-      total += tq;
-    }
-    const float pl = __builtin_amdgcn_exp2f(total);
-    if (cg == 0) sm.pl[ci] = pl;
-    if (total < -kMaxLog2) sm.range_bad = 1;
-    uint16_t khh[8], khl[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int tau = 8 * cg + t;
-      const float lam = prefix + cum[t];
-      const float lam_prev = t ? prefix + cum[t - 1] : prefix;
-      const float rb = rr[t] * __builtin_amdgcn_exp2f(lam_prev);
-      const float kt = kk[t] * __builtin_amdgcn_exp2f(-lam);
-      const float kh = kt * pl;
-      uint16_t hi, lo;
-      split(rb, hi, lo);
-      sm.rb_hi[tau][ci] = hi;
-      sm.rb_lo[tau][ci] = lo;
-      split(kt, hi, lo);
-      sm.kt_hi[tau][ci] = hi;
-      sm.kt_lo[tau][ci] = lo;
-      split(kh, khh[t], khl[t]);
-    }
-    *reinterpret_cast<uint4 *>(&sm.kh_hi[ci][8 * cg]) =
-        make_uint4(khh[0] | ((uint32_t)khh[1] << 16), khh[2] | ((uint32_t)khh[3] << 16),
-                   khh[4] | ((uint32_t)khh[5] << 16), khh[6] | ((uint32_t)khh[7] << 16));
-    *reinterpret_cast<uint4 *>(&sm.kh_lo[ci][8 * cg]) =
-        make_uint4(khl[0] | ((uint32_t)khl[1] << 16), khl[2] | ((uint32_t)khl[3] << 16),
-                   khl[4] | ((uint32_t)khl[5] << 16), khl[6] | ((uint32_t)khl[7] << 16));
-    __syncthreads();
-    {  // bonus diagonal: b[tau] = sum_i r u k, 8 lanes per token
-      const int tau = tid >> 3, q = tid & 7;
-      const float4 a0 = *reinterpret_cast<const float4 *>(&sm.bp[tau][8 * q]);
-      const float4 a1 = *reinterpret_cast<const float4 *>(&sm.bp[tau][8 * q + 4]);
-      float s = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if (q == 0) sm.bonus[tau] = s;
+      const float l0 = valid ? -fast_exp(x0) * 1.4426950408889634f : 0.f;
+      const float l1 = valid ? -fast_exp(x1) * 1.4426950408889634f : 0.f;
+      run0 += l0;
+      run1 += l1;
+      cum0[t] = run0;
+      cum1[t] = run1;
+      bon[t] = fmaf(r1 * u2.y, k1, r0 * u2.x * k0);
     }
     if (c + 1 < nchunks) prefetch(c + 1);
-    __syncthreads();
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp][4 * tg]) =
+        make_uint2(__builtin_amdgcn_perm(vraw[1], vraw[0], 0x05040100u), __builtin_amdgcn_perm(vraw[3], vraw[2], 0x05040100u));
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp + 1][4 * tg]) =
+        make_uint2(__builtin_amdgcn_perm(vraw[1], vraw[0], 0x07060302u), __builtin_amdgcn_perm(vraw[3], vraw[2], 0x07060302u));
+    {  // bonus diagonal: sum over the 32 channel pairs of this token group (one half-wave)
+      const bool up16 = lane & 16;
+      float keep0 = up16 ? bon[2] : bon[0], keep1 = up16 ? bon[3] : bon[1];
+      const float send0 = up16 ? bon[0] : bon[2], send1 = up16 ? bon[1] : bon[3];
+      keep0 += __shfl_xor(send0, 16);
+      keep1 += __shfl_xor(send1, 16);
+      const bool up8 = lane & 8;
+      float kk = up8 ? keep1 : keep0;
+      kk += __shfl_xor(up8 ? keep0 : keep1, 8);
+      kk += __shfl_xor(kk, 4);
+      kk += __shfl_xor(kk, 2);
+      kk += __shfl_xor(kk, 1);
+      if ((lane & 7) == 0) o.bonus[4 * tg + (up16 ? 2 : 0) + (up8 ? 1 : 0)] = kk;
+    }
+    // wave totals: the upper half-wave (odd token group) adds the lower one's total
+    lower0 = __shfl_xor(run0, 32);
+    lower1 = __shfl_xor(run1, 32);
+    if (hh) sm.wtot[pwave][cp] = make_float2(run0 + lower0, run1 + lower1);
+  };
 
-    // ================= MFMA phase
+  // producer phase 2 of chunk c: prefix, scaled operands, bf16 hi / lo
+  auto produce2 = [&](int c) {
+    Ops &o = sm.ops[c & 1];
+    float pre0 = hh ? lower0 : 0.f, pre1 = hh ? lower1 : 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int tb = part == 0 ? (pass == 0 ? 0 : 3) : (pass == 0 ? 1 : 2);
-      // A^T tiles (sb, tb), sb <= tb: rows = key token s, cols = query token t
-      f32x4 At[4];
+    for (int w = 0; w < 8; ++w) {
+      const float2 wt = sm.wtot[w][cp];
+      if (w < pwave) { pre0 += wt.x; pre1 += wt.y; }
+      tot0 += wt.x;
+      tot1 += wt.y;
+    }
+    if (tg == 0) *reinterpret_cast<float2 *>(&o.pl[2 * cp]) =
+        make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
+    if (tot0 < -kMaxLog2 || tot1 < -kMaxLog2) sm.range_bad = 1;
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        At[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (sb > tb) continue;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 ah = ld8(&sm.kt_hi[16 * sb + l16][32 * s + 8 * g]);
-          const bf16x8 al = ld8(&sm.kt_lo[16 * sb + l16][32 * s + 8 * g]);
-          const bf16x8 bh = ld8(&sm.rb_hi[16 * tb + l16][32 * s + 8 * g]);
-          const bf16x8 bl = ld8(&sm.rb_lo[16 * tb + l16][32 * s + 8 * g]);
-          At[sb] = mfma(ah, bh, At[sb]);
-          At[sb] = mfma(ah, bl, At[sb]);
-          At[sb] = mfma(al, bh, At[sb]);
-        }
-        if (sb == tb) {  // causal mask and bonus diagonal
-          const int t = 16 * tb + l16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int s = 16 * sb + 4 * g + e;
-            At[sb][e] = s < t ? At[sb][e] : (s == t ? sm.bonus[t] : 0.f);
-          }
-        }
-      }
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-      // inter-chunk: Y += rbar S0  (K = key row i)
+    for (int t = 0; t < 4; ++t) {
+      const int tau = 4 * tg + t;
+      const float lp0 = t ? pre0 + cum0[t - 1] : pre0, lp1 = t ? pre1 + cum1[t - 1] : pre1;
+      const float la0 = pre0 + cum0[t], la1 = pre1 + cum1[t];
+      const float r0 = bf16_bits_to_f32(rkeep[t] & 0xffffu), r1 = __uint_as_float(rkeep[t] & 0xffff0000u);
+      const float k0 = bf16_bits_to_f32(kkeep[t] & 0xffffu), k1 = __uint_as_float(kkeep[t] & 0xffff0000u);
+      uint32_t hi, lo;
+      split2(r0 * __builtin_amdgcn_exp2f(lp0), r1 * __builtin_amdgcn_exp2f(lp1), hi, lo);
+      *reinterpret_cast<uint32_t *>(&o.rb_hi[tau][2 * cp]) = hi;
+      *reinterpret_cast<uint32_t *>(&o.rb_lo[tau][2 * cp]) = lo;
+      split2(k0 * __builtin_amdgcn_exp2f(-la0), k1 * __builtin_amdgcn_exp2f(-la1), hi, lo);
+      *reinterpret_cast<uint32_t *>(&o.kt_hi[tau][2 * cp]) = hi;
+      *reinterpret_cast<uint32_t *>(&o.kt_lo[tau][2 * cp]) = lo;
+    }
+  };
+
+  // consumer M1 of chunk c: causal A^T tiles, masked, stored as A hi / lo
+  constexpr unsigned long long kM1Sb = 0x3210210100ull, kM1Tb = 0x3333222110ull;  // tile ti: (sb, tb) nibbles
+  auto consume1 = [&](int c) {
+    const Ops &o = sm.ops[c & 1];
+    for (int ti = cw; ti < 10; ti += 8) {
+      const int sb = (int)((kM1Sb >> (4 * ti)) & 15), tb = (int)((kM1Tb >> (4 * ti)) & 15);
+      f32x4 At = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 ah = ld8(&sm.rb_hi[16 * tb + l16][32 * s + 8 * g]);
-        const bf16x8 al = ld8(&sm.rb_lo[16 * tb + l16][32 * s + 8 * g]);
-        const bf16x8 bh = ld8(&sm.st_hi[buf][jcol][32 * s + 8 * g]);
-        const bf16x8 bl = ld8(&sm.st_lo[buf][jcol][32 * s + 8 * g]);
-        Y = mfma(ah, bh, Y);
-        Y = mfma(ah, bl, Y);
-        Y = mfma(al, bh, Y);
+        const bf16x8 ah = ld8(&o.kt_hi[16 * sb + l16][32 * s + 8 * g4]);
+        const bf16x8 al = ld8(&o.kt_lo[16 * sb + l16][32 * s + 8 * g4]);
+        const bf16x8 bh = ld8(&o.rb_hi[16 * tb + l16][32 * s + 8 * g4]);
+        const bf16x8 bl = ld8(&o.rb_lo[16 * tb + l16][32 * s + 8 * g4]);
+        At = mfma16(ah, bh, At);
+        At = mfma16(ah, bl, At);
+        At = mfma16(al, bh, At);
       }
-      // intra-chunk: Y += A V  (K = key token s; operand slot e of group g holds
-      // s = 32sp + 4g + e for e < 4 and 32sp + 16 + 4g + (e-4) for e >= 4)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        if (2 * sp > tb) continue;
-        uint16_t ahi[8], alo[8];
+      // lane holds A^T[s = 16sb + 4g4 + e][t = 16tb + l16]
+      const int t = 16 * tb + l16;
+      if (sb == tb) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          split(At[2 * sp][e], ahi[e], alo[e]);
-          split(At[2 * sp + 1][e], ahi[4 + e], alo[4 + e]);
+          const int s = 16 * sb + 4 * g4 + e;
+          At[e] = s < t ? At[e] : (s == t ? o.bonus[t] : 0.f);
         }
-        bf16x8 ah, al;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ah[e] = __builtin_bit_cast(__bf16, ahi[e]);
-          al[e] = __builtin_bit_cast(__bf16, alo[e]);
-        }
-        const bf16x8 bv = ld4x2(&sm.vt[jcol][32 * sp + 4 * g], &sm.vt[jcol][32 * sp + 16 + 4 * g]);
-        Y = mfma(ah, bv, Y);
-        Y = mfma(al, bv, Y);
       }
-      // store outputs: rows t = 16tb + 4g + e, column jcol
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * tb + 4 * g + e;
-        if (t < nvalid) p.y[(tok0 + t0 + t) * C + h * kHead + jcol] = Y[e];
-      }
+      uint32_t h0, l0, h1, l1;
+      split2(At[0], At[1], h0, l0);
+      split2(At[2], At[3], h1, l1);
+      *reinterpret_cast<uint2 *>(&sm.a_hi[t][16 * sb + 4 * g4]) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(&sm.a_lo[t][16 * sb + 4 * g4]) = make_uint2(l0, l1);
     }
+  };
 
-    // state update: S <- diag(pl) S + khat^T V  (K = key token s)
+  // consumer M2 of chunk c
+  auto consume2 = [&](int c) {
+    const Ops &o = sm.ops[c & 1];
+    const int buf = c & 1;
+    const int nvalid = min(L, T - c * L);
+    if (y_wave) {
+      const int trow = 32 * tile_r + l32;
+      f32x16 Y = {};
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int ib = 2 * part + q;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Sacc[q][e] *= sm.pl[16 * ib + 4 * g + e];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 ah = ld8(&sm.kh_hi[16 * ib + l16][32 * s + 8 * g]);
-        const bf16x8 al = ld8(&sm.kh_lo[16 * ib + l16][32 * s + 8 * g]);
-        const bf16x8 bv = ld8(&sm.vt[jcol][32 * s + 8 * g]);
-        Sacc[q] = mfma(ah, bv, Sacc[q]);
-        Sacc[q] = mfma(al, bv, Sacc[q]);
+      for (int s = 0; s < 4; ++s) {  // rbar S0, K = key row
+        const bf16x8 ah = ld8(&o.rb_hi[trow][16 * s + 8 * hh]);
+        const bf16x8 al = ld8(&o.rb_lo[trow][16 * s + 8 * hh]);
+        const bf16x8 bh = ld8(&sm.st_hi[buf][jcol][16 * s + 8 * hh]);
+        const bf16x8 bl = ld8(&sm.st_lo[buf][jcol][16 * s + 8 * hh]);
+        Y = mfma32(ah, bh, Y);
+        Y = mfma32(ah, bl, Y);
+        Y = mfma32(al, bh, Y);
       }
+      const int nks = 2 * (tile_r + 1);
+      for (int s = 0; s < nks; ++s) {  // A V, K = key token (causal: up to the tile's last token)
+        const bf16x8 ah = ld8(&sm.a_hi[trow][16 * s + 8 * hh]);
+        const bf16x8 al = ld8(&sm.a_lo[trow][16 * s + 8 * hh]);
+        const bf16x8 bv = ld8(&o.vt[jcol][16 * s + 8 * hh]);
+        Y = mfma32(ah, bv, Y);
+        Y = mfma32(al, bv, Y);
+      }
+      float *yp = p.y + (tok0 + (long)c * L) * C + h * kHead + jcol;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = 32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (t < nvalid) yp[(long)t * C] = Y[e];
+      }
+    } else {
+      // S += ktil^T V, K = key token, in two 32-token blocks.  The transpose
+      // T[s][i] = sum_i' ktil[s][i'] I[i'][i] leaves lane (i, hh) holding tokens
+      // 32sb + 8q + 4hh + (0..3); K step ks of the update uses q = 2ks, 2ks+1, so
+      // operand slot e maps to token 32sb + 16ks + 8(e/4) + 4hh + e%4, and V is
+      // read in that same order.
+      const int irow = 32 * tile_r + l32;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        uint32_t hp[8], lp[8];  // transposed ktil hi / lo of this token block, as packed bf16 pairs
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const uint16_t(*src)[RS] = part ? o.kt_lo : o.kt_hi;
+          f32x16 Tr = {};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int kbase = 32 * tile_r + 16 * ks + 8 * hh;  // channels i' of this K step
+            bf16x8 id;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) id[e] = (kbase + e == irow) ? (__bf16)1.0f : (__bf16)0.0f;
+            Tr = mfma32(ld8(&src[32 * sb + l32][kbase]), id, Tr);
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) (part ? lp : hp)[q] = pack_bf16(Tr[2 * q], Tr[2 * q + 1]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 ah = as_bf16x8(hp[4 * ks], hp[4 * ks + 1], hp[4 * ks + 2], hp[4 * ks + 3]);
+          const bf16x8 al = as_bf16x8(lp[4 * ks], lp[4 * ks + 1], lp[4 * ks + 2], lp[4 * ks + 3]);
+          const int s0 = 32 * sb + 16 * ks + 4 * hh;
+          const bf16x8 bv = ld4x2(&o.vt[jcol][s0], &o.vt[jcol][s0 + 8]);
+          S = mfma32(ah, bv, S);
+          S = mfma32(al, bv, S);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 pl4 = *reinterpret_cast<const float4 *>(&o.pl[32 * tile_r + 8 * q + 4 * hh]);
+        S[4 * q] *= pl4.x;
+        S[4 * q + 1] *= pl4.y;
+        S[4 * q + 2] *= pl4.z;
+        S[4 * q + 3] *= pl4.w;
+      }
+      publish_state(buf ^ 1);
     }
-    publish_state(buf ^ 1);
-    __syncthreads();
+  };
+
+  // Iteration c: producers prepare chunk c + 1 while consumers process chunk c.
+  // The two roles run separate loops (so each keeps only its own registers
+  // live) that execute the same number of workgroup barriers.
+  if (producer) {
+    prefetch(0);
+    for (int c = -1; c < nchunks; ++c) {
+      if (c + 1 < nchunks) produce1(c + 1);
+      __syncthreads();
+      if (c + 1 < nchunks) produce2(c + 1);
+      __syncthreads();
+    }
+  } else {
+    for (int c = -1; c < nchunks; ++c) {
+      if (c >= 0) consume1(c);
+      __syncthreads();
+      if (c >= 0) consume2(c);
+      __syncthreads();
+    }
   }
 
   if (tid == 0 && sm.range_bad && p.dev_status) atomicOr(p.dev_status, WKV_DEV_DECAY_RANGE);
-  if (p.state_out) {
+  if (!producer && !y_wave && p.state_out) {
+    float *sp = p.state_out + ((long)b * p.H + h) * (kHead * kHead);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int ib = 2 * part + q;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * ib + 4 * g + e;
-        p.state_out[(((long)b * p.H + h) * kHead + i) * kHead + jcol] = Sacc[q][e];
-      }
-    }
+    for (int e = 0; e < 16; ++e) sp[(32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3)) * kHead + jcol] = S[e];
   }
 }
 
 template <bool V6>
 hipError_t launch(const ScanParams &p, hipStream_t s) {
   const size_t lds = sizeof(Smem);
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&wkv56_chunked_kernel<V6>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&wkv56_chunked_kernel<V6>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   dim3 grid(p.H, p.units);
   hipLaunchKernelGGL((wkv56_chunked_kernel<V6>), grid, dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
-
-size_t wkv56_chunked_lds_bytes() { return sizeof(Smem); }
 
 hipError_t launch_wkv56_chunked(const ScanParams &p, bool v6, bool bf16, hipStream_t s) {
   if (!bf16) return hipErrorInvalidValue;  // the ABI layer routes fp32 inputs to the scan
