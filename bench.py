@@ -77,7 +77,7 @@ def kernel_digest(algo):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(algo, workload, launches_bytes):
+def measured_traffic(algo, workload):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
     was taken on the kernel source as it stands (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -183,11 +183,14 @@ def main():
     avg_kernel_s = float(np.mean(kernel_ms)) / 1000.0
     achieved = alg_bytes / avg_kernel_s / 1e9
     workload = f"wkv6_B{B}_T{T}_H{H}_N{N}_bf16"
-    traffic = measured_traffic(algo, workload, alg_bytes)
+    traffic = measured_traffic(algo, workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": KERNEL_NAMES[algo], "algorithmic_bytes_per_launch": alg_bytes,
                 "avg_kernel_ms": round(avg_kernel_s * 1000.0, 4)}
+    if traffic is not None:
+        # measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) over the same time
+        roofline["traffic_GBs"] = round(traffic / avg_kernel_s / 1e9, 1)
     if algo == "scan":
         # The token-sequential scan is bound by the vector ALUs: 3 fp32 FMA-class ops per state element
         # and token (64 per token-channel), packed FP32 off, so the peak is the unpacked fp32 rate

@@ -46,6 +46,8 @@
 //       layout as the A operand of ktil^T V by reading V in the matching
 //       permuted token order.  The state goes to the output waves as bf16
 //       hi / lo S^T in a ping-pong buffer.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "wkv.h"
@@ -113,6 +115,27 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Cross-lane helpers without address arithmetic: quad permutes on DPP, other
+// xor distances inside 32-lane groups on the LDS swizzle crossbar.
+__device__ __forceinline__ float xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+template <int M>
+__device__ __forceinline__ float xor_swz(float x) {  // M in {4, 8, 16}
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (M << 10)));
+}
+
+// A wave-uniform 64-bit value the compiler cannot rewrite into per-lane
+// induction variables (keeps per-chunk bases in scalar registers).
+__device__ __forceinline__ long uniform64(long x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long)x >> 32));
+  return (long)(((unsigned long)hi << 32) | lo);
+}
+
 // Keeps the compiler from moving work on a prefetched register above this
 // point, so the wait for the load lands here.
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
@@ -146,9 +169,9 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   // ---------------- producer roles: channels 2cp, 2cp+1; tokens 4tg .. 4tg+3 of a chunk
   const int cp = tid & 31;
   const int tg = (tid >> 5) & 15;
-  const int pwave = (tid >> 6) & 7;
+  const int pwave = wave_u & 7;
   // ---------------- consumer roles
-  const int cw = (tid >> 6) & 7;         // consumer wave 0..7
+  const int cw = wave_u & 7;             // consumer wave 0..7
   const bool y_wave = cw < 4;            // M2: output tile / state tile
   const int tile_r = (cw & 3) >> 1;      // token block (output) / key-row block (state)
   const int tile_c = cw & 1;             // value-column block
@@ -196,24 +219,37 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     u2 = *reinterpret_cast<const float2 *>(p.u + h * kHead + 2 * cp);
     if (!V6) xs = *reinterpret_cast<const float2 *>(static_cast<const float *>(p.w) + h * kHead + 2 * cp);
   }
-  const long thr_off = (long)(4 * tg) * C + h * kHead + 2 * cp;  // element offset of this thread's first row
+  // byte offsets of this thread's four rows inside a chunk (the chunk base is wave-uniform)
+  uint32_t roff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) roff[t] = (uint32_t)(((4 * tg + t) * C + h * kHead + 2 * cp) * 2);
   uint32_t nr[4], nk[4], nv[4], nx[4];
   auto prefetch = [&](int c) {
-    const long base = (tok0 + (long)c * L) * C;
-    const int last = T - 1 - c * L - 4 * tg;  // rows past the end: read the last row, zeroed on use
+    const long base = uniform64((tok0 + (long)c * L) * C * 2);  // bytes
+    const char *pr = static_cast<const char *>(p.r) + base, *pk = static_cast<const char *>(p.k) + base;
+    const char *pv = static_cast<const char *>(p.v) + base, *pw = static_cast<const char *>(p.w) + base;
+    const int rows = T - c * L;  // rows past the end: read the chunk's last row, zeroed on use
+    uint32_t o[4];
+    if (rows >= L) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] = roff[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] = (uint32_t)((min(4 * tg + t, rows - 1) * C + h * kHead + 2 * cp) * 2);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const long e = base + thr_off + (long)min(t, last) * C;
-      nr[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.r) + e);
-      nk[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.k) + e);
-      nv[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.v) + e);
-      if (V6) nx[t] = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(p.w) + e);
+      nr[t] = *reinterpret_cast<const uint32_t *>(pr + o[t]);
+      nk[t] = *reinterpret_cast<const uint32_t *>(pk + o[t]);
+      nv[t] = *reinterpret_cast<const uint32_t *>(pv + o[t]);
+      if (V6) nx[t] = *reinterpret_cast<const uint32_t *>(pw + o[t]);
     }
   };
   uint32_t rkeep[4], kkeep[4];  // this chunk's r and k words, carried to phase 2
   float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f;
 
   // producer phase 1 of chunk c: decay, in-thread prefix, bonus, V^T, wave totals
+  const int lane_x32 = (lane ^ 32) << 2;  // ds_bpermute address of the other half-wave
   auto produce1 = [&](int c) {
     Ops &o = sm.ops[c & 1];
     const int nvalid = min(L, T - c * L);
@@ -222,14 +258,26 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       pin(nr[t]); pin(nk[t]); pin(nv[t]);
       if (V6) pin(nx[t]);
     }
+    if (nvalid < L) {  // partial last chunk: tokens past the end contribute nothing
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool valid = 4 * tg + t < nvalid;
+        nr[t] = valid ? nr[t] : 0u;
+        nk[t] = valid ? nk[t] : 0u;
+        nv[t] = valid ? nv[t] : 0u;
+        if (V6) nx[t] = valid ? nx[t] : 0xff80ff80u;  // x = -inf: decay exactly 1
+      }
+    }
+    // V^T: tokens 4tg..4tg+3 of channels 2cp (low halves) and 2cp+1 (high halves)
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp][4 * tg]) =
+        make_uint2(__builtin_amdgcn_perm(nv[1], nv[0], 0x05040100u), __builtin_amdgcn_perm(nv[3], nv[2], 0x05040100u));
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp + 1][4 * tg]) =
+        make_uint2(__builtin_amdgcn_perm(nv[1], nv[0], 0x07060302u), __builtin_amdgcn_perm(nv[3], nv[2], 0x07060302u));
     float bon[4];
-    uint32_t vraw[4];
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bool valid = 4 * tg + t < nvalid;
-      const uint32_t rw = valid ? nr[t] : 0u, kw = valid ? nk[t] : 0u;
-      vraw[t] = valid ? nv[t] : 0u;
+      const uint32_t rw = nr[t], kw = nk[t];
       rkeep[t] = rw;
       kkeep[t] = kw;
       const float r0 = bf16_bits_to_f32(rw & 0xffffu), r1 = __uint_as_float(rw & 0xffff0000u);
@@ -240,49 +288,55 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
         x1 = __uint_as_float(nx[t] & 0xffff0000u);
       }
       // log2 of the decay exp(-exp(x)) is -exp(x) * log2(e)
-      const float l0 = valid ? -fast_exp(x0) * 1.4426950408889634f : 0.f;
-      const float l1 = valid ? -fast_exp(x1) * 1.4426950408889634f : 0.f;
-      run0 += l0;
-      run1 += l1;
+      run0 -= fast_exp(x0) * 1.4426950408889634f;
+      run1 -= fast_exp(x1) * 1.4426950408889634f;
       cum0[t] = run0;
       cum1[t] = run1;
       bon[t] = fmaf(r1 * u2.y, k1, r0 * u2.x * k0);
     }
+    if (!V6 && nvalid < L) {  // static decay: tokens past the end must not decay the prefix
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (4 * tg + t >= nvalid) {
+          cum0[t] = t ? cum0[t - 1] : 0.f;
+          cum1[t] = t ? cum1[t - 1] : 0.f;
+        }
+      }
+      run0 = cum0[3];
+      run1 = cum1[3];
+    }
     if (c + 1 < nchunks) prefetch(c + 1);
-    *reinterpret_cast<uint2 *>(&o.vt[2 * cp][4 * tg]) =
-        make_uint2(__builtin_amdgcn_perm(vraw[1], vraw[0], 0x05040100u), __builtin_amdgcn_perm(vraw[3], vraw[2], 0x05040100u));
-    *reinterpret_cast<uint2 *>(&o.vt[2 * cp + 1][4 * tg]) =
-        make_uint2(__builtin_amdgcn_perm(vraw[1], vraw[0], 0x07060302u), __builtin_amdgcn_perm(vraw[3], vraw[2], 0x07060302u));
     {  // bonus diagonal: sum over the 32 channel pairs of this token group (one half-wave)
       const bool up16 = lane & 16;
       float keep0 = up16 ? bon[2] : bon[0], keep1 = up16 ? bon[3] : bon[1];
-      const float send0 = up16 ? bon[0] : bon[2], send1 = up16 ? bon[1] : bon[3];
-      keep0 += __shfl_xor(send0, 16);
-      keep1 += __shfl_xor(send1, 16);
+      keep0 += xor_swz<16>(up16 ? bon[0] : bon[2]);
+      keep1 += xor_swz<16>(up16 ? bon[1] : bon[3]);
       const bool up8 = lane & 8;
       float kk = up8 ? keep1 : keep0;
-      kk += __shfl_xor(up8 ? keep0 : keep1, 8);
-      kk += __shfl_xor(kk, 4);
-      kk += __shfl_xor(kk, 2);
-      kk += __shfl_xor(kk, 1);
+      kk += xor_swz<8>(up8 ? keep0 : keep1);
+      kk += xor_swz<4>(kk);
+      kk += xor2(kk);
+      kk += xor1(kk);
       if ((lane & 7) == 0) o.bonus[4 * tg + (up16 ? 2 : 0) + (up8 ? 1 : 0)] = kk;
     }
     // wave totals: the upper half-wave (odd token group) adds the lower one's total
-    lower0 = __shfl_xor(run0, 32);
-    lower1 = __shfl_xor(run1, 32);
+    lower0 = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_x32, __float_as_int(run0)));
+    lower1 = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_x32, __float_as_int(run1)));
     if (hh) sm.wtot[pwave][cp] = make_float2(run0 + lower0, run1 + lower1);
   };
 
   // producer phase 2 of chunk c: prefix, scaled operands, bf16 hi / lo
   auto produce2 = [&](int c) {
     Ops &o = sm.ops[c & 1];
+    float2 wt[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) wt[w] = sm.wtot[w][cp];
     float pre0 = hh ? lower0 : 0.f, pre1 = hh ? lower1 : 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      const float2 wt = sm.wtot[w][cp];
-      if (w < pwave) { pre0 += wt.x; pre1 += wt.y; }
-      tot0 += wt.x;
-      tot1 += wt.y;
+      if (w == pwave) { pre0 += tot0; pre1 += tot1; }  // pwave is wave-uniform: a scalar branch
+      tot0 += wt[w].x;
+      tot1 += wt[w].y;
     }
     if (tg == 0) *reinterpret_cast<float2 *>(&o.pl[2 * cp]) =
         make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
@@ -306,36 +360,41 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
 
   // consumer M1 of chunk c: causal A^T tiles, masked, stored as A hi / lo
   constexpr unsigned long long kM1Sb = 0x3210210100ull, kM1Tb = 0x3333222110ull;  // tile ti: (sb, tb) nibbles
+  auto m1_tile = [&](const Ops &o, int ti) {
+    const int sb = (int)((kM1Sb >> (4 * ti)) & 15), tb = (int)((kM1Tb >> (4 * ti)) & 15);
+    const int t = 16 * tb + l16;
+    bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      ah[s] = ld8(&o.kt_hi[16 * sb + l16][32 * s + 8 * g4]);
+      al[s] = ld8(&o.kt_lo[16 * sb + l16][32 * s + 8 * g4]);
+      bh[s] = ld8(&o.rb_hi[t][32 * s + 8 * g4]);
+      bl[s] = ld8(&o.rb_lo[t][32 * s + 8 * g4]);
+    }
+    const float bon = o.bonus[t];
+    f32x4 At = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      At = mfma16(ah[s], bh[s], At);
+      At = mfma16(ah[s], bl[s], At);
+      At = mfma16(al[s], bh[s], At);
+    }
+    // lane holds A^T[s = 16sb + 4g4 + e][t]; keep s < t, put the bonus on s == t
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int sidx = 16 * sb + 4 * g4 + e;
+      At[e] = sidx < t ? At[e] : (sidx == t ? bon : 0.f);
+    }
+    uint32_t h0, l0, h1, l1;
+    split2(At[0], At[1], h0, l0);
+    split2(At[2], At[3], h1, l1);
+    *reinterpret_cast<uint2 *>(&sm.a_hi[t][16 * sb + 4 * g4]) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2 *>(&sm.a_lo[t][16 * sb + 4 * g4]) = make_uint2(l0, l1);
+  };
   auto consume1 = [&](int c) {
     const Ops &o = sm.ops[c & 1];
-    for (int ti = cw; ti < 10; ti += 8) {
-      const int sb = (int)((kM1Sb >> (4 * ti)) & 15), tb = (int)((kM1Tb >> (4 * ti)) & 15);
-      f32x4 At = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 ah = ld8(&o.kt_hi[16 * sb + l16][32 * s + 8 * g4]);
-        const bf16x8 al = ld8(&o.kt_lo[16 * sb + l16][32 * s + 8 * g4]);
-        const bf16x8 bh = ld8(&o.rb_hi[16 * tb + l16][32 * s + 8 * g4]);
-        const bf16x8 bl = ld8(&o.rb_lo[16 * tb + l16][32 * s + 8 * g4]);
-        At = mfma16(ah, bh, At);
-        At = mfma16(ah, bl, At);
-        At = mfma16(al, bh, At);
-      }
-      // lane holds A^T[s = 16sb + 4g4 + e][t = 16tb + l16]
-      const int t = 16 * tb + l16;
-      if (sb == tb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = 16 * sb + 4 * g4 + e;
-          At[e] = s < t ? At[e] : (s == t ? o.bonus[t] : 0.f);
-        }
-      }
-      uint32_t h0, l0, h1, l1;
-      split2(At[0], At[1], h0, l0);
-      split2(At[2], At[3], h1, l1);
-      *reinterpret_cast<uint2 *>(&sm.a_hi[t][16 * sb + 4 * g4]) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2 *>(&sm.a_lo[t][16 * sb + 4 * g4]) = make_uint2(l0, l1);
-    }
+    m1_tile(o, cw);
+    if (cw < 2) m1_tile(o, cw + 8);
   };
 
   // consumer M2 of chunk c
@@ -347,28 +406,48 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       const int trow = 32 * tile_r + l32;
       f32x16 Y = {};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {  // rbar S0, K = key row
-        const bf16x8 ah = ld8(&o.rb_hi[trow][16 * s + 8 * hh]);
-        const bf16x8 al = ld8(&o.rb_lo[trow][16 * s + 8 * hh]);
-        const bf16x8 bh = ld8(&sm.st_hi[buf][jcol][16 * s + 8 * hh]);
-        const bf16x8 bl = ld8(&sm.st_lo[buf][jcol][16 * s + 8 * hh]);
-        Y = mfma32(ah, bh, Y);
-        Y = mfma32(ah, bl, Y);
-        Y = mfma32(al, bh, Y);
+      for (int s2 = 0; s2 < 4; s2 += 2) {  // rbar S0, K = key row, two K steps per batch of loads
+        bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int col = 16 * (s2 + q) + 8 * hh;
+          ah[q] = ld8(&o.rb_hi[trow][col]);
+          al[q] = ld8(&o.rb_lo[trow][col]);
+          bh[q] = ld8(&sm.st_hi[buf][jcol][col]);
+          bl[q] = ld8(&sm.st_lo[buf][jcol][col]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          Y = mfma32(ah[q], bh[q], Y);
+          Y = mfma32(ah[q], bl[q], Y);
+          Y = mfma32(al[q], bh[q], Y);
+        }
       }
-      const int nks = 2 * (tile_r + 1);
-      for (int s = 0; s < nks; ++s) {  // A V, K = key token (causal: up to the tile's last token)
-        const bf16x8 ah = ld8(&sm.a_hi[trow][16 * s + 8 * hh]);
-        const bf16x8 al = ld8(&sm.a_lo[trow][16 * s + 8 * hh]);
-        const bf16x8 bv = ld8(&o.vt[jcol][16 * s + 8 * hh]);
-        Y = mfma32(ah, bv, Y);
-        Y = mfma32(al, bv, Y);
+      // A V, K = key token (causal: up to the tile's last token)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (half > tile_r) break;
+        bf16x8 xh[2], xl[2], bv[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int col = 32 * half + 16 * s + 8 * hh;
+          xh[s] = ld8(&sm.a_hi[trow][col]);
+          xl[s] = ld8(&sm.a_lo[trow][col]);
+          bv[s] = ld8(&o.vt[jcol][col]);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          Y = mfma32(xh[s], bv[s], Y);
+          Y = mfma32(xl[s], bv[s], Y);
+        }
       }
-      float *yp = p.y + (tok0 + (long)c * L) * C + h * kHead + jcol;
+      char *yb = reinterpret_cast<char *>(p.y) + uniform64(((tok0 + (long)c * L) * C + h * kHead) * 4);
+      const uint32_t lane_off = (uint32_t)((jcol + (32 * tile_r + 4 * hh) * C) * 4);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = 32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3);
-        if (t < nvalid) yp[(long)t * C] = Y[e];
+        if (nvalid == L || t < nvalid)
+          *reinterpret_cast<float *>(yb + lane_off + (uint32_t)((8 * (e >> 2) + (e & 3)) * C * 4)) = Y[e];
       }
     } else {
       // S += ktil^T V, K = key token, in two 32-token blocks.  The transpose
@@ -377,28 +456,34 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       // operand slot e maps to token 32sb + 16ks + 8(e/4) + 4hh + e%4, and V is
       // read in that same order.
       const int irow = 32 * tile_r + l32;
+      bf16x8 id[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kbase = 32 * tile_r + 16 * ks + 8 * hh;  // channels i' of this K step
+#pragma unroll
+        for (int e = 0; e < 8; ++e) id[ks][e] = (kbase + e == irow) ? (__bf16)1.0f : (__bf16)0.0f;
+      }
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        uint32_t hp[8], lp[8];  // transposed ktil hi / lo of this token block, as packed bf16 pairs
+        bf16x8 src[2][2];  // [hi / lo][K step]
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const uint16_t(*src)[RS] = part ? o.kt_lo : o.kt_hi;
-          f32x16 Tr = {};
+        for (int ks = 0; ks < 2; ++ks) {
+          const int kbase = 32 * tile_r + 16 * ks + 8 * hh;
+          src[0][ks] = ld8(&o.kt_hi[32 * sb + l32][kbase]);
+          src[1][ks] = ld8(&o.kt_lo[32 * sb + l32][kbase]);
+        }
+        f32x16 Th = {}, Tl = {};
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int kbase = 32 * tile_r + 16 * ks + 8 * hh;  // channels i' of this K step
-            bf16x8 id;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) id[e] = (kbase + e == irow) ? (__bf16)1.0f : (__bf16)0.0f;
-            Tr = mfma32(ld8(&src[32 * sb + l32][kbase]), id, Tr);
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q) (part ? lp : hp)[q] = pack_bf16(Tr[2 * q], Tr[2 * q + 1]);
+        for (int ks = 0; ks < 2; ++ks) {
+          Th = mfma32(src[0][ks], id[ks], Th);
+          Tl = mfma32(src[1][ks], id[ks], Tl);
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 ah = as_bf16x8(hp[4 * ks], hp[4 * ks + 1], hp[4 * ks + 2], hp[4 * ks + 3]);
-          const bf16x8 al = as_bf16x8(lp[4 * ks], lp[4 * ks + 1], lp[4 * ks + 2], lp[4 * ks + 3]);
+          const bf16x8 ah = as_bf16x8(pack_bf16(Th[8 * ks + 0], Th[8 * ks + 1]), pack_bf16(Th[8 * ks + 2], Th[8 * ks + 3]),
+                                      pack_bf16(Th[8 * ks + 4], Th[8 * ks + 5]), pack_bf16(Th[8 * ks + 6], Th[8 * ks + 7]));
+          const bf16x8 al = as_bf16x8(pack_bf16(Tl[8 * ks + 0], Tl[8 * ks + 1]), pack_bf16(Tl[8 * ks + 2], Tl[8 * ks + 3]),
+                                      pack_bf16(Tl[8 * ks + 4], Tl[8 * ks + 5]), pack_bf16(Tl[8 * ks + 6], Tl[8 * ks + 7]));
           const int s0 = 32 * sb + 16 * ks + 4 * hh;
           const bf16x8 bv = ld4x2(&o.vt[jcol][s0], &o.vt[jcol][s0 + 8]);
           S = mfma32(ah, bv, S);
@@ -447,10 +532,19 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
 
 template <bool V6>
 hipError_t launch(const ScanParams &p, hipStream_t s) {
+  // The dynamic-LDS limit is a per-device function attribute: set it once per device.
+  static std::atomic<unsigned long long> configured{0};
   const size_t lds = sizeof(Smem);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&wkv56_chunked_kernel<V6>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  const unsigned long long bit = 1ull << (dev & 63);
+  if (!(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&wkv56_chunked_kernel<V6>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured.fetch_or(bit, std::memory_order_acq_rel);
+  }
   dim3 grid(p.H, p.units);
   hipLaunchKernelGGL((wkv56_chunked_kernel<V6>), grid, dim3(kThreads), lds, s, p);
   return hipGetLastError();
