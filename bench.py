@@ -1,16 +1,23 @@
 #!/usr/bin/env python3
-"""Throughput of the WKV6 forward on one MI355X.
+"""Throughput of the WKV forward on one MI355X.
 
-Default workload: WKV6 forward, B=8, T=4096, H=32, N=64 (C=2048); r, k, v ~
-N(0, 0.5) and the decay parameter x ~ U(-6, 0) stored as bf16, u ~ N(0, 0.5)
-fp32, zero initial state, fp32 output and final state (seeded, synthetic).
-One step = one wkv6_forward call over the whole batch (inputs resident in
-HBM).  Prints one JSON line with the throughput in tokens*channels/s, the
-roofline of the kernel (algorithmic bytes / HIP-event kernel time against the
-8 TB/s HBM peak) and the fp64 CPU oracle timed on a bounded sample of the
-same workload.
+Default workload (``--workload wkv6``): WKV6 forward, B=8, T=4096, H=32, N=64
+(C=2048); r, k, v ~ N(0, 0.5) and the decay parameter x ~ U(-6, 0) stored as
+bf16, u ~ N(0, 0.5) fp32, zero initial state, fp32 output and final state
+(seeded, synthetic).  One step = one wkv6_forward call over the whole batch,
+inputs resident in HBM.  Prints one JSON line with the throughput in
+tokens*channels/s, the roofline of the dominant kernel (algorithmic bytes or
+flops per launch over its HIP-event duration, against the MI355X peak) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--algo auto|scan|chunked]
+Other workloads (same JSON layout, not the headline):
+  wkv5     v5 static decay, B=8 T=4096 H=32 N=64, bf16 r/k/v, fp32 decay/u
+  wkv4     v4, B=8 T=1024 C=2048, fp32 r/k/v, then one T=1 decode step
+  decode   one T=1 v6 step for 64 slots in place on [64, 32, 64, 64] fp32 states
+  serving  64 slots with prompts ~ U{1..2048} fed through a 128-token budget per
+           call (round robin), then 256 T=1 decode steps
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload wkv6] [--algo auto|scan|chunked]
 """
 from __future__ import annotations
 
@@ -23,12 +30,14 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-METRIC = "WKV6 fwd tokens·channels/s + % HBM peak (rocprof), B=8 T=4096 H=32 N=64"
+# fp32 vector peak with packed FP32 disabled: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
+VALU_PEAK_TFLOPS = 78.6
 KERNEL_SOURCES = {
-    "scan": ["wkv56_scan.hip"],
-    "chunked": ["wkv56_chunked.hip"],
+    "wkv56_scan_kernel": ["wkv56_scan.hip"],
+    "wkv56_chunked_kernel": ["wkv56_chunked.hip"],
+    "wkv4_scan_kernel": ["wkv4_scan.hip"],
 }
-KERNEL_NAMES = {"scan": "wkv56_scan_kernel", "chunked": "wkv56_chunked_kernel"}
+TC = "tokens·channels/s"
 
 
 def parse():
@@ -36,10 +45,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
-    ap.add_argument("--B", type=int, default=8)
-    ap.add_argument("--T", type=int, default=4096)
+    ap.add_argument("--B", type=int, default=None)
+    ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--H", type=int, default=32)
+    ap.add_argument("--budget", type=int, default=128, help="serving: tokens per call")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
@@ -69,15 +80,15 @@ def copy_calibration(args):
                       "ms_per_copy": dt * 1e3, "GBs": 2 * 4 * n / dt / 1e9}))
 
 
-def kernel_digest(algo):
+def kernel_digest(kernel):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES[algo] + ["common.hpp", "kernels.hpp"]:
+    for name in KERNEL_SOURCES[kernel] + ["common.hpp", "kernels.hpp"]:
         with open(os.path.join(ROOT, "rwkv_linear_attention_wkv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(algo, workload):
+def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
     was taken on the kernel source as it stands (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -85,46 +96,332 @@ def measured_traffic(algo, workload):
         return None
     with open(path) as f:
         table = json.load(f)
-    rec = table.get(f"{algo}:{workload}")
-    if not rec or rec.get("kernel_digest") != kernel_digest(algo):
+    rec = table.get(f"{kernel}:{workload}")
+    if not rec or rec.get("kernel_digest") != kernel_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, target_s, gpu_y=None, gpu_S=None):
-    """Time the fp64 oracle on whole (batch row, head) units of the workload."""
-    import numpy as np
-    import oracle
+# ----------------------------------------------------------------------------- workloads
+#
+# A workload builds its device inputs and returns a dict with
+#   launches: list of (label, kernel_name, callable, algorithmic_bytes, algorithmic_flops)
+#             run in order as one step
+#   tc: token*channel units per step; config, metric, dtype, data; cpu(target_s) -> (baseline, parity)
 
-    B, T, H, N = inp["B"], inp["T"], inp["H"], inp["N"]
+
+def _bf16_dev(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _oracle_units_baseline(inp, target_s, units_all, run_units, tc_per_unit, describe):
+    """Time the oracle on about target_s seconds' worth of independent units."""
+    import numpy as np
     threads = max(1, min(16, os.cpu_count() or 1))
-    oracle.load()
     rng = np.random.default_rng(123)
-    order = [(int(w) // H, int(w) % H) for w in rng.permutation(B * H)]
-    # calibrate on one unit, then size the sample to about target_s seconds
+    order = [units_all[int(i)] for i in rng.permutation(len(units_all))]
     t0 = time.perf_counter()
-    oracle.wkv56(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, units=order[:1], threads=1)
+    run_units(order[:1], 1)
     one = time.perf_counter() - t0
-    n_units = int(max(threads, min(len(order), round(target_s * threads / max(one, 1e-3)))))
-    n_units = max(threads, (n_units // threads) * threads)
-    units = order[:n_units]
+    n = int(max(threads, min(len(order), round(target_s * threads / max(one, 1e-3)))))
+    n = min(len(order), max(threads, (n // threads) * threads))
+    units = order[:n]
     t0 = time.perf_counter()
-    yo, So = oracle.wkv56(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, units=units, threads=threads)
+    out = run_units(units, threads)
     dt = time.perf_counter() - t0
-    tc = len(units) * T * N
-    res = {"value": tc / dt, "unit": "tokens·channels/s", "cores": threads, "kind": "oracle",
-           "sample": f"{len(units)} of {B * H} (batch row, head) units x T={T} tokens x N={N} channels "
-                     f"of the same workload, fp64, {dt:.1f} s wall"}
-    parity = None
-    if gpu_y is not None:
-        ys = np.stack([gpu_y[b, :, h * N:(h + 1) * N] for b, h in units])
+    tc = sum(tc_per_unit(x) for x in units) if callable(tc_per_unit) else n * tc_per_unit
+    res = {"value": tc / dt, "unit": TC, "cores": threads, "kind": "oracle",
+           "sample": f"{n} of {len(order)} {describe}, fp64, {dt:.1f} s wall"}
+    return res, units, out
+
+
+def _err(got, ref):
+    import numpy as np
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def workload_wkv56(args, version):
+    import numpy as np
+    import torch
+    import rwkv_linear_attention_wkv_amd as wkv
+    from wkv_inputs import wkv5_inputs, wkv6_inputs
+
+    B, T, H, N = args.B or 8, args.T or 4096, args.H, 64
+    C = H * N
+    inp = (wkv6_inputs if version == 6 else wkv5_inputs)(B, T, H, N, seed=args.seed)
+    r, k, v = (_bf16_dev(inp[n]) for n in ("r", "k", "v"))
+    x = _bf16_dev(inp["x"]) if version == 6 else torch.from_numpy(inp["x"]).cuda()
+    u = torch.from_numpy(inp["u"]).cuda()
+    y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
+    S = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
+    algo = wkv.resolve_algo(version, B, T, H, N, args.algo)
+    fwd = wkv.wkv6_forward if version == 6 else wkv.wkv5_forward
+    kernel = "wkv56_chunked_kernel" if algo == "chunked" else "wkv56_scan_kernel"
+    tc = B * T * C
+    in_bytes = (4 if version == 6 else 3) * 2 * tc + (0 if version == 6 else 4 * C)
+    alg_bytes = in_bytes + 4 * tc + 4 * B * H * N * N + 4 * C  # inputs + y + state_out + u
+    flops = 2 * 3 * N * tc  # scan: 3 FMA per state element and token
+
+    def run():
+        fwd(r, k, v, x, u, H, algo=algo, y=y, state_out=S)
+
+    def cpu(target_s):
+        import oracle
+        oracle.load()
+        units_all = [(b, h) for b in range(B) for h in range(H)]
+
+        def run_units(units, threads):
+            return oracle.wkv56(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, units=units,
+                                threads=threads)
+        res, units, (yo, So) = _oracle_units_baseline(inp, target_s, units_all, run_units, T * N,
+                                                      f"(batch row, head) units x T={T} x N={N}")
+        yg, Sg = y.cpu().numpy(), S.cpu().numpy()
+        ys = np.stack([yg[b, :, h * N:(h + 1) * N] for b, h in units])
         yos = np.stack([yo[b, :, h * N:(h + 1) * N] for b, h in units])
-        Ss = np.stack([gpu_S[b, h] for b, h in units])
-        Sos = np.stack([So[b, h] for b, h in units])
-        dy, dS = np.abs(ys - yos), np.abs(Ss - Sos)
-        parity = {"units": len(units), "y_max_abs": float(dy.max()), "y_mean_abs": float(dy.mean()),
-                  "state_max_abs": float(dS.max()), "state_mean_abs": float(dS.mean())}
-    return res, parity
+        ymax, ymean = _err(ys, yos)
+        smax, smean = _err(np.stack([Sg[b, h] for b, h in units]), np.stack([So[b, h] for b, h in units]))
+        return res, {"units": len(units), "y_max_abs": ymax, "y_mean_abs": ymean,
+                     "state_max_abs": smax, "state_mean_abs": smean}
+
+    name = f"WKV{version}"
+    return {
+        "metric": f"{name} fwd tokens·channels/s + % HBM peak (rocprof), B={B} T={T} H={H} N={N}",
+        "workload_key": f"wkv{version}_B{B}_T{T}_H{H}_N{N}_bf16",
+        "launches": [("forward", kernel, run, alg_bytes, flops)],
+        "tc": tc,
+        "dtype": "bf16" if algo == "chunked" else "fp32",
+        "compute": ("bf16 MFMA on hi/lo-split operands, fp32 accumulation" if algo == "chunked"
+                    else "fp32 vector ALU"),
+        "data": "synthetic (seeded numpy PCG64; bf16 r,k,v" + (",x" if version == 6 else "; fp32 x") +
+                "; fp32 u; zero initial state)",
+        "config": {"workload": f"{name} forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
+                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
+                   "parallelism": "single GPU"},
+        "cpu": cpu,
+    }
+
+
+def workload_wkv4(args):
+    import numpy as np
+    import torch
+    import rwkv_linear_attention_wkv_amd as wkv
+    from wkv_inputs import wkv4_inputs
+
+    B, T, C = args.B or 8, args.T or 1024, 2048
+    inp = wkv4_inputs(B, T, C, seed=args.seed, with_r=True, decode_steps=1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    tau, u, k, v, r = (dev(inp[n]) for n in ("tau", "u", "k", "v", "r"))
+    d = inp["decode"][0]
+    dk, dv, dr = dev(d["k"]), dev(d["v"]), dev(d["r"])
+    y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
+    yd = torch.empty((B, 1, C), dtype=torch.float32, device="cuda")
+    st = torch.empty((B, 3, C), dtype=torch.float32, device="cuda")
+    st2 = torch.empty((B, 3, C), dtype=torch.float32, device="cuda")
+    tc = B * (T + 1) * C
+    pre_bytes = 16 * B * T * C + 12 * B * C + 8 * C
+    dec_bytes = 16 * B * C + 24 * B * C + 8 * C
+
+    def prefill():
+        wkv.wkv4_forward(tau, u, k, v, r, y=y, state_out=st)
+
+    def decode():
+        wkv.wkv4_forward(tau, u, dk, dv, dr, st, y=yd, state_out=st2)
+
+    def cpu(target_s):
+        import oracle
+        oracle.load()
+        # whole workload if it fits the time budget, else a channel subset
+        t0 = time.perf_counter()
+        oracle.wkv4(inp["tau"][:64], inp["u"][:64], inp["k"][:1, :, :64], inp["v"][:1, :, :64],
+                    inp["r"][:1, :, :64], threads=1)
+        one = (time.perf_counter() - t0) / 64
+        threads = max(1, min(16, os.cpu_count() or 1))
+        nc = int(min(C, max(64, target_s * threads / max(one * B, 1e-9))))
+        nc = max(64, (nc // 64) * 64)
+        sl = slice(0, nc)
+        t0 = time.perf_counter()
+        yo, Ao, Bo = oracle.wkv4(inp["tau"][sl], inp["u"][sl], inp["k"][:, :, sl], inp["v"][:, :, sl],
+                                 inp["r"][:, :, sl], threads=threads)
+        dt = time.perf_counter() - t0
+        res = {"value": B * T * nc / dt, "unit": TC, "cores": threads, "kind": "oracle",
+               "sample": f"channels 0..{nc - 1} of {C} for all B={B} rows x T={T} tokens (prefill), fp64, "
+                         f"{dt:.1f} s wall"}
+        yg = y.cpu().numpy()[:, :, sl].astype(np.float64)
+        sg = st.cpu().numpy().astype(np.float64)[:, :, sl]
+        Ag, Bg = sg[:, 0] * np.exp(sg[:, 2]), sg[:, 1] * np.exp(sg[:, 2])
+        def rel(g, o):  # max |g - o| / max(|o|, rms(o)), the fp32 parity metric
+            return float((np.abs(g - o) / np.maximum(np.abs(o), np.sqrt(np.mean(o ** 2)))).max())
+        return res, {"channels": nc, "y_max_rel": rel(yg, yo), "A_max_rel": rel(Ag, Ao), "B_max_rel": rel(Bg, Bo)}
+
+    return {
+        "metric": f"WKV4 fwd tokens·channels/s + % HBM peak (rocprof), B={B} T={T} C={C} + 1 decode step",
+        "workload_key": f"wkv4_B{B}_T{T}_C{C}_f32",
+        "launches": [("prefill", "wkv4_scan_kernel", prefill, pre_bytes, 0),
+                     ("decode", "wkv4_scan_kernel", decode, dec_bytes, 0)],
+        "tc": tc,
+        "dtype": "fp32",
+        "compute": "fp32 vector ALU",
+        "data": "synthetic (seeded numpy PCG64; fp32 time_decay ~ U(-5,1), u ~ N(0,0.5), r,k,v ~ N(0,1); "
+                "zero initial state)",
+        "config": {"workload": f"WKV4 forward B={B} T={T} C={C} fp32 with sigmoid(r) gate, then one T=1 step "
+                               "from the carried state", "B": B, "T": T, "C": C, "global_batch": B, "seq_len": T,
+                   "parallelism": "single GPU"},
+        "cpu": cpu,
+    }
+
+
+def _serving_setup(args, decode_only):
+    import numpy as np
+    import torch
+    import rwkv_linear_attention_wkv_amd as wkv
+    from wkv_inputs import varlen_inputs
+
+    Sn, H, N = 64, args.H, 64
+    C = H * N
+    steps = 256
+    inp = varlen_inputs(Sn, H, N, seed=args.seed, decode_steps=steps)
+    lengths = inp["lengths"].astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    u = torch.from_numpy(inp["u"]).cuda()
+    state0 = torch.from_numpy(inp["state"]).cuda()
+    state = state0.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    launches = []
+    # prefill calls: round-robin split of a token budget per call, inputs gathered once in call order
+    calls = []
+    if not decode_only:
+        consumed = np.zeros(Sn, dtype=np.int64)
+        rows_all = []
+        while True:
+            take = wkv.schedule_round_robin(lengths - consumed, args.budget)
+            if take.sum() == 0:
+                break
+            rows = np.concatenate([np.arange(off[s] + consumed[s], off[s] + consumed[s] + take[s])
+                                   for s in range(Sn) if take[s] > 0])
+            calls.append((take.copy(), len(rows_all), len(rows)))
+            rows_all.extend(rows.tolist())
+            consumed += take
+        idx = torch.from_numpy(np.asarray(rows_all, dtype=np.int64)).cuda()
+        packed = {n: _bf16_dev(inp[n]).index_select(0, idx) for n in ("r", "k", "v", "x")}
+        y_pre = torch.empty((len(rows_all), C), dtype=torch.float32, device="cuda")
+        for take, start, n in calls:
+            tk = torch.from_numpy(take.astype(np.int32)).cuda()
+            mx = int(take.max())
+            sl = slice(start, start + n)
+            a = [packed[nm][sl] for nm in ("r", "k", "v", "x")]
+            act = int((take > 0).sum())
+
+            def run(tk=tk, a=a, sl=sl, mx=mx):
+                wkv.wkv6_forward_varlen(tk, *a, u, H, state, max_len=mx, y=y_pre[sl], dev_status=status)
+            launches.append(("prefill", "wkv56_scan_kernel", run, 12 * n * C + 2 * act * H * N * N * 4 + 4 * C,
+                             2 * 3 * N * n * C))
+    else:
+        y_pre, idx = None, None
+    ones = torch.ones(Sn, dtype=torch.int32, device="cuda")
+    dec = {n: _bf16_dev(inp["decode"][n]) for n in ("r", "k", "v", "x")}
+    y_dec = torch.empty((steps, Sn, C), dtype=torch.float32, device="cuda")
+    n_dec = 1 if decode_only else steps
+    for t in range(n_dec):
+        def run(t=t):
+            wkv.wkv6_forward_varlen(ones, dec["r"][t], dec["k"][t], dec["v"][t], dec["x"][t], u, H, state,
+                                    max_len=1, y=y_dec[t], dev_status=status)
+        launches.append(("decode", "wkv56_scan_kernel", run, 12 * Sn * C + 2 * Sn * H * N * N * 4 + 4 * C,
+                         2 * 3 * N * Sn * C))
+    return dict(inp=inp, lengths=lengths, off=off, state0=state0, state=state, status=status, launches=launches,
+                y_pre=y_pre, idx=idx, y_dec=y_dec, Sn=Sn, H=H, N=N, C=C, steps=steps, n_dec=n_dec,
+                ncalls=len(calls))
+
+
+def workload_serving(args, decode_only=False):
+    import numpy as np
+    import torch
+
+    st = _serving_setup(args, decode_only)
+    inp, lengths, off, Sn, H, N, C = st["inp"], st["lengths"], st["off"], st["Sn"], st["H"], st["N"], st["C"]
+    n_dec = st["n_dec"]
+    tc = (0 if decode_only else int(lengths.sum()) * C) + n_dec * Sn * C
+
+    def reset():
+        st["state"].copy_(st["state0"])
+
+    def parity_pass():
+        """One pass from the initial states, compared with the oracle on sampled slots."""
+        import oracle
+        reset()
+        for _, _, fn, _, _ in st["launches"]:
+            fn()
+        torch.cuda.synchronize()
+        status = int(st["status"].item())
+        sample = sorted({0, 1, int(np.argmax(lengths)), int(np.argmin(lengths)), 33, Sn - 1})
+        dec = inp["decode"]
+        if decode_only:
+            L = np.ones(len(sample), dtype=np.int64)
+            seq = {n: np.concatenate([dec[n][0, s:s + 1] for s in sample]) for n in ("r", "k", "v", "x")}
+            yg = st["y_dec"][0].cpu().numpy()
+            got = np.concatenate([yg[s:s + 1] for s in sample])
+        else:
+            L = lengths[sample] + n_dec
+            seq = {n: np.concatenate([np.concatenate([inp[n][off[s]:off[s] + lengths[s]], dec[n][:n_dec, s]])
+                                      for s in sample]) for n in ("r", "k", "v", "x")}
+            yp = torch.empty((int(lengths.sum()), C), device="cuda")
+            yp.index_copy_(0, st["idx"], st["y_pre"])
+            yp = yp.cpu().numpy()
+            yd = st["y_dec"].cpu().numpy()
+            got = np.concatenate([np.concatenate([yp[off[s]:off[s] + lengths[s]], yd[:n_dec, s]]) for s in sample])
+        yo, so = oracle.wkv6_varlen(L, seq["r"], seq["k"], seq["v"], seq["x"], inp["u"], H, N,
+                                    inp["state"][sample])
+        ymax, ymean = _err(got, yo)
+        smax, smean = _err(st["state"].cpu().numpy()[sample], so)
+        return {"slots": sample, "dev_status": status, "y_max_abs": ymax, "y_mean_abs": ymean,
+                "state_max_abs": smax, "state_mean_abs": smean}
+
+    def cpu(target_s):
+        import oracle
+        oracle.load()
+        parity = parity_pass()
+        dec = inp["decode"]
+        units_all = list(range(Sn))
+
+        def run_units(units, threads):
+            L = (np.ones(len(units), np.int64) if decode_only else lengths[units] + n_dec)
+            if decode_only:
+                seq = {n: np.concatenate([dec[n][0, s:s + 1] for s in units]) for n in ("r", "k", "v", "x")}
+            else:
+                seq = {n: np.concatenate([np.concatenate([inp[n][off[s]:off[s] + lengths[s]], dec[n][:n_dec, s]])
+                                          for s in units]) for n in ("r", "k", "v", "x")}
+            return oracle.wkv6_varlen(L, seq["r"], seq["k"], seq["v"], seq["x"], inp["u"], H, N,
+                                      inp["state"][units], threads=threads)
+        res, units, _ = _oracle_units_baseline(inp, target_s, units_all, run_units,
+                                               lambda s: (1 if decode_only else int(lengths[s]) + n_dec) * C,
+                                               "slots (prompt + decode tokens, all heads)")
+        return res, parity
+
+    if decode_only:
+        metric = f"WKV6 T=1 decode tokens·channels/s, {Sn} slots H={H} N=64, state in place"
+        cfg = {"workload": f"WKV6 T=1 decode step for {Sn} slots, H={H} N=64, bf16 tokens, fp32 states "
+                           "updated in place", "slots": Sn, "H": H, "N": 64, "global_batch": Sn, "seq_len": 1,
+               "parallelism": "single GPU"}
+        key = f"decode_S{Sn}_H{H}_N64_bf16"
+    else:
+        metric = (f"WKV6 serving tokens·channels/s, {Sn} slots H={H} N=64: prompts U{{1..2048}} at "
+                  f"{args.budget} tokens/call + {n_dec} decode steps")
+        cfg = {"workload": f"WKV6 varlen serving: {Sn} slots, H={H} N=64, prompts U{{1..2048}} split "
+                           f"round-robin at {args.budget} tokens per call ({st['ncalls']} calls), then "
+                           f"{n_dec} T=1 decode steps", "slots": Sn, "H": H, "N": 64,
+               "prompt_tokens": int(lengths.sum()), "calls": st["ncalls"], "decode_steps": n_dec,
+               "budget": args.budget, "global_batch": Sn, "seq_len": int(lengths.max()),
+               "parallelism": "single GPU"}
+        key = f"serving_S{Sn}_H{H}_N64_bf16_budget{args.budget}"
+    return {"metric": metric, "workload_key": key, "launches": st["launches"], "tc": tc, "dtype": "fp32",
+            "compute": "fp32 vector ALU (scan)",
+            "data": "synthetic (seeded numpy PCG64; bf16 r,k,v,x; fp32 u; initial states ~ N(0,0.1))",
+            "config": cfg, "cpu": cpu}
+
+
+# ----------------------------------------------------------------------------- main
 
 
 def main():
@@ -140,81 +437,82 @@ def main():
     import torch
 
     sys.path.insert(0, ROOT)
-    import rwkv_linear_attention_wkv_amd as wkv
-    from wkv_inputs import wkv6_inputs
-
-    B, T, H, N = args.B, args.T, args.H, 64
-    C = H * N
     t0 = time.perf_counter()
-    inp = wkv6_inputs(B, T, H, N, seed=args.seed)
+    if args.workload in ("wkv6", "wkv5"):
+        W = workload_wkv56(args, 6 if args.workload == "wkv6" else 5)
+    elif args.workload == "wkv4":
+        W = workload_wkv4(args)
+    else:
+        W = workload_serving(args, decode_only=args.workload == "decode")
     gen_s = time.perf_counter() - t0
-
-    def dev(a):
-        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-
-    r, k, v, x = (dev(inp[n]) for n in ("r", "k", "v", "x"))
-    u = torch.from_numpy(inp["u"]).cuda()
-    y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
-    S = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
-    algo = wkv.resolve_algo(6, B, T, H, N, args.algo)
+    launches = W["launches"]
 
     def step():
-        wkv.wkv6_forward(r, k, v, x, u, H, algo=algo, y=y, state_out=S)
+        for _, _, fn, _, _ in launches:
+            fn()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # HIP events around every launch, on the stream the binding launches on (torch's current stream)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    nl = len(launches)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nl)]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
+        for j, (_, _, fn, _, _) in enumerate(launches):
+            ev[i][j][0].record(stream)
+            fn()
+            ev[i][j][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = wall * 1000.0 / args.steps
-    tc = B * T * C
-    value = tc / (ms_per_step / 1000.0)
+    value = W["tc"] / (ms_per_step / 1000.0)
 
-    alg_bytes = 4 * 2 * tc + 4 * tc + 4 * B * H * N * N + 4 * C  # r,k,v,x bf16 + y + state_out + u
-    avg_kernel_s = float(np.mean(kernel_ms)) / 1000.0
-    achieved = alg_bytes / avg_kernel_s / 1e9
-    workload = f"wkv6_B{B}_T{T}_H{H}_N{N}_bf16"
-    traffic = measured_traffic(algo, workload)
+    # per label: summed algorithmic bytes / flops and kernel time
+    per = {}
+    for j, (label, kernel, _, nbytes, flops) in enumerate(launches):
+        t = float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)])) / 1000.0
+        d = per.setdefault(label, {"kernel": kernel, "launches": 0, "s": 0.0, "bytes": 0, "flops": 0})
+        d["launches"] += 1
+        d["s"] += t
+        d["bytes"] += nbytes
+        d["flops"] += flops
+    dom = max(per, key=lambda k: per[k]["s"])
+    D = per[dom]
+    avg_s = D["s"] / D["launches"]
+    bytes_per_launch = D["bytes"] / D["launches"]
+    achieved = D["bytes"] / D["s"] / 1e9
+    traffic = measured_traffic(D["kernel"], W["workload_key"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": KERNEL_NAMES[algo], "algorithmic_bytes_per_launch": alg_bytes,
-                "avg_kernel_ms": round(avg_kernel_s * 1000.0, 4)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": D["kernel"],
+                "launch": dom, "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                "avg_kernel_ms": round(avg_s * 1000.0, 4)}
     if traffic is not None:
         # measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) over the same time
-        roofline["traffic_GBs"] = round(traffic / avg_kernel_s / 1e9, 1)
-    if algo == "scan":
-        # The token-sequential scan is bound by the vector ALUs: 3 fp32 FMA-class ops per state element
-        # and token (64 per token-channel), packed FP32 off, so the peak is the unpacked fp32 rate
-        # 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz = 78.6 TFLOP/s.  The HBM figures stay alongside.
-        flops = 2 * 3 * 64 * tc
-        ach = flops / avg_kernel_s / 1e12
-        roofline = {"bound": "alu", "achieved": round(ach, 2), "peak": 78.6, "unit": "TFLOP/s",
-                    "frac": round(ach / 78.6, 4), "traffic": traffic, "kernel": KERNEL_NAMES[algo],
-                    "algorithmic_flops_per_launch": flops, "avg_kernel_ms": round(avg_kernel_s * 1000.0, 4),
-                    "hbm_achieved_GBs": round(achieved, 1), "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "algorithmic_bytes_per_launch": alg_bytes}
+        roofline["traffic_GBs"] = round(traffic / avg_s / 1e9, 1)
+    if D["kernel"] == "wkv56_scan_kernel" and dom == "forward":
+        # The dense token-sequential scan is bound by the vector ALUs: 3 fp32 FMA-class ops per state element
+        # and token, packed FP32 off, against the unpacked fp32 peak.  The HBM figures stay alongside.
+        ach = D["flops"] / D["s"] / 1e12
+        roofline = {"bound": "alu", "achieved": round(ach, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / VALU_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": D["kernel"],
+                    "launch": dom, "algorithmic_flops_per_launch": int(D["flops"] / D["launches"]),
+                    "avg_kernel_ms": round(avg_s * 1000.0, 4), "hbm_achieved_GBs": round(achieved, 1),
+                    "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    phases = {k: {"launches": d["launches"], "kernel_ms": round(d["s"] * 1000.0, 4),
+                  "avg_kernel_us": round(d["s"] / d["launches"] * 1e6, 2),
+                  "hbm_GBs": round(d["bytes"] / d["s"] / 1e9, 1)} for k, d in per.items()}
 
-    out = {"metric": METRIC, "value": value, "unit": "tokens·channels/s", "n_gpus": 1, "steps": args.steps,
+    out = {"metric": W["metric"], "value": value, "unit": TC, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16x3-mfma/fp32" if algo == "chunked" else "fp32",
-           "data": "synthetic (seeded numpy PCG64; bf16 r,k,v,x; fp32 u; zero initial state)",
-           "config": {"workload": f"WKV6 forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
-                      "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
-                      "parallelism": "single GPU"},
-           "roofline": roofline, "input_gen_s": round(gen_s, 2)}
+           "vs_baseline": None, "dtype": W["dtype"], "compute": W["compute"], "data": W["data"],
+           "config": W["config"], "roofline": roofline, "phases": phases, "input_gen_s": round(gen_s, 2)}
     if not args.no_cpu_baseline:
-        yh = y.cpu().numpy().astype(np.float64)
-        Sh = S.cpu().numpy().astype(np.float64)
-        cb, parity = cpu_baseline(inp, args.cpu_seconds, yh, Sh)
+        cb, parity = W["cpu"](args.cpu_seconds)
         out["cpu_baseline"] = cb
         out["parity_vs_oracle"] = parity
     else:
