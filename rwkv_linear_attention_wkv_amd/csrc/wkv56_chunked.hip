@@ -28,25 +28,29 @@
 // limit).  Per-step decays exp(-exp(x)) with x <= 0 stay far inside it.
 //
 // Work decomposition: one 1024-thread workgroup (16 waves) per (batch row,
-// head) walks the chunks in order as a two-stage pipeline, so that the
-// vector-ALU work of one chunk overlaps the matrix-core work of the previous
-// one.  Every operand the producers write is double-buffered in LDS.
-//   producers (waves 0-7), chunk c+1: thread (channel pair cp, token group tg
-//     of 4) consumes its inputs (4-byte loads issued one chunk ahead), forms
-//     the log2-decay prefix (wave totals exchanged through LDS), and writes
-//     rbar, ktil row-major and V transposed as bf16 hi / lo; the bonus
-//     diagonal is reduced across the lanes of a half-wave.
-//   consumers (waves 8-15), chunk c:
-//     M1: the ten causal 16x16 tiles of A^T (v_mfma_f32_16x16x32_bf16),
-//       masked and stored to LDS as A hi / lo;
-//     M2: four waves own the 32x32 output tiles (v_mfma_f32_32x32x16_bf16:
-//       rbar S0 + A V); four waves own the 32x32 state tiles in fp32
-//       accumulators.  They transpose ktil on the matrix core (a product with
-//       the identity is exact for bf16 values) and reuse the accumulator
-//       layout as the A operand of ktil^T V by reading V in the matching
-//       permuted token order.  The state goes to the output waves as bf16
-//       hi / lo S^T in a ping-pong buffer.
+// head) walks the chunks in order as a pipeline with one workgroup barrier
+// per step, so that the vector-ALU work of later chunks overlaps the
+// matrix-core work of the current one.  At step i:
+//   producers (waves 0-7) finish chunk i+1 and start chunk i+2.  Thread
+//     (channel pair cp, token group tg of 4) consumes its inputs (4-byte
+//     loads issued one step ahead), forms its part of the log2-decay prefix
+//     and the bonus diagonal (reduced across the lanes of a half-wave) and
+//     posts its wave's decay total; one step later it adds the totals of the
+//     waves before it and writes rbar, ktil row-major and V transposed as
+//     bf16 hi / lo into the chunk's operand buffer.
+//   consumers (waves 8-15) process chunk i (v_mfma_f32_32x32x16_bf16):
+//     four output waves own the 32x32 output tiles.  Each forms the causal
+//     32x32 blocks of A^T that its token block needs in accumulators (the
+//     rbar registers serve both A^T = ktil rbar^T and rbar S0), masks them,
+//     splits them into bf16 hi / lo in registers and adds A V, reading V in
+//     the token order the accumulator layout gives.  Four state waves own the
+//     32x32 fp32 state tiles: they transpose ktil on the matrix core (a
+//     product with the identity is exact for bf16 values), add ktil^T V in
+//     the same permuted token order, rescale, and publish the state as bf16
+//     hi / lo S^T in a ping-pong buffer for the next chunk's outputs.
+// Operand buffers and the decay totals are double-buffered in LDS.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -74,9 +78,8 @@ struct Ops {                      // one chunk's operands, written by the produc
 
 struct Smem {
   Ops ops[2];
-  uint16_t a_hi[L][RS], a_lo[L][RS];                  // A   [query token][key token]
   uint16_t st_hi[2][kHead][RS], st_lo[2][kHead][RS];  // S^T [value col][key row], ping-pong
-  float2 wtot[8][32];                                 // log2-decay total of each producer wave, per channel pair
+  float2 wtot[2][8][32];                              // log2-decay total of each producer wave, per channel pair
   int range_bad;
 };
 
@@ -103,6 +106,16 @@ __device__ __forceinline__ bf16x8 ld4x2(const uint16_t *p0, const uint16_t *p1) 
   const uint2 a = *reinterpret_cast<const uint2 *>(p0);
   const uint2 b = *reinterpret_cast<const uint2 *>(p1);
   return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// ds_read_b64_tr_b16: within each group of 16 lanes, source lane 4a + b
+// points at 4 consecutive bf16 values; result lane i receives element i % 4
+// of source lanes 4e + i / 4 (e = 0..3).  With source lane 4a + b at
+// &M[t0 + a][c0 + 4b] of a row-major M, lane i gets M[t0 + e][c0 + i]: a
+// column of four rows, i.e. a transposed read.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_tr(const uint16_t *p) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(p));
+  return __builtin_bit_cast(uint2, r);
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
@@ -177,8 +190,6 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   const int tile_c = cw & 1;             // value-column block
   const int l32 = lane & 31;
   const int jcol = 32 * tile_c + l32;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
 
   f32x16 S = {};  // state waves: rows 32*tile_r + 8*(e/4) + 4*hh + e%4, column jcol
   auto publish_state = [&](int buf) {
@@ -200,15 +211,6 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       for (int e = 0; e < 16; ++e) S[e] = sp[(32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3)) * kHead + jcol];
     }
     if (!y_wave) publish_state(0);
-    // A tiles that the causal mask zeroes but the 32-wide K steps of A V read
-    // (rows 0-15 x cols 16-31 and rows 32-47 x cols 48-63): zero them once.
-    const int ct = tid - 512;
-    if (ct < 128) {
-      const int region = ct >> 6, rem = ct & 63;
-      const int row = 32 * region + (rem >> 2), col = 16 + 32 * region + 4 * (rem & 3);
-      *reinterpret_cast<uint2 *>(&sm.a_hi[row][col]) = make_uint2(0u, 0u);
-      *reinterpret_cast<uint2 *>(&sm.a_lo[row][col]) = make_uint2(0u, 0u);
-    }
   } else if (tid == 0) {
     sm.range_bad = 0;
   }
@@ -245,13 +247,13 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       if (V6) nx[t] = *reinterpret_cast<const uint32_t *>(pw + o[t]);
     }
   };
-  uint32_t rkeep[4], kkeep[4];  // this chunk's r and k words, carried to phase 2
-  float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f;
+  // carried from phase 1 to phase 2 of a chunk (one pipeline step apart)
+  uint32_t rkeep[4], kkeep[4], vkeep[4];
+  float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f, bonus_keep = 0.f;
 
-  // producer phase 1 of chunk c: decay, in-thread prefix, bonus, V^T, wave totals
+  // producer phase 1 of chunk c: decay, in-thread prefix, bonus, wave totals
   const int lane_x32 = (lane ^ 32) << 2;  // ds_bpermute address of the other half-wave
   auto produce1 = [&](int c) {
-    Ops &o = sm.ops[c & 1];
     const int nvalid = min(L, T - c * L);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -268,11 +270,6 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
         if (V6) nx[t] = valid ? nx[t] : 0xff80ff80u;  // x = -inf: decay exactly 1
       }
     }
-    // V^T: tokens 4tg..4tg+3 of channels 2cp (low halves) and 2cp+1 (high halves)
-    *reinterpret_cast<uint2 *>(&o.vt[2 * cp][4 * tg]) =
-        make_uint2(__builtin_amdgcn_perm(nv[1], nv[0], 0x05040100u), __builtin_amdgcn_perm(nv[3], nv[2], 0x05040100u));
-    *reinterpret_cast<uint2 *>(&o.vt[2 * cp + 1][4 * tg]) =
-        make_uint2(__builtin_amdgcn_perm(nv[1], nv[0], 0x07060302u), __builtin_amdgcn_perm(nv[3], nv[2], 0x07060302u));
     float bon[4];
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
@@ -280,6 +277,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       const uint32_t rw = nr[t], kw = nk[t];
       rkeep[t] = rw;
       kkeep[t] = kw;
+      vkeep[t] = nv[t];
       const float r0 = bf16_bits_to_f32(rw & 0xffffu), r1 = __uint_as_float(rw & 0xffff0000u);
       const float k0 = bf16_bits_to_f32(kw & 0xffffu), k1 = __uint_as_float(kw & 0xffff0000u);
       float x0 = xs.x, x1 = xs.y;
@@ -317,20 +315,20 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       kk += xor_swz<4>(kk);
       kk += xor2(kk);
       kk += xor1(kk);
-      if ((lane & 7) == 0) o.bonus[4 * tg + (up16 ? 2 : 0) + (up8 ? 1 : 0)] = kk;
+      bonus_keep = kk;  // lanes with (lane & 7) == 0 hold token 4tg + 2*up16 + up8
     }
     // wave totals: the upper half-wave (odd token group) adds the lower one's total
     lower0 = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_x32, __float_as_int(run0)));
     lower1 = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_x32, __float_as_int(run1)));
-    if (hh) sm.wtot[pwave][cp] = make_float2(run0 + lower0, run1 + lower1);
+    if (hh) sm.wtot[c & 1][pwave][cp] = make_float2(run0 + lower0, run1 + lower1);
   };
 
-  // producer phase 2 of chunk c: prefix, scaled operands, bf16 hi / lo
+  // producer phase 2 of chunk c: prefix, scaled operands as bf16 hi / lo, V^T, bonus
   auto produce2 = [&](int c) {
     Ops &o = sm.ops[c & 1];
     float2 wt[8];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) wt[w] = sm.wtot[w][cp];
+    for (int w = 0; w < 8; ++w) wt[w] = sm.wtot[c & 1][w][cp];
     float pre0 = hh ? lower0 : 0.f, pre1 = hh ? lower1 : 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -341,6 +339,12 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     if (tg == 0) *reinterpret_cast<float2 *>(&o.pl[2 * cp]) =
         make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
     if (tot0 < -kMaxLog2 || tot1 < -kMaxLog2) sm.range_bad = 1;
+    // V^T: tokens 4tg..4tg+3 of channels 2cp (low halves) and 2cp+1 (high halves)
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp][4 * tg]) = make_uint2(
+        __builtin_amdgcn_perm(vkeep[1], vkeep[0], 0x05040100u), __builtin_amdgcn_perm(vkeep[3], vkeep[2], 0x05040100u));
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp + 1][4 * tg]) = make_uint2(
+        __builtin_amdgcn_perm(vkeep[1], vkeep[0], 0x07060302u), __builtin_amdgcn_perm(vkeep[3], vkeep[2], 0x07060302u));
+    if ((lane & 7) == 0) o.bonus[4 * tg + ((lane & 16) ? 2 : 0) + ((lane & 8) ? 1 : 0)] = bonus_keep;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int tau = 4 * tg + t;
@@ -358,137 +362,127 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     }
   };
 
-  // consumer M1 of chunk c: causal A^T tiles, masked, stored as A hi / lo
-  constexpr unsigned long long kM1Sb = 0x3210210100ull, kM1Tb = 0x3333222110ull;  // tile ti: (sb, tb) nibbles
-  auto m1_tile = [&](const Ops &o, int ti) {
-    const int sb = (int)((kM1Sb >> (4 * ti)) & 15), tb = (int)((kM1Tb >> (4 * ti)) & 15);
-    const int t = 16 * tb + l16;
-    bf16x8 ah[2], al[2], bh[2], bl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      ah[s] = ld8(&o.kt_hi[16 * sb + l16][32 * s + 8 * g4]);
-      al[s] = ld8(&o.kt_lo[16 * sb + l16][32 * s + 8 * g4]);
-      bh[s] = ld8(&o.rb_hi[t][32 * s + 8 * g4]);
-      bl[s] = ld8(&o.rb_lo[t][32 * s + 8 * g4]);
-    }
-    const float bon = o.bonus[t];
-    f32x4 At = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      At = mfma16(ah[s], bh[s], At);
-      At = mfma16(ah[s], bl[s], At);
-      At = mfma16(al[s], bh[s], At);
-    }
-    // lane holds A^T[s = 16sb + 4g4 + e][t]; keep s < t, put the bonus on s == t
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int sidx = 16 * sb + 4 * g4 + e;
-      At[e] = sidx < t ? At[e] : (sidx == t ? bon : 0.f);
-    }
-    uint32_t h0, l0, h1, l1;
-    split2(At[0], At[1], h0, l0);
-    split2(At[2], At[3], h1, l1);
-    *reinterpret_cast<uint2 *>(&sm.a_hi[t][16 * sb + 4 * g4]) = make_uint2(h0, h1);
-    *reinterpret_cast<uint2 *>(&sm.a_lo[t][16 * sb + 4 * g4]) = make_uint2(l0, l1);
-  };
-  auto consume1 = [&](int c) {
-    const Ops &o = sm.ops[c & 1];
-    m1_tile(o, cw);
-    if (cw < 2) m1_tile(o, cw + 8);
-  };
-
-  // consumer M2 of chunk c
-  auto consume2 = [&](int c) {
+  // consumer work on chunk c
+  auto consume = [&](int c) {
     const Ops &o = sm.ops[c & 1];
     const int buf = c & 1;
     const int nvalid = min(L, T - c * L);
     if (y_wave) {
-      const int trow = 32 * tile_r + l32;
-      f32x16 Y = {};
+      // Output tile: tokens 32 TB + (0..31) x value columns 32 tile_c + (0..31),
+      // accumulated transposed (Y^T) so that each lane ends up with one token's
+      // columns.  Per K step q (key rows 16q + 8hh + 0..7) the lane's rbar row
+      // is the B operand of both
+      //   Y^T += S0^T rbar^T     (S^T rows from LDS as the A operand)
+      //   AT  += ktil rbar^T     (ktil rows of each causal s-block as the A operand)
+      // AT then holds A^T[s = 32 sb + 8(e/4) + 4hh + e%4][t] in lane (t, hh).
+      auto out_tile = [&](auto tb_c) {
+        constexpr int TB = decltype(tb_c)::value;
+        const int trow = 32 * TB + l32;
+        f32x16 Y = {}, AT[TB + 1];
 #pragma unroll
-      for (int s2 = 0; s2 < 4; s2 += 2) {  // rbar S0, K = key row, two K steps per batch of loads
-        bf16x8 ah[2], al[2], bh[2], bl[2];
+        for (int sb = 0; sb <= TB; ++sb) AT[sb] = f32x16{};
+        // Operands of K step q.  Each group of the next step's operands is
+        // loaded as soon as the products of this step that read the same group
+        // have been issued, so the loads overlap the remaining products while
+        // only the rbar pair needs a second set of registers.
+        auto col_of = [&](int q) { return 16 * q + 8 * hh; };
+        bf16x8 rh = ld8(&o.rb_hi[trow][col_of(0)]), rl = ld8(&o.rb_lo[trow][col_of(0)]);
+        bf16x8 sh = ld8(&sm.st_hi[buf][jcol][col_of(0)]), sl = ld8(&sm.st_lo[buf][jcol][col_of(0)]);
+        bf16x8 kh[TB + 1], kl[TB + 1];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int col = 16 * (s2 + q) + 8 * hh;
-          ah[q] = ld8(&o.rb_hi[trow][col]);
-          al[q] = ld8(&o.rb_lo[trow][col]);
-          bh[q] = ld8(&sm.st_hi[buf][jcol][col]);
-          bl[q] = ld8(&sm.st_lo[buf][jcol][col]);
+        for (int sb = 0; sb <= TB; ++sb) {
+          kh[sb] = ld8(&o.kt_hi[32 * sb + l32][col_of(0)]);
+          kl[sb] = ld8(&o.kt_lo[32 * sb + l32][col_of(0)]);
         }
+        bf16x8 bv[TB + 1][2];  // V in the permuted token order of A V, loaded during the last K step
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          Y = mfma32(ah[q], bh[q], Y);
-          Y = mfma32(ah[q], bl[q], Y);
-          Y = mfma32(al[q], bh[q], Y);
+        for (int q = 0; q < 4; ++q) {
+          const int nc = col_of(q + 1);
+          Y = mfma32(sh, rh, Y);
+          Y = mfma32(sl, rh, Y);
+          Y = mfma32(sh, rl, Y);
+          __builtin_amdgcn_sched_barrier(0);
+          if (q < 3) {
+            sh = ld8(&sm.st_hi[buf][jcol][nc]);
+            sl = ld8(&sm.st_lo[buf][jcol][nc]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int sb = 0; sb <= TB; ++sb) {
+            AT[sb] = mfma32(kh[sb], rh, AT[sb]);
+            AT[sb] = mfma32(kh[sb], rl, AT[sb]);
+            AT[sb] = mfma32(kl[sb], rh, AT[sb]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q < 3) {
+              kh[sb] = ld8(&o.kt_hi[32 * sb + l32][nc]);
+              kl[sb] = ld8(&o.kt_lo[32 * sb + l32][nc]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (q < 3) {
+            rh = ld8(&o.rb_hi[trow][nc]);
+            rl = ld8(&o.rb_lo[trow][nc]);
+          } else {
+#pragma unroll
+            for (int sb = 0; sb <= TB; ++sb)
+#pragma unroll
+              for (int ks = 0; ks < 2; ++ks) {
+                const int s0 = 32 * sb + 16 * ks + 4 * hh;
+                bv[sb][ks] = ld4x2(&o.vt[jcol][s0], &o.vt[jcol][s0 + 8]);
+              }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // A V, K = key token (causal: up to the tile's last token)
+        {  // diagonal block: keep s < t, the bonus on s == t, zero above
+          const float bon = o.bonus[trow];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (half > tile_r) break;
-        bf16x8 xh[2], xl[2], bv[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int col = 32 * half + 16 * s + 8 * hh;
-          xh[s] = ld8(&sm.a_hi[trow][col]);
-          xl[s] = ld8(&sm.a_lo[trow][col]);
-          bv[s] = ld8(&o.vt[jcol][col]);
+          for (int e = 0; e < 16; ++e) {
+            const int sl = 8 * (e >> 2) + 4 * hh + (e & 3);
+            AT[TB][e] = sl < l32 ? AT[TB][e] : (sl == l32 ? bon : 0.f);
+          }
         }
+        // Y^T += V^T A^T.  K step (sb, ks) uses AT[sb][8ks .. 8ks+7] as the B operand:
+        // slot 8hh + e' is token s = 32 sb + 16 ks + 8(e'/4) + 4hh + e'%4, and V^T is
+        // read in that order.
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          Y = mfma32(xh[s], bv[s], Y);
-          Y = mfma32(xl[s], bv[s], Y);
+        for (int sb = 0; sb <= TB; ++sb) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) split2(AT[sb][8 * ks + 2 * m], AT[sb][8 * ks + 2 * m + 1], hw[m], lw[m]);
+            Y = mfma32(bv[sb][ks], as_bf16x8(hw[0], hw[1], hw[2], hw[3]), Y);
+            Y = mfma32(bv[sb][ks], as_bf16x8(lw[0], lw[1], lw[2], lw[3]), Y);
+          }
         }
-      }
-      char *yb = reinterpret_cast<char *>(p.y) + uniform64(((tok0 + (long)c * L) * C + h * kHead) * 4);
-      const uint32_t lane_off = (uint32_t)((jcol + (32 * tile_r + 4 * hh) * C) * 4);
+        // Y^T accumulators: lane (token trow, hh) holds y[trow][32 tile_c + 8m + 4hh + 0..3] in
+        // Y[4m .. 4m+3], four 16-byte stores per lane
+        char *yb = reinterpret_cast<char *>(p.y) + uniform64(((tok0 + (long)c * L) * C + h * kHead) * 4);
+        float4 *yrow = reinterpret_cast<float4 *>(yb + (uint32_t)((trow * C + 32 * tile_c + 4 * hh) * 4));
+        if (nvalid == L || trow < nvalid) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = 32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3);
-        if (nvalid == L || t < nvalid)
-          *reinterpret_cast<float *>(yb + lane_off + (uint32_t)((8 * (e >> 2) + (e & 3)) * C * 4)) = Y[e];
-      }
+          for (int m = 0; m < 4; ++m) yrow[2 * m] = make_float4(Y[4 * m], Y[4 * m + 1], Y[4 * m + 2], Y[4 * m + 3]);
+        }
+      };
+      if (tile_r) out_tile(std::integral_constant<int, 1>{});
+      else out_tile(std::integral_constant<int, 0>{});
     } else {
-      // S += ktil^T V, K = key token, in two 32-token blocks.  The transpose
-      // T[s][i] = sum_i' ktil[s][i'] I[i'][i] leaves lane (i, hh) holding tokens
-      // 32sb + 8q + 4hh + (0..3); K step ks of the update uses q = 2ks, 2ks+1, so
-      // operand slot e maps to token 32sb + 16ks + 8(e/4) + 4hh + e%4, and V is
-      // read in that same order.
-      const int irow = 32 * tile_r + l32;
-      bf16x8 id[2];
+      // S += ktil^T V over the chunk's 64 tokens in four K steps of 16.  The
+      // A operand (row = key i = 32 tile_r + lane % 32, slots 8hh + e = tokens
+      // 16 ks + 8hh + e) is read transposed from the row-major ktil: lane group
+      // g = lane / 16 covers keys 32 tile_r + 16 (g & 1) + (0..15), and its
+      // source lane 4a + b points at ktil[token 16 ks + 8hh + a (+4)][key + 4b].
+      const int g = lane >> 4;
+      const int kcol = 32 * tile_r + 16 * (g & 1) + 4 * (lane & 3);
+      const int trow0 = 8 * (g >> 1) + ((lane >> 2) & 3);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int kbase = 32 * tile_r + 16 * ks + 8 * hh;  // channels i' of this K step
-#pragma unroll
-        for (int e = 0; e < 8; ++e) id[ks][e] = (kbase + e == irow) ? (__bf16)1.0f : (__bf16)0.0f;
-      }
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        bf16x8 src[2][2];  // [hi / lo][K step]
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int kbase = 32 * tile_r + 16 * ks + 8 * hh;
-          src[0][ks] = ld8(&o.kt_hi[32 * sb + l32][kbase]);
-          src[1][ks] = ld8(&o.kt_lo[32 * sb + l32][kbase]);
-        }
-        f32x16 Th = {}, Tl = {};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          Th = mfma32(src[0][ks], id[ks], Th);
-          Tl = mfma32(src[1][ks], id[ks], Tl);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 ah = as_bf16x8(pack_bf16(Th[8 * ks + 0], Th[8 * ks + 1]), pack_bf16(Th[8 * ks + 2], Th[8 * ks + 3]),
-                                      pack_bf16(Th[8 * ks + 4], Th[8 * ks + 5]), pack_bf16(Th[8 * ks + 6], Th[8 * ks + 7]));
-          const bf16x8 al = as_bf16x8(pack_bf16(Tl[8 * ks + 0], Tl[8 * ks + 1]), pack_bf16(Tl[8 * ks + 2], Tl[8 * ks + 3]),
-                                      pack_bf16(Tl[8 * ks + 4], Tl[8 * ks + 5]), pack_bf16(Tl[8 * ks + 6], Tl[8 * ks + 7]));
-          const int s0 = 32 * sb + 16 * ks + 4 * hh;
-          const bf16x8 bv = ld4x2(&o.vt[jcol][s0], &o.vt[jcol][s0 + 8]);
-          S = mfma32(ah, bv, S);
-          S = mfma32(al, bv, S);
-        }
+      for (int ks = 0; ks < 4; ++ks) {
+        const int tr = 16 * ks + trow0;
+        const uint2 h0 = ld_tr(&o.kt_hi[tr][kcol]), h1 = ld_tr(&o.kt_hi[tr + 4][kcol]);
+        const uint2 l0 = ld_tr(&o.kt_lo[tr][kcol]), l1 = ld_tr(&o.kt_lo[tr + 4][kcol]);
+        const bf16x8 bv = ld8(&o.vt[jcol][16 * ks + 8 * hh]);
+        S = mfma32(as_bf16x8(h0.x, h0.y, h1.x, h1.y), bv, S);
+        S = mfma32(as_bf16x8(l0.x, l0.y, l1.x, l1.y), bv, S);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -502,22 +496,25 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     }
   };
 
-  // Iteration c: producers prepare chunk c + 1 while consumers process chunk c.
-  // The two roles run separate loops (so each keeps only its own registers
-  // live) that execute the same number of workgroup barriers.
+  // Step i: producers finish chunk i + 1 and start chunk i + 2 while the
+  // consumers process chunk i.  Producers, output waves and state waves run
+  // separate loops (so each keeps only its own registers live) with one
+  // workgroup barrier per step.
   if (producer) {
     prefetch(0);
-    for (int c = -1; c < nchunks; ++c) {
-      if (c + 1 < nchunks) produce1(c + 1);
+    for (int i = -2; i < nchunks; ++i) {
+      if (i >= -1 && i + 1 < nchunks) produce2(i + 1);
+      if (i + 2 < nchunks) produce1(i + 2);
       __syncthreads();
-      if (c + 1 < nchunks) produce2(c + 1);
+    }
+  } else if (y_wave) {
+    for (int i = -2; i < nchunks; ++i) {
+      if (i >= 0) consume(i);
       __syncthreads();
     }
   } else {
-    for (int c = -1; c < nchunks; ++c) {
-      if (c >= 0) consume1(c);
-      __syncthreads();
-      if (c >= 0) consume2(c);
+    for (int i = -2; i < nchunks; ++i) {
+      if (i >= 0) consume(i);
       __syncthreads();
     }
   }
