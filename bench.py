@@ -474,12 +474,13 @@ def main():
     # per label: summed algorithmic bytes / flops and kernel time
     per = {}
     for j, (label, kernel, _, nbytes, flops) in enumerate(launches):
-        t = float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)])) / 1000.0
-        d = per.setdefault(label, {"kernel": kernel, "launches": 0, "s": 0.0, "bytes": 0, "flops": 0})
+        times = [ev[i][j][0].elapsed_time(ev[i][j][1]) / 1000.0 for i in range(args.steps)]
+        d = per.setdefault(label, {"kernel": kernel, "launches": 0, "s": 0.0, "bytes": 0, "flops": 0, "times": []})
         d["launches"] += 1
-        d["s"] += t
+        d["s"] += float(np.mean(times))
         d["bytes"] += nbytes
         d["flops"] += flops
+        d["times"].extend(times)
     dom = max(per, key=lambda k: per[k]["s"])
     D = per[dom]
     avg_s = D["s"] / D["launches"]
@@ -505,6 +506,8 @@ def main():
                     "algorithmic_bytes_per_launch": int(bytes_per_launch)}
     phases = {k: {"launches": d["launches"], "kernel_ms": round(d["s"] * 1000.0, 4),
                   "avg_kernel_us": round(d["s"] / d["launches"] * 1e6, 2),
+                  "min_kernel_us": round(min(d["times"]) * 1e6, 2),
+                  "median_kernel_us": round(float(np.median(d["times"])) * 1e6, 2),
                   "hbm_GBs": round(d["bytes"] / d["s"] / 1e9, 1)} for k, d in per.items()}
 
     out = {"metric": W["metric"], "value": value, "unit": TC, "n_gpus": 1, "steps": args.steps,

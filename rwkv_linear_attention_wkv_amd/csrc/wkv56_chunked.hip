@@ -96,7 +96,9 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // Split two floats into packed hi and lo bf16 pairs.
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
   hi = pack_bf16(a, b);
-  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+  uint32_t h = hi;
+  asm("" : "+v"(h));  // widen the packed halves as they are, not by converting a again
+  lo = pack_bf16(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
 }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) {
@@ -158,8 +160,13 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
 
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  // Consecutive workgroups go to different XCDs (round robin over the 8), so
+  // batch row = id % B puts all heads of a row on one XCD (when B divides
+  // into the XCD count): they stream the same token rows at about the same
+  // time, which keeps HBM page and L2 locality.
+  const int wg = blockIdx.x;
+  const int b = wg % p.units;
+  const int h = wg / p.units;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int hh = lane >> 5;
@@ -221,65 +228,65 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     u2 = *reinterpret_cast<const float2 *>(p.u + h * kHead + 2 * cp);
     if (!V6) xs = *reinterpret_cast<const float2 *>(static_cast<const float *>(p.w) + h * kHead + 2 * cp);
   }
-  // byte offsets of this thread's four rows inside a chunk (the chunk base is wave-uniform)
+  // Token rows are read with buffer loads: one resource per input array and
+  // chunk (wave-uniform, in scalar registers) whose record count ends at the
+  // batch row's last token, so rows past it read as zero (r = k = v = 0 adds
+  // nothing); per-thread offsets are fixed.  Loaded words of chunk c live in register set c & 1 from the load
+  // (issued one step ahead) until phase 2 of chunk c, one step after phase 1.
   uint32_t roff[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) roff[t] = (uint32_t)(((4 * tg + t) * C + h * kHead + 2 * cp) * 2);
-  uint32_t nr[4], nk[4], nv[4], nx[4];
-  auto prefetch = [&](int c) {
-    const long base = uniform64((tok0 + (long)c * L) * C * 2);  // bytes
-    const char *pr = static_cast<const char *>(p.r) + base, *pk = static_cast<const char *>(p.k) + base;
-    const char *pv = static_cast<const char *>(p.v) + base, *pw = static_cast<const char *>(p.w) + base;
-    const int rows = T - c * L;  // rows past the end: read the chunk's last row, zeroed on use
-    uint32_t o[4];
-    if (rows >= L) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) o[t] = roff[t];
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) o[t] = (uint32_t)((min(4 * tg + t, rows - 1) * C + h * kHead + 2 * cp) * 2);
-    }
+  const unsigned long long row_end = (unsigned long long)(tok0 + T) * C * 2;  // end of this batch row
+  auto rsrc_at = [&](const void *base, unsigned long long off) {
+    const unsigned long long rem = off < row_end ? row_end - off : 0ull;
+    const int n = (int)(rem > 0x7fffffffull ? 0x7fffffffull : rem);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(base) + off), 0, n,
+                                             0x00020000);
+  };
+  uint32_t ld[2][3][4];  // [set][r, k, v][token of the thread's group]
+  uint32_t ldx[4];       // x words: consumed in phase 1, before the next chunk's load reuses them
+  auto prefetch = [&](int c, auto set_c) {
+    constexpr int S = decltype(set_c)::value;
+    const unsigned long long off = (unsigned long long)uniform64((tok0 + (long)c * L) * C * 2);
+    const auto rr = rsrc_at(p.r, off), rk = rsrc_at(p.k, off), rv = rsrc_at(p.v, off);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      nr[t] = *reinterpret_cast<const uint32_t *>(pr + o[t]);
-      nk[t] = *reinterpret_cast<const uint32_t *>(pk + o[t]);
-      nv[t] = *reinterpret_cast<const uint32_t *>(pv + o[t]);
-      if (V6) nx[t] = *reinterpret_cast<const uint32_t *>(pw + o[t]);
+      ld[S][0][t] = __builtin_amdgcn_raw_buffer_load_b32(rr, (int)roff[t], 0, 0);
+      ld[S][1][t] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)roff[t], 0, 0);
+      ld[S][2][t] = __builtin_amdgcn_raw_buffer_load_b32(rv, (int)roff[t], 0, 0);
+    }
+    if (V6) {
+      const auto rw = rsrc_at(p.w, off);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ldx[t] = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)roff[t], 0, 0);
     }
   };
   // carried from phase 1 to phase 2 of a chunk (one pipeline step apart)
-  uint32_t rkeep[4], kkeep[4], vkeep[4];
-  float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f, bonus_keep = 0.f;
+  float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f;
 
-  // producer phase 1 of chunk c: decay, in-thread prefix, bonus, wave totals
+  // producer phase 1 of chunk c: decay, in-thread prefix, wave totals; loads chunk c + 1
   const int lane_x32 = (lane ^ 32) << 2;  // ds_bpermute address of the other half-wave
-  auto produce1 = [&](int c) {
+  auto produce1 = [&](int c, auto set_c, auto tail_c) {
+    constexpr int S = decltype(set_c)::value;
+    constexpr bool TAIL = decltype(tail_c)::value;  // the chunk ends past the last token
     const int nvalid = min(L, T - c * L);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      pin(nr[t]); pin(nk[t]); pin(nv[t]);
-      if (V6) pin(nx[t]);
+      pin(ld[S][0][t]); pin(ld[S][1][t]); pin(ld[S][2][t]);
+      if (V6) pin(ldx[t]);
     }
-    if (nvalid < L) {  // partial last chunk: tokens past the end contribute nothing
+    uint32_t nx[4] = {0u, 0u, 0u, 0u};
+    if (V6) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bool valid = 4 * tg + t < nvalid;
-        nr[t] = valid ? nr[t] : 0u;
-        nk[t] = valid ? nk[t] : 0u;
-        nv[t] = valid ? nv[t] : 0u;
-        if (V6) nx[t] = valid ? nx[t] : 0xff80ff80u;  // x = -inf: decay exactly 1
-      }
+      for (int t = 0; t < 4; ++t) nx[t] = ldx[t];
     }
-    float bon[4];
+    if (V6 && TAIL) {  // tokens past the end do not decay (x = -inf)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) nx[t] = 4 * tg + t < nvalid ? nx[t] : 0xff80ff80u;
+    }
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t rw = nr[t], kw = nk[t];
-      rkeep[t] = rw;
-      kkeep[t] = kw;
-      vkeep[t] = nv[t];
-      const float r0 = bf16_bits_to_f32(rw & 0xffffu), r1 = __uint_as_float(rw & 0xffff0000u);
-      const float k0 = bf16_bits_to_f32(kw & 0xffffu), k1 = __uint_as_float(kw & 0xffff0000u);
       float x0 = xs.x, x1 = xs.y;
       if (V6) {
         x0 = bf16_bits_to_f32(nx[t] & 0xffffu);
@@ -290,9 +297,8 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       run1 -= fast_exp(x1) * 1.4426950408889634f;
       cum0[t] = run0;
       cum1[t] = run1;
-      bon[t] = fmaf(r1 * u2.y, k1, r0 * u2.x * k0);
     }
-    if (!V6 && nvalid < L) {  // static decay: tokens past the end must not decay the prefix
+    if (!V6 && TAIL) {  // static decay: tokens past the end must not decay the prefix
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (4 * tg + t >= nvalid) {
@@ -303,20 +309,8 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       run0 = cum0[3];
       run1 = cum1[3];
     }
-    if (c + 1 < nchunks) prefetch(c + 1);
-    {  // bonus diagonal: sum over the 32 channel pairs of this token group (one half-wave)
-      const bool up16 = lane & 16;
-      float keep0 = up16 ? bon[2] : bon[0], keep1 = up16 ? bon[3] : bon[1];
-      keep0 += xor_swz<16>(up16 ? bon[0] : bon[2]);
-      keep1 += xor_swz<16>(up16 ? bon[1] : bon[3]);
-      const bool up8 = lane & 8;
-      float kk = up8 ? keep1 : keep0;
-      kk += xor_swz<8>(up8 ? keep0 : keep1);
-      kk += xor_swz<4>(kk);
-      kk += xor2(kk);
-      kk += xor1(kk);
-      bonus_keep = kk;  // lanes with (lane & 7) == 0 hold token 4tg + 2*up16 + up8
-    }
+    // next chunk (rows past the end read as zero or belong to the next batch row; masked on use)
+    prefetch(c + 1, std::integral_constant<int, S ^ 1>{});
     // wave totals: the upper half-wave (odd token group) adds the lower one's total
     lower0 = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_x32, __float_as_int(run0)));
     lower1 = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_x32, __float_as_int(run1)));
@@ -324,34 +318,39 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   };
 
   // producer phase 2 of chunk c: prefix, scaled operands as bf16 hi / lo, V^T, bonus
-  auto produce2 = [&](int c) {
+  auto produce2 = [&](int c, auto set_c) {
+    constexpr int S = decltype(set_c)::value;
     Ops &o = sm.ops[c & 1];
-    float2 wt[8];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) wt[w] = sm.wtot[c & 1][w][cp];
+    const uint32_t *rw = ld[S][0], *kw = ld[S][1], *vw = ld[S][2];  // zero past the last token
+    // decay prefix of the waves before this one (pwave is wave-uniform) and the
+    // chunk totals, from the eight wave totals read four at a time
     float pre0 = hh ? lower0 : 0.f, pre1 = hh ? lower1 : 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      if (w == pwave) { pre0 += tot0; pre1 += tot1; }  // pwave is wave-uniform: a scalar branch
-      tot0 += wt[w].x;
-      tot1 += wt[w].y;
+    for (int half = 0; half < 2; ++half) {
+      float2 wt[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wt[q] = sm.wtot[c & 1][4 * half + q][cp];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float m = 4 * half + q < pwave ? 1.f : 0.f;
+        pre0 = fmaf(m, wt[q].x, pre0);
+        pre1 = fmaf(m, wt[q].y, pre1);
+        tot0 += wt[q].x;
+        tot1 += wt[q].y;
+      }
     }
-    if (tg == 0) *reinterpret_cast<float2 *>(&o.pl[2 * cp]) =
-        make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
-    if (tot0 < -kMaxLog2 || tot1 < -kMaxLog2) sm.range_bad = 1;
-    // V^T: tokens 4tg..4tg+3 of channels 2cp (low halves) and 2cp+1 (high halves)
-    *reinterpret_cast<uint2 *>(&o.vt[2 * cp][4 * tg]) = make_uint2(
-        __builtin_amdgcn_perm(vkeep[1], vkeep[0], 0x05040100u), __builtin_amdgcn_perm(vkeep[3], vkeep[2], 0x05040100u));
-    *reinterpret_cast<uint2 *>(&o.vt[2 * cp + 1][4 * tg]) = make_uint2(
-        __builtin_amdgcn_perm(vkeep[1], vkeep[0], 0x07060302u), __builtin_amdgcn_perm(vkeep[3], vkeep[2], 0x07060302u));
-    if ((lane & 7) == 0) o.bonus[4 * tg + ((lane & 16) ? 2 : 0) + ((lane & 8) ? 1 : 0)] = bonus_keep;
+    if (pwave == 0) {  // exp(Lam_{L-1}) per key row and the range check
+      if (!hh) *reinterpret_cast<float2 *>(&o.pl[2 * cp]) =
+          make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
+      if (tot0 < -kMaxLog2 || tot1 < -kMaxLog2) sm.range_bad = 1;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int tau = 4 * tg + t;
       const float lp0 = t ? pre0 + cum0[t - 1] : pre0, lp1 = t ? pre1 + cum1[t - 1] : pre1;
       const float la0 = pre0 + cum0[t], la1 = pre1 + cum1[t];
-      const float r0 = bf16_bits_to_f32(rkeep[t] & 0xffffu), r1 = __uint_as_float(rkeep[t] & 0xffff0000u);
-      const float k0 = bf16_bits_to_f32(kkeep[t] & 0xffffu), k1 = __uint_as_float(kkeep[t] & 0xffff0000u);
+      const float r0 = bf16_bits_to_f32(rw[t] & 0xffffu), r1 = __uint_as_float(rw[t] & 0xffff0000u);
+      const float k0 = bf16_bits_to_f32(kw[t] & 0xffffu), k1 = __uint_as_float(kw[t] & 0xffff0000u);
       uint32_t hi, lo;
       split2(r0 * __builtin_amdgcn_exp2f(lp0), r1 * __builtin_amdgcn_exp2f(lp1), hi, lo);
       *reinterpret_cast<uint32_t *>(&o.rb_hi[tau][2 * cp]) = hi;
@@ -360,6 +359,33 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       *reinterpret_cast<uint32_t *>(&o.kt_hi[tau][2 * cp]) = hi;
       *reinterpret_cast<uint32_t *>(&o.kt_lo[tau][2 * cp]) = lo;
     }
+    // bonus diagonal: the sum over the 32 channel pairs of a token group (one half-wave)
+    float bon[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float r0 = bf16_bits_to_f32(rw[t] & 0xffffu), r1 = __uint_as_float(rw[t] & 0xffff0000u);
+      const float k0 = bf16_bits_to_f32(kw[t] & 0xffffu), k1 = __uint_as_float(kw[t] & 0xffff0000u);
+      bon[t] = fmaf(r1 * u2.y, k1, r0 * u2.x * k0);
+    }
+    float bsum;
+    {
+      const bool up16 = lane & 16;
+      float keep0 = up16 ? bon[2] : bon[0], keep1 = up16 ? bon[3] : bon[1];
+      keep0 += xor_swz<16>(up16 ? bon[0] : bon[2]);
+      keep1 += xor_swz<16>(up16 ? bon[1] : bon[3]);
+      const bool up8 = lane & 8;
+      bsum = up8 ? keep1 : keep0;
+      bsum += xor_swz<8>(up8 ? keep0 : keep1);
+      bsum += xor_swz<4>(bsum);
+      bsum += xor2(bsum);
+      bsum += xor1(bsum);
+    }
+    // V^T: tokens 4tg..4tg+3 of channels 2cp (low halves) and 2cp+1 (high halves)
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp][4 * tg]) = make_uint2(
+        __builtin_amdgcn_perm(vw[1], vw[0], 0x05040100u), __builtin_amdgcn_perm(vw[3], vw[2], 0x05040100u));
+    *reinterpret_cast<uint2 *>(&o.vt[2 * cp + 1][4 * tg]) = make_uint2(
+        __builtin_amdgcn_perm(vw[1], vw[0], 0x07060302u), __builtin_amdgcn_perm(vw[3], vw[2], 0x07060302u));
+    if ((lane & 7) == 0) o.bonus[4 * tg + ((lane & 16) ? 2 : 0) + ((lane & 8) ? 1 : 0)] = bsum;
   };
 
   // consumer work on chunk c
@@ -501,11 +527,26 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   // separate loops (so each keeps only its own registers live) with one
   // workgroup barrier per step.
   if (producer) {
-    prefetch(0);
-    for (int i = -2; i < nchunks; ++i) {
-      if (i >= -1 && i + 1 < nchunks) produce2(i + 1);
-      if (i + 2 < nchunks) produce1(i + 2);
+    // step i works on chunks i + 1 (register set (i + 1) & 1) and i + 2 (set i & 1);
+    // the loop is unrolled by two so that the sets are fixed in each copy
+    auto step = [&](int i, auto par) {
+      constexpr int P = decltype(par)::value;
+      if (i >= -1 && i + 1 < nchunks) produce2(i + 1, std::integral_constant<int, P ^ 1>{});
+      if (i + 3 < nchunks || (i + 3 == nchunks && T % L == 0))
+        produce1(i + 2, std::integral_constant<int, P>{}, std::false_type{});
+      else if (i + 2 < nchunks)
+        produce1(i + 2, std::integral_constant<int, P>{}, std::true_type{});
+    };
+    prefetch(0, std::integral_constant<int, 0>{});
+    // the producers' vector-ALU chain is the longest per step: let them issue first
+    __builtin_amdgcn_s_setprio(2);
+    for (int i = -2; i < nchunks; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
       __syncthreads();
+      if (i + 1 < nchunks) {
+        step(i + 1, std::integral_constant<int, 1>{});
+        __syncthreads();
+      }
     }
   } else if (y_wave) {
     for (int i = -2; i < nchunks; ++i) {
@@ -542,7 +583,7 @@ hipError_t launch(const ScanParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  dim3 grid(p.H, p.units);
+  dim3 grid(p.H * p.units);
   hipLaunchKernelGGL((wkv56_chunked_kernel<V6>), grid, dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
