@@ -50,6 +50,37 @@ def test_varlen_small_with_empty_slots_and_map():
             assert np.array_equal(sh[row], state[row].astype(np.float64)), f"row {row} modified"
 
 
+@pytest.mark.parametrize("max_len", [8, 64])
+def test_varlen_few_tokens_many_slots(max_len):
+    """More slots than a workgroup has threads, 0..8 tokens each, a permuted map into a larger
+    state table: the few-token path (max_len <= 8) and the staged path must both match the oracle,
+    and agree with each other."""
+    H, N, S, n_state = 2, 64, 300, 320
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(0, 9, size=S).astype(np.int32)
+    inp = varlen_inputs(S, H, N, seed=53, decode_steps=0, lengths=lengths)
+    state = rng.standard_normal((n_state, H, N, N)).astype(np.float32) * 0.1
+    smap = rng.permutation(n_state)[:S].astype(np.int32)
+    st = dev(state)
+    total = int(lengths.sum())
+    y = torch.full((total, H * N), float("nan"), device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wkv.wkv6_forward_varlen(dev(lengths), dev(inp["r"]), dev(inp["k"]), dev(inp["v"]), dev(inp["x"]),
+                            dev(inp["u"]), H, st, max_len=max_len, state_map=dev(smap), y=y, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    yo, so = oracle.wkv6_varlen(lengths, inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, state,
+                                state_map=smap)
+    assert_bf16(host(y), yo, "varlen y")
+    sh = host(st)
+    touched = {int(smap[s]) for s in range(S) if lengths[s] > 0}
+    for row in range(n_state):
+        if row in touched:
+            assert_bf16(sh[row], so[row], f"varlen state row {row}")
+        else:
+            assert np.array_equal(sh[row], state[row].astype(np.float64)), f"row {row} modified"
+
+
 def test_varlen_out_of_place_copies_empty_slots():
     H, N = 1, 64
     lengths = np.array([0, 3], dtype=np.int32)
