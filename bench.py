@@ -45,7 +45,8 @@ TC = "tokens·channels/s"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for the short decode step, 5 for the serving pass)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
@@ -316,8 +317,7 @@ def _serving_setup(args, decode_only):
             a = [packed[nm][sl] for nm in ("r", "k", "v", "x")]
             act = int((take > 0).sum())
 
-            def run(tk=tk, a=a, sl=sl, mx=mx):
-                wkv.wkv6_forward_varlen(tk, *a, u, H, state, max_len=mx, y=y_pre[sl], dev_status=status)
+            run = wkv.varlen_plan(tk, *a, u, H, state, max_len=mx, y=y_pre[sl], dev_status=status)
             kname = "wkv6_varlen_short_kernel" if mx <= SHORT_MAX else "wkv56_scan_kernel"
             launches.append(("prefill", kname, run, 12 * n * C + 2 * act * H * N * N * 4 + 4 * C,
                              2 * 3 * N * n * C))
@@ -328,9 +328,8 @@ def _serving_setup(args, decode_only):
     y_dec = torch.empty((steps, Sn, C), dtype=torch.float32, device="cuda")
     n_dec = 1 if decode_only else steps
     for t in range(n_dec):
-        def run(t=t):
-            wkv.wkv6_forward_varlen(ones, dec["r"][t], dec["k"][t], dec["v"][t], dec["x"][t], u, H, state,
-                                    max_len=1, y=y_dec[t], dev_status=status)
+        run = wkv.varlen_plan(ones, dec["r"][t], dec["k"][t], dec["v"][t], dec["x"][t], u, H, state,
+                              max_len=1, y=y_dec[t], dev_status=status)
         launches.append(("decode", "wkv6_varlen_short_kernel", run, 12 * Sn * C + 2 * Sn * H * N * N * 4 + 4 * C,
                          2 * 3 * N * Sn * C))
     return dict(inp=inp, lengths=lengths, off=off, state0=state0, state=state, status=status, launches=launches,
@@ -429,6 +428,8 @@ def workload_serving(args, decode_only=False):
 
 def main():
     args = parse()
+    if args.steps is None:
+        args.steps = {"decode": 200, "serving": 5}.get(args.workload, 20)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the WKV path here runs on a "
               "single MI355X and has no multi-GPU mode.", file=sys.stderr)

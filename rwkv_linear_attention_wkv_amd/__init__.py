@@ -26,7 +26,7 @@ _lib = _native.load()
 
 _ALGOS = {"auto": WKV_ALGO_AUTO, "scan": WKV_ALGO_SCAN, "chunked": WKV_ALGO_CHUNKED}
 
-__all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_forward_varlen",
+__all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_forward_varlen", "varlen_plan", "VarlenPlan",
            "schedule_round_robin", "resolve_algo", "WkvError", "library"]
 
 
@@ -153,14 +153,27 @@ def wkv6_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y
     return _dense56(6, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status)
 
 
-def wkv6_forward_varlen(lengths, r, k, v, w, u, H, state, *, max_len, state_out=None, state_map=None,
-                        y=None, dev_status=None):
-    """Varlen v6 over packed token rows; updates ``state_out`` (default: ``state`` in place).
+class VarlenPlan:
+    """A validated, pre-marshalled ``wkv6_forward_varlen`` call.
 
-    ``lengths``: [S] int32 device tensor (tokens each slot consumes); ``r, k, v, w``:
-    [total_tokens, H*N]; ``state``: [n_state, H, N, N] fp32; ``state_map``: [S] int32.
-    Returns ``y`` [total_tokens, H*N] fp32.
+    Calling the plan enqueues the kernel on the stream captured when the plan
+    was made, with no per-call Python checks (for serving loops that repeat
+    the same call on the same buffers).  ``y`` is the output tensor.
     """
+
+    def __init__(self, args, y, tensors):
+        self._args = args
+        self._tensors = tensors  # the plan holds raw pointers: keep their tensors alive
+        self.y = y
+
+    def __call__(self):
+        check(_lib.wkv6_forward_varlen(*self._args))
+        return self.y
+
+
+def varlen_plan(lengths, r, k, v, w, u, H, state, *, max_len, state_out=None, state_map=None, y=None,
+                dev_status=None):
+    """Validate and marshal a varlen call once; see :func:`wkv6_forward_varlen` for the arguments."""
     S = lengths.shape[0]
     total, C = r.shape
     if C % H:
@@ -182,10 +195,22 @@ def wkv6_forward_varlen(lengths, r, k, v, w, u, H, state, *, max_len, state_out=
         y = torch.empty((total, C), dtype=torch.float32, device=r.device)
     _dev(y, "y", torch.float32, (total, C))
     _dev(dev_status, "dev_status", torch.int32, (1,))
-    check(_lib.wkv6_forward_varlen(S, H, N, _ptr(lengths), int(max_len), total, _ptr(r), _ptr(k), _ptr(v),
-                                   _ptr(w), _dtype_code(r), _ptr(u), _ptr(y), _ptr(state), _ptr(state_out),
-                                   _ptr(state_map), state.shape[0], _ptr(dev_status), _stream(r)))
-    return y
+    args = (S, H, N, _ptr(lengths), int(max_len), total, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r),
+            _ptr(u), _ptr(y), _ptr(state), _ptr(state_out), _ptr(state_map), state.shape[0], _ptr(dev_status),
+            _stream(r))
+    return VarlenPlan(args, y, (lengths, r, k, v, w, u, y, state, state_out, state_map, dev_status))
+
+
+def wkv6_forward_varlen(lengths, r, k, v, w, u, H, state, *, max_len, state_out=None, state_map=None,
+                        y=None, dev_status=None):
+    """Varlen v6 over packed token rows; updates ``state_out`` (default: ``state`` in place).
+
+    ``lengths``: [S] int32 device tensor (tokens each slot consumes); ``r, k, v, w``:
+    [total_tokens, H*N]; ``state``: [n_state, H, N, N] fp32; ``state_map``: [S] int32.
+    Returns ``y`` [total_tokens, H*N] fp32.
+    """
+    return varlen_plan(lengths, r, k, v, w, u, H, state, max_len=max_len, state_out=state_out,
+                       state_map=state_map, y=y, dev_status=dev_status)()
 
 
 def schedule_round_robin(remaining, budget):

@@ -209,143 +209,102 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
 
 // Varlen calls whose slots consume only a few tokens (T = 1 decode steps, or a
 // token budget spread over many slots) are bound by streaming the 16 KiB
-// state of every (slot, head) in and out.  This variant keeps the memory
-// latencies off each other's path: the state block is requested as soon as
-// the slot's row is known (from a clamped row; an invalid row is rejected
-// before anything is written), while the slot offset is summed; the token
-// rows are read straight into registers.  Same thread
-// layout and reduction order as the staged kernel.
+// state of every (slot, head) in and out.  This variant gives each
+// (slot, head) one wave: lane j holds column j of the state (S[0..63][j]), so
+// every state load and store is a fully coalesced 256-byte row, the output
+// y_t[j] = sum_i r_t[i] S[i][j] + (r_t . (u * k_t)) v_t[j] is a sum inside the
+// lane, and the row factors r_t[i], k_t[i], d_t[i] reach all lanes as scalar
+// operands (v_readlane).  No workgroup barrier: the state is requested as soon
+// as the slot's row is known (clamped; an invalid row is rejected before
+// anything is written), and the slot offset is a wave reduction.
 constexpr int kShortMax = 8;
 
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
-wkv6_varlen_short_kernel(ScanParams p) {
+__global__ void __launch_bounds__(64) wkv6_varlen_short_kernel(ScanParams p) {
   const int h = blockIdx.x;
   const int unit = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int rg = tid >> 4;  // key rows 4rg .. 4rg+3
-  const int cq = tid & 15;  // value columns 4cq .. 4cq+3
+  const int lane = threadIdx.x;  // value column j for the state and y; channel i for r, k, d
   const long C = (long)p.H * kHead;
 
-  __shared__ float4 s_y[2][4][16];
-  __shared__ int s_meta[3];
-
-  if (tid == 0) { s_meta[0] = 0; s_meta[1] = 0; s_meta[2] = 0; }
   const int my_len = p.lengths[unit];
   const int my_row = p.state_map ? p.state_map[unit] : unit;
-  // the other slots' lengths and rows first (slot tid; more slots than threads is the rare case
-  // handled after), then the state block of the (clamped) row, so that waiting for the former
-  // does not wait for the latter
-  const int li = tid < p.units ? p.lengths[tid] : 0;
-  const int mi = (p.state_map && tid < p.units) ? p.state_map[tid] : 0;
-  const int row_c = min(max(my_row, 0), p.n_state - 1);
-  float s[4][4];
-  {
-    const float *sp = p.state_in + ((long)row_c * p.H + h) * (kHead * kHead);
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float4 t = *reinterpret_cast<const float4 *>(sp + (4 * rg + a) * kHead + 4 * cq);
-      s[a][0] = t.x; s[a][1] = t.y; s[a][2] = t.z; s[a][3] = t.w;
-    }
-  }
-  __syncthreads();  // s_meta cleared
+  // the other slots' lengths and rows (64 per pass) first, then the state column of the
+  // (clamped) row, so that waiting for the former does not wait for the latter
   int sum = 0, bad = 0, dup = 0;
-  if (tid < p.units) {
-    if (tid < unit) { sum = li; bad = li < 0; }
-    dup = p.state_map && tid != unit && mi == my_row;
+  {
+    const bool in = lane < p.units;
+    const int L = in ? p.lengths[lane] : 0;
+    const int m = (p.state_map && in) ? p.state_map[lane] : 0;
+    if (lane < unit) { sum = L; bad = L < 0; }
+    dup = p.state_map && in && lane != unit && m == my_row;
   }
-  for (int i = tid + kThreads; i < p.units; i += kThreads) {
+  const int row_c = min(max(my_row, 0), p.n_state - 1);
+  float s[kHead];
+  {
+    const float *sp = p.state_in + ((long)row_c * p.H + h) * (kHead * kHead) + lane;
+#pragma unroll
+    for (int i = 0; i < kHead; ++i) s[i] = sp[i * kHead];
+  }
+  for (int i = lane + 64; i < p.units; i += 64) {
     const int L = p.lengths[i];
     if (i < unit) { sum += L; bad |= (L < 0); }
     if (p.state_map && i != unit && p.state_map[i] == my_row) dup = 1;
   }
-  if (sum) atomicAdd(&s_meta[0], sum);
-  if (bad) atomicOr(&s_meta[1], 1);
-  if (dup) atomicOr(&s_meta[2], 1);
-  float ur[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) ur[a] = p.u[h * kHead + 4 * rg + a];
-  __syncthreads();
-  const int off = s_meta[0];
+  const int off = wave_sum_i(sum);
+  const bool any_bad = __any(bad), any_dup = __any(dup);
   int status = 0;
-  if (my_len < 0 || my_len > p.max_len || s_meta[1]) status |= WKV_DEV_BAD_LENGTH;
+  if (my_len < 0 || my_len > p.max_len || any_bad) status |= WKV_DEV_BAD_LENGTH;
   if (my_row < 0 || my_row >= p.n_state) status |= WKV_DEV_BAD_STATE_MAP;
-  if (s_meta[2]) status |= WKV_DEV_DUPLICATE_ROW;
+  if (any_dup) status |= WKV_DEV_DUPLICATE_ROW;
   if (!(status & WKV_DEV_BAD_LENGTH) && (long)off + my_len > (long)p.total_tokens)
     status |= WKV_DEV_TOKEN_OVERFLOW;
   if (status) {
-    if (tid == 0 && p.dev_status) atomicOr(p.dev_status, status);
+    if (lane == 0 && p.dev_status) atomicOr(p.dev_status, status);
     return;
   }
   const int ntok = my_len;
+  const float ui = p.u[h * kHead + lane];
 
-  // raw words of one token (bf16: 8 bytes per four values, widened on use)
-  typedef typename std::conditional<BF16, uint2, float4>::type Raw;
-  auto load_raw = [&](const void *base, long idx) -> Raw {
-    if constexpr (BF16) return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
-    else return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
-  };
-  auto widen = [&](Raw w) -> float4 {
-    if constexpr (BF16) return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-    else return w;
-  };
-  Raw nr, nk, nx, nv;
-  auto load_tok = [&](int t) {
-    const long e = ((long)off + t) * C + h * kHead;
-    nr = load_raw(p.r, e + 4 * rg);
-    nk = load_raw(p.k, e + 4 * rg);
-    nx = load_raw(p.w, e + 4 * rg);
-    nv = load_raw(p.v, e + 4 * cq);
-  };
+  // token rows one token ahead
+  const long e0 = (long)off * C + h * kHead + lane;
+  float nr = 0.f, nk = 0.f, nv = 0.f, nx = 0.f;
+  if (ntok > 0) {
+    nr = load1<BF16>(p.r, e0); nk = load1<BF16>(p.k, e0); nv = load1<BF16>(p.v, e0); nx = load1<BF16>(p.w, e0);
+  }
   for (int t = 0; t < ntok; ++t) {
-    load_tok(t);
-    const float4 r4 = widen(nr), k4 = widen(nk), x4 = widen(nx), v4 = widen(nv);
-    const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-    const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
-    const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-    const float dd[4] = {decay_of(x4.x), decay_of(x4.y), decay_of(x4.z), decay_of(x4.w)};
-    float ruk = 0.f;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) ruk = fmaf(rr[a] * ur[a], kk[a], ruk);
-    float yp[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float acc = ruk * vv[c];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) acc = fmaf(rr[a], s[a][c], acc);
-      yp[c] = acc;
+    const long e = e0 + (long)t * C;
+    const float rj = nr, kj = nk, vj = nv, dj = decay_of(nx);
+    if (t + 1 < ntok) {
+      nr = load1<BF16>(p.r, e + C); nk = load1<BF16>(p.k, e + C); nv = load1<BF16>(p.v, e + C); nx = load1<BF16>(p.w, e + C);
     }
+    float yj = wave_sum_f(rj * ui * kj) * vj;  // bonus: (r_t . (u * k_t)) v_t[j]
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) s[a][c] = fmaf(dd[a], s[a][c], kk[a] * vv[c]);
-    // sum the wave's four row groups (lanes differing in bits 4 and 5), then the four waves
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float x = yp[c];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      yp[c] = x;
+    for (int i = 0; i < kHead; ++i) {
+      const float ri = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rj), i));
+      const float ki = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kj), i));
+      const float di = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dj), i));
+      yj = fmaf(ri, s[i], yj);
+      s[i] = fmaf(di, s[i], ki * vj);
     }
-    if (lane < 16) s_y[t & 1][wave][cq] = f4(yp[0], yp[1], yp[2], yp[3]);
-    __syncthreads();
-    if (tid < 16) {
-      const float4 a0 = s_y[t & 1][0][tid], a1 = s_y[t & 1][1][tid], a2 = s_y[t & 1][2][tid], a3 = s_y[t & 1][3][tid];
-      const float4 o = f4(((a0.x + a1.x) + a2.x) + a3.x, ((a0.y + a1.y) + a2.y) + a3.y,
-                          ((a0.z + a1.z) + a2.z) + a3.z, ((a0.w + a1.w) + a2.w) + a3.w);
-      *reinterpret_cast<float4 *>(p.y + ((long)off + t) * C + h * kHead + 4 * tid) = o;
-    }
-    // s_y[t & 1] is written again two tokens later, after the next barrier
+    p.y[e] = yj;
   }
 
   if (p.state_out) {
     if (ntok == 0 && p.state_out == p.state_in) return;  // empty slot: untouched
-    float *sp = p.state_out + ((long)my_row * p.H + h) * (kHead * kHead);
+    float *sp = p.state_out + ((long)my_row * p.H + h) * (kHead * kHead) + lane;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      *reinterpret_cast<float4 *>(sp + (4 * rg + a) * kHead + 4 * cq) = f4(s[a][0], s[a][1], s[a][2], s[a][3]);
+    for (int i = 0; i < kHead; ++i) sp[i * kHead] = s[i];
   }
 }
 
@@ -363,8 +322,8 @@ hipError_t launch_wkv56_scan(const ScanParams &p, bool v6, bool bf16, bool varle
     // varlen always carries a per-token decay
     if (p.max_len <= kShortMax) {
       dim3 grid(p.H, p.units);
-      if (bf16) hipLaunchKernelGGL((wkv6_varlen_short_kernel<true>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((wkv6_varlen_short_kernel<false>), grid, dim3(kThreads), 0, s, p);
+      if (bf16) hipLaunchKernelGGL((wkv6_varlen_short_kernel<true>), grid, dim3(64), 0, s, p);
+      else hipLaunchKernelGGL((wkv6_varlen_short_kernel<false>), grid, dim3(64), 0, s, p);
       return hipGetLastError();
     }
     return bf16 ? launch<true, true, true>(p, s) : launch<true, false, true>(p, s);

@@ -182,3 +182,41 @@ def test_serving_workload_prefill_and_decode():
     got = np.concatenate([np.concatenate([yp[off[s]:off[s] + lengths[s]], yd[:, s]]) for s in sample])
     assert_bf16(got, yo, "serving y")
     assert_bf16(host(state)[sample], so, "serving states")
+
+
+def test_varlen_plan_repeats_the_eager_call():
+    """A pre-marshalled plan called twice gives bitwise the same states and outputs as two eager calls."""
+    H, N, S = 2, 64, 5
+    inp = varlen_inputs(S, H, N, seed=54, decode_steps=0, lengths=[1, 1, 0, 1, 1])
+    args = [dev(inp[n]) for n in ("r", "k", "v", "x")]
+    lengths = dev(inp["lengths"])
+    u = dev(inp["u"])
+    st_a, st_b = dev(inp["state"]), dev(inp["state"])
+    y_a = [wkv.wkv6_forward_varlen(lengths, *args, u, H, st_a, max_len=1) for _ in range(2)]
+    plan = wkv.varlen_plan(lengths, *args, u, H, st_b, max_len=1)
+    y_b = []
+    for _ in range(2):
+        y_b.append(plan().clone())
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b)
+    for a, b in zip(y_a, y_b):
+        assert torch.equal(a, b)
+
+
+def test_varlen_plan_keeps_its_tensors_alive():
+    """A plan made from temporaries (lengths built inline) must still read them when called later."""
+    import gc
+    H, N, S = 1, 64, 3
+    inp = varlen_inputs(S, H, N, seed=55, decode_steps=0, lengths=[2, 1, 3])
+    u = dev(inp["u"])
+    st_a, st_b = dev(inp["state"]), dev(inp["state"])
+    plan = wkv.varlen_plan(dev(inp["lengths"]), *[dev(inp[n]) for n in ("r", "k", "v", "x")], u, H, st_b,
+                           max_len=3)
+    gc.collect()
+    junk = [torch.full((1 << 16,), 7, dtype=torch.int32, device="cuda") for _ in range(8)]  # reuse freed blocks
+    y_b = plan()
+    y_a = wkv.wkv6_forward_varlen(dev(inp["lengths"]), *[dev(inp[n]) for n in ("r", "k", "v", "x")], u, H, st_a,
+                                  max_len=3)
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(y_a, y_b) and torch.equal(st_a, st_b)
