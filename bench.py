@@ -458,27 +458,40 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # HIP events around every launch, on the stream the binding launches on (torch's current stream)
+    # HIP events on the stream the binding launches on (torch's current stream).  A workload whose
+    # launches all share one label is timed by one event pair around the whole back-to-back region
+    # (per launch: region time / launches); a workload with several labels gets an event pair around
+    # every launch, so that each label's time is its own.
     stream = torch.cuda.current_stream()
     nl = len(launches)
+    per_launch_events = len({lab for lab, _, _, _, _ in launches}) > 1
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nl)]
-          for _ in range(args.steps)]
+          for _ in range(args.steps)] if per_launch_events else None
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    region[0].record(stream)
     for i in range(args.steps):
         for j, (_, _, fn, _, _) in enumerate(launches):
-            ev[i][j][0].record(stream)
+            if per_launch_events:
+                ev[i][j][0].record(stream)
             fn()
-            ev[i][j][1].record(stream)
+            if per_launch_events:
+                ev[i][j][1].record(stream)
+    region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1000.0 / args.steps
+    region_s = region[0].elapsed_time(region[1]) / 1000.0
     value = W["tc"] / (ms_per_step / 1000.0)
 
     # per label: summed algorithmic bytes / flops and kernel time
     per = {}
     for j, (label, kernel, _, nbytes, flops) in enumerate(launches):
-        times = [ev[i][j][0].elapsed_time(ev[i][j][1]) / 1000.0 for i in range(args.steps)]
+        if per_launch_events:
+            times = [ev[i][j][0].elapsed_time(ev[i][j][1]) / 1000.0 for i in range(args.steps)]
+        else:
+            times = [region_s / (args.steps * nl)] * args.steps
         d = per.setdefault(label, {"kernel": kernel, "launches": 0, "s": 0.0, "bytes": 0, "flops": 0, "times": [],
                                    "kernels": {}})
         d["kernels"][kernel] = d["kernels"].get(kernel, 0) + 1
@@ -513,8 +526,9 @@ def main():
                     "algorithmic_bytes_per_launch": int(bytes_per_launch)}
     phases = {k: {"launches": d["launches"], "kernel_ms": round(d["s"] * 1000.0, 4),
                   "avg_kernel_us": round(d["s"] / d["launches"] * 1e6, 2),
-                  "min_kernel_us": round(min(d["times"]) * 1e6, 2),
-                  "median_kernel_us": round(float(np.median(d["times"])) * 1e6, 2),
+                  "min_kernel_us": round(min(d["times"]) * 1e6, 2) if per_launch_events else None,
+                  "median_kernel_us": round(float(np.median(d["times"])) * 1e6, 2) if per_launch_events else None,
+                  "timing": "event pair per launch" if per_launch_events else "event pair around the timed region",
                   "kernels": d["kernels"],
                   "hbm_GBs": round(d["bytes"] / d["s"] / 1e9, 1)} for k, d in per.items()}
 
