@@ -39,11 +39,11 @@
 //     waves before it and writes rbar, ktil row-major and V transposed as
 //     bf16 hi / lo into the chunk's operand buffer.
 //   consumers (waves 8-15) process chunk i (v_mfma_f32_32x32x16_bf16):
-//     four output waves own the 32x32 output tiles.  Each forms the causal
-//     32x32 blocks of A^T that its token block needs in accumulators (the
-//     rbar registers serve both A^T = ktil rbar^T and rbar S0), masks them,
-//     splits them into bf16 hi / lo in registers and adds A V, reading V in
-//     the token order the accumulator layout gives.  Four state waves own the
+//     two output waves own the 32-token blocks with all 64 value columns.
+//     Each forms the causal 32x32 blocks of A^T that its token block needs in
+//     accumulators (the rbar registers serve both A^T = ktil rbar^T and
+//     rbar S0), masks them, splits them into bf16 hi / lo in registers and
+//     adds A V, reading V in the token order the accumulator layout gives.  Four state waves own the
 //     32x32 fp32 state tiles: they transpose ktil on the matrix core (a
 //     product with the identity is exact for bf16 values), add ktil^T V in
 //     the same permuted token order, rescale, and publish the state as bf16
@@ -394,9 +394,9 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     const int buf = c & 1;
     const int nvalid = min(L, T - c * L);
     if (y_wave) {
-      // Output tile: tokens 32 TB + (0..31) x value columns 32 tile_c + (0..31),
-      // accumulated transposed (Y^T) so that each lane ends up with one token's
-      // columns.  Per K step q (key rows 16q + 8hh + 0..7) the lane's rbar row
+      // Output tile: tokens 32 TB + (0..31) x all 64 value columns (two 32x32
+      // accumulators), accumulated transposed (Y^T) so that each lane ends up
+      // with one token's columns.  Per K step q (key rows 16q + 8hh + 0..7) the lane's rbar row
       // is the B operand of both
       //   Y^T += S0^T rbar^T     (S^T rows from LDS as the A operand)
       //   AT  += ktil rbar^T     (ktil rows of each causal s-block as the A operand)
@@ -404,60 +404,77 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       auto out_tile = [&](auto tb_c) {
         constexpr int TB = decltype(tb_c)::value;
         const int trow = 32 * TB + l32;
-        f32x16 Y = {}, AT[TB + 1];
+        f32x16 Y[2] = {f32x16{}, f32x16{}}, AT[TB + 1];
 #pragma unroll
         for (int sb = 0; sb <= TB; ++sb) AT[sb] = f32x16{};
         // Operands of K step q.  Each group of the next step's operands is
         // loaded as soon as the products of this step that read the same group
         // have been issued, so the loads overlap the remaining products while
-        // only the rbar pair needs a second set of registers.
+        // only the rbar pair needs a second set of registers.  With two A^T
+        // blocks (TB = 1) the r̄ S0 and A^T products take separate passes over
+        // K (rbar read twice) to stay within the register budget.
         auto col_of = [&](int q) { return 16 * q + 8 * hh; };
-        bf16x8 rh = ld8(&o.rb_hi[trow][col_of(0)]), rl = ld8(&o.rb_lo[trow][col_of(0)]);
-        bf16x8 sh = ld8(&sm.st_hi[buf][jcol][col_of(0)]), sl = ld8(&sm.st_lo[buf][jcol][col_of(0)]);
-        bf16x8 kh[TB + 1], kl[TB + 1];
+        auto k_pass = [&](auto do_y_c, auto do_at_c) {
+          constexpr bool DY = decltype(do_y_c)::value, DA = decltype(do_at_c)::value;
+          bf16x8 rh = ld8(&o.rb_hi[trow][col_of(0)]), rl = ld8(&o.rb_lo[trow][col_of(0)]);
+          bf16x8 sh[2], sl[2], kh[TB + 1], kl[TB + 1];
+          if (DY) {
 #pragma unroll
-        for (int sb = 0; sb <= TB; ++sb) {
-          kh[sb] = ld8(&o.kt_hi[32 * sb + l32][col_of(0)]);
-          kl[sb] = ld8(&o.kt_lo[32 * sb + l32][col_of(0)]);
-        }
-        bf16x8 bv[TB + 1][2];  // V in the permuted token order of A V, loaded during the last K step
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nc = col_of(q + 1);
-          Y = mfma32(sh, rh, Y);
-          Y = mfma32(sl, rh, Y);
-          Y = mfma32(sh, rl, Y);
-          __builtin_amdgcn_sched_barrier(0);
-          if (q < 3) {
-            sh = ld8(&sm.st_hi[buf][jcol][nc]);
-            sl = ld8(&sm.st_lo[buf][jcol][nc]);
+            for (int tc = 0; tc < 2; ++tc) {
+              sh[tc] = ld8(&sm.st_hi[buf][32 * tc + l32][col_of(0)]);
+              sl[tc] = ld8(&sm.st_lo[buf][32 * tc + l32][col_of(0)]);
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
+          if (DA) {
 #pragma unroll
-          for (int sb = 0; sb <= TB; ++sb) {
-            AT[sb] = mfma32(kh[sb], rh, AT[sb]);
-            AT[sb] = mfma32(kh[sb], rl, AT[sb]);
-            AT[sb] = mfma32(kl[sb], rh, AT[sb]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int sb = 0; sb <= TB; ++sb) {
+              kh[sb] = ld8(&o.kt_hi[32 * sb + l32][col_of(0)]);
+              kl[sb] = ld8(&o.kt_lo[32 * sb + l32][col_of(0)]);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nc = col_of(q + 1);
+            if (DY) {
+#pragma unroll
+              for (int tc = 0; tc < 2; ++tc) {
+                Y[tc] = mfma32(sh[tc], rh, Y[tc]);
+                Y[tc] = mfma32(sl[tc], rh, Y[tc]);
+                Y[tc] = mfma32(sh[tc], rl, Y[tc]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q < 3) {
+                  sh[tc] = ld8(&sm.st_hi[buf][32 * tc + l32][nc]);
+                  sl[tc] = ld8(&sm.st_lo[buf][32 * tc + l32][nc]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
+            if (DA) {
+#pragma unroll
+              for (int sb = 0; sb <= TB; ++sb) {
+                AT[sb] = mfma32(kh[sb], rh, AT[sb]);
+                AT[sb] = mfma32(kh[sb], rl, AT[sb]);
+                AT[sb] = mfma32(kl[sb], rh, AT[sb]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q < 3) {
+                  kh[sb] = ld8(&o.kt_hi[32 * sb + l32][nc]);
+                  kl[sb] = ld8(&o.kt_lo[32 * sb + l32][nc]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            }
             if (q < 3) {
-              kh[sb] = ld8(&o.kt_hi[32 * sb + l32][nc]);
-              kl[sb] = ld8(&o.kt_lo[32 * sb + l32][nc]);
+              rh = ld8(&o.rb_hi[trow][nc]);
+              rl = ld8(&o.rb_lo[trow][nc]);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (q < 3) {
-            rh = ld8(&o.rb_hi[trow][nc]);
-            rl = ld8(&o.rb_lo[trow][nc]);
-          } else {
-#pragma unroll
-            for (int sb = 0; sb <= TB; ++sb)
-#pragma unroll
-              for (int ks = 0; ks < 2; ++ks) {
-                const int s0 = 32 * sb + 16 * ks + 4 * hh;
-                bv[sb][ks] = ld4x2(&o.vt[jcol][s0], &o.vt[jcol][s0 + 8]);
-              }
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        };
+        if (TB == 0) {
+          k_pass(std::true_type{}, std::true_type{});
+        } else {
+          k_pass(std::true_type{}, std::false_type{});
+          k_pass(std::false_type{}, std::true_type{});
         }
         {  // diagonal block: keep s < t, the bonus on s == t, zero above
           const float bon = o.bonus[trow];
@@ -474,24 +491,37 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
         for (int sb = 0; sb <= TB; ++sb) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
+            const int s0 = 32 * sb + 16 * ks + 4 * hh;
+            bf16x8 bv[2];
+#pragma unroll
+            for (int tc = 0; tc < 2; ++tc) bv[tc] = ld4x2(&o.vt[32 * tc + l32][s0], &o.vt[32 * tc + l32][s0 + 8]);
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) split2(AT[sb][8 * ks + 2 * m], AT[sb][8 * ks + 2 * m + 1], hw[m], lw[m]);
-            Y = mfma32(bv[sb][ks], as_bf16x8(hw[0], hw[1], hw[2], hw[3]), Y);
-            Y = mfma32(bv[sb][ks], as_bf16x8(lw[0], lw[1], lw[2], lw[3]), Y);
+            const bf16x8 ah = as_bf16x8(hw[0], hw[1], hw[2], hw[3]), al = as_bf16x8(lw[0], lw[1], lw[2], lw[3]);
+#pragma unroll
+            for (int tc = 0; tc < 2; ++tc) {
+              Y[tc] = mfma32(bv[tc], ah, Y[tc]);
+              Y[tc] = mfma32(bv[tc], al, Y[tc]);
+            }
           }
         }
-        // Y^T accumulators: lane (token trow, hh) holds y[trow][32 tile_c + 8m + 4hh + 0..3] in
-        // Y[4m .. 4m+3], four 16-byte stores per lane
+        // Y^T accumulators: lane (token trow, hh) holds y[trow][32 tc + 8m + 4hh + 0..3] in
+        // Y[tc][4m .. 4m+3], four 16-byte stores per lane and column block
         char *yb = reinterpret_cast<char *>(p.y) + uniform64(((tok0 + (long)c * L) * C + h * kHead) * 4);
-        float4 *yrow = reinterpret_cast<float4 *>(yb + (uint32_t)((trow * C + 32 * tile_c + 4 * hh) * 4));
+        float4 *yrow = reinterpret_cast<float4 *>(yb + (uint32_t)((trow * C + 4 * hh) * 4));
         if (nvalid == L || trow < nvalid) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) yrow[2 * m] = make_float4(Y[4 * m], Y[4 * m + 1], Y[4 * m + 2], Y[4 * m + 3]);
+          for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+              yrow[8 * tc + 2 * m] = make_float4(Y[tc][4 * m], Y[tc][4 * m + 1], Y[tc][4 * m + 2], Y[tc][4 * m + 3]);
         }
       };
-      if (tile_r) out_tile(std::integral_constant<int, 1>{});
-      else out_tile(std::integral_constant<int, 0>{});
+      // output waves 0 and 1 own token blocks 0 and 1 with all 64 value columns, so each A^T
+      // block is formed once; consumer waves 2 and 3 have no output work
+      if (cw == 1) out_tile(std::integral_constant<int, 1>{});
+      else if (cw == 0) out_tile(std::integral_constant<int, 0>{});
     } else {
       // S += ktil^T V over the chunk's 64 tokens in four K steps of 16.  The
       // A operand (row = key i = 32 tile_r + lane % 32, slots 8hh + e = tokens
