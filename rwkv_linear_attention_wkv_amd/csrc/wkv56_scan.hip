@@ -7,14 +7,16 @@
 // (the rwkv_ops page's RWKV6_OP call: r, k, v, w, u, init_state, state_map ->
 // y, y_state; the standard RWKV-5/6 recurrence).
 //
-// Work decomposition: one 256-thread workgroup per (head, unit).  Thread
-// (rg, cq) owns the 4x4 block of the fp32 state with rows 4rg..4rg+3 and
-// columns 4cq..4cq+3 in registers for the whole call, so the state is read
-// once and written once.  Tokens are staged 16 at a time through LDS as fp32
-// (decay already exponentiated); each thread forms partial outputs over its
-// four key rows, the four row groups of a wave are summed with lane
-// shuffles, and the four waves are summed through LDS in a fixed order, so
-// results are deterministic.
+// Work decomposition: one 512-thread workgroup per (head, unit).  Wave w owns
+// key rows 8w..8w+7 of the fp32 state and lane j owns value column j, so the
+// state is read and written as coalesced 256-byte rows and stays in
+// registers for the whole call (8 values per lane).  Tokens are staged 16 at
+// a time through LDS as fp32 (decay already exponentiated), together with
+// each token's bonus r . (u * k).  Per token a lane updates its 8 state
+// values and forms its wave's partial output over the wave's rows, reading
+// the row factors r, k, d as LDS broadcasts; the eight partials and the bonus
+// term are then summed through LDS in a fixed order, so results are
+// deterministic.
 #include <type_traits>
 
 #include "common.hpp"
@@ -24,25 +26,24 @@
 namespace wkv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTB = 16;  // tokens staged per block
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRows = kHead / kWaves;  // key rows per wave
+constexpr int kTB = 16;                 // tokens staged per block
 
 template <bool V6, bool BF16, bool VARLEN>
 __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   const int h = blockIdx.x;
   const int unit = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int rg = tid >> 4;  // key rows 4rg .. 4rg+3
-  const int cq = tid & 15;  // value columns 4cq .. 4cq+3
+  const int lane = tid & 63;  // value column j
+  const int wave = tid >> 6;  // key rows kRows*wave ..
   const long C = (long)p.H * kHead;
 
-  __shared__ float4 s_r[kTB][16];
-  __shared__ float4 s_k[kTB][16];
-  __shared__ float4 s_d[kTB][16];
-  __shared__ float4 s_v[kTB][16];
-  __shared__ float4 s_y[kTB][4][16];
+  __shared__ float4 s_r[kTB][16], s_k[kTB][16], s_d[kTB][16];  // per token, channels 4q..4q+3
+  __shared__ float s_v[kTB][kHead];
+  __shared__ float s_bon[kTB];                 // r . (u * k) per token
+  __shared__ float s_y[kTB][kWaves][kHead];    // per-wave partial outputs
   __shared__ int s_meta[3];
 
   long tok0;
@@ -94,116 +95,98 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
     }
   }
 
-  // ---- state block in registers
-  float s[4][4];
+  // ---- this lane's column of the wave's key rows, in registers
+  float s[kRows];
   if (row_in >= 0 && p.state_in) {
-    const float *sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead);
+    const float *sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead) + lane;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const float4 t = *reinterpret_cast<const float4 *>(sp + (4 * rg + a) * kHead + 4 * cq);
-      s[a][0] = t.x; s[a][1] = t.y; s[a][2] = t.z; s[a][3] = t.w;
-    }
+    for (int a = 0; a < kRows; ++a) s[a] = sp[(kRows * wave + a) * kHead];
   } else {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) s[a][c] = 0.f;
+    for (int a = 0; a < kRows; ++a) s[a] = 0.f;
   }
-
-  float ur[4], dstat[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    ur[a] = p.u[h * kHead + 4 * rg + a];
-    dstat[a] = V6 ? 0.f : decay_of(static_cast<const float *>(p.w)[h * kHead + 4 * rg + a]);
+  // staging role: thread (token tt, channel quad q), 256 threads
+  const int st_tt = tid >> 4, st_q = tid & 15;
+  float4 u4 = make_float4(0.f, 0.f, 0.f, 0.f), dst4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < 256) {
+    u4 = *reinterpret_cast<const float4 *>(p.u + h * kHead + 4 * st_q);
+    if constexpr (!V6) {
+      const float4 x = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + h * kHead + 4 * st_q);
+      dst4 = f4(decay_of(x.x), decay_of(x.y), decay_of(x.z), decay_of(x.w));
+    }
   }
 
   for (int t0 = 0; t0 < ntok; t0 += kTB) {
     const int nb = min(kTB, ntok - t0);
-    {  // stage kTB tokens of this head as fp32
-      const int tt = tid >> 4, q = tid & 15;
-      if (tt < nb) {
-        const long e = (tok0 + t0 + tt) * C + h * kHead + 4 * q;
-        s_r[tt][q] = load4<BF16>(p.r, e);
-        s_k[tt][q] = load4<BF16>(p.k, e);
-        s_v[tt][q] = load4<BF16>(p.v, e);
+    if (tid < 256) {  // stage kTB tokens of this head as fp32, with each token's bonus
+      float bon = 0.f;
+      if (st_tt < nb) {
+        const long e = (tok0 + t0 + st_tt) * C + h * kHead + 4 * st_q;
+        const float4 r4 = load4<BF16>(p.r, e), k4 = load4<BF16>(p.k, e), v4 = load4<BF16>(p.v, e);
+        s_r[st_tt][st_q] = r4;
+        s_k[st_tt][st_q] = k4;
+        *reinterpret_cast<float4 *>(&s_v[st_tt][4 * st_q]) = v4;
         if constexpr (V6) {
           const float4 x = load4<BF16>(p.w, e);
-          s_d[tt][q] = f4(decay_of(x.x), decay_of(x.y), decay_of(x.z), decay_of(x.w));
+          s_d[st_tt][st_q] = f4(decay_of(x.x), decay_of(x.y), decay_of(x.z), decay_of(x.w));
+        } else {
+          s_d[st_tt][st_q] = dst4;
         }
+        bon = fmaf(r4.x * u4.x, k4.x, fmaf(r4.y * u4.y, k4.y, fmaf(r4.z * u4.z, k4.z, r4.w * u4.w * k4.w)));
       }
+      // sum over the 16 channel quads of the token (lanes differing in bits 0..3)
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) bon += __shfl_xor(bon, m);
+      if (st_q == 0) s_bon[st_tt] = bon;
     }
     __syncthreads();
 
-    float yp[kTB][4];
 #pragma unroll
     for (int tt = 0; tt < kTB; ++tt) {
       if (tt < nb) {
-        const float4 r4 = s_r[tt][rg], k4 = s_k[tt][rg], v4 = s_v[tt][cq];
-        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-        const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
-        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-        float dd[4];
-        if constexpr (V6) {
-          const float4 d4 = s_d[tt][rg];
-          dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
-        } else {
+        const float vj = s_v[tt][lane];
+        float yp = 0.f;
 #pragma unroll
-          for (int a = 0; a < 4; ++a) dd[a] = dstat[a];
+        for (int g = 0; g < kRows / 4; ++g) {
+          const float4 r4 = s_r[tt][2 * wave + g], k4 = s_k[tt][2 * wave + g], d4 = s_d[tt][2 * wave + g];
+          const float rr[4] = {r4.x, r4.y, r4.z, r4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            yp = fmaf(rr[a], s[4 * g + a], yp);
+            s[4 * g + a] = fmaf(dd[a], s[4 * g + a], kk[a] * vj);
+          }
         }
-        float ruk = 0.f;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) ruk = fmaf(rr[a] * ur[a], kk[a], ruk);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float acc = ruk * vv[c];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) acc = fmaf(rr[a], s[a][c], acc);
-          yp[tt][c] = acc;
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) s[a][c] = fmaf(dd[a], s[a][c], kk[a] * vv[c]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) yp[tt][c] = 0.f;
+        s_y[tt][wave][lane] = yp;
       }
-    }
-    // sum the wave's four row groups (lanes differing in bits 4 and 5)
-#pragma unroll
-    for (int tt = 0; tt < kTB; ++tt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float x = yp[tt][c];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        yp[tt][c] = x;
-      }
-    if (lane < 16) {
-#pragma unroll
-      for (int tt = 0; tt < kTB; ++tt)
-        if (tt < nb) s_y[tt][wave][cq] = f4(yp[tt][0], yp[tt][1], yp[tt][2], yp[tt][3]);
     }
     __syncthreads();
-    {  // sum the four waves in a fixed order and store fp32 outputs
-      const int tt = tid >> 4, q = tid & 15;
+    {  // sum the wave partials in a fixed order, add the bonus term, store fp32 outputs
+      const int tt = tid >> 5, j = 2 * (tid & 31);
       if (tt < nb) {
-        const float4 a0 = s_y[tt][0][q], a1 = s_y[tt][1][q], a2 = s_y[tt][2][q], a3 = s_y[tt][3][q];
-        const float4 o = f4(((a0.x + a1.x) + a2.x) + a3.x, ((a0.y + a1.y) + a2.y) + a3.y,
-                            ((a0.z + a1.z) + a2.z) + a3.z, ((a0.w + a1.w) + a2.w) + a3.w);
-        *reinterpret_cast<float4 *>(p.y + (tok0 + t0 + tt) * C + h * kHead + 4 * q) = o;
+        float2 o = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float2 a = *reinterpret_cast<const float2 *>(&s_y[tt][w][j]);
+          o.x += a.x;
+          o.y += a.y;
+        }
+        const float b = s_bon[tt];
+        o.x = fmaf(b, s_v[tt][j], o.x);
+        o.y = fmaf(b, s_v[tt][j + 1], o.y);
+        *reinterpret_cast<float2 *>(p.y + (tok0 + t0 + tt) * C + h * kHead + j) = o;
       }
     }
-    // The next staging writes s_r..s_v, which nobody reads any more; the
-    // next write of s_y happens after the next staging barrier.
+    // The next staging writes s_r..s_bon after this block's reads (ordered by the barrier
+    // above); s_y is written again only after the next staging barrier.
+    __syncthreads();
   }
 
   if (p.state_out) {
     if (VARLEN && ntok == 0 && p.state_out == p.state_in) return;  // empty slot: untouched
-    float *sp = p.state_out + ((long)row_out * p.H + h) * (kHead * kHead);
+    float *sp = p.state_out + ((long)row_out * p.H + h) * (kHead * kHead) + lane;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      *reinterpret_cast<float4 *>(sp + (4 * rg + a) * kHead + 4 * cq) = f4(s[a][0], s[a][1], s[a][2], s[a][3]);
+    for (int a = 0; a < kRows; ++a) sp[(kRows * wave + a) * kHead] = s[a];
   }
 }
 
