@@ -29,7 +29,8 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = kHead / kWaves;  // key rows per wave
-constexpr int kTB = 16;                 // tokens staged per block
+constexpr int kTB = 32;                 // tokens staged per block
+static_assert(16 * kTB == kThreads, "one staging thread per (token, channel quad)");
 
 template <bool V6, bool BF16, bool VARLEN>
 __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
@@ -105,10 +106,10 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
 #pragma unroll
     for (int a = 0; a < kRows; ++a) s[a] = 0.f;
   }
-  // staging role: thread (token tt, channel quad q), 256 threads
+  // staging role: thread (token tt, channel quad q)
   const int st_tt = tid >> 4, st_q = tid & 15;
   float4 u4 = make_float4(0.f, 0.f, 0.f, 0.f), dst4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tid < 256) {
+  {
     u4 = *reinterpret_cast<const float4 *>(p.u + h * kHead + 4 * st_q);
     if constexpr (!V6) {
       const float4 x = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + h * kHead + 4 * st_q);
@@ -116,18 +117,38 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
     }
   }
 
+  // staged token rows are loaded one block ahead, as raw words
+  typedef typename std::conditional<BF16, uint2, float4>::type Raw;
+  auto load_raw = [&](const void *base, long idx) -> Raw {
+    if constexpr (BF16) return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
+    else return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+  };
+  auto widen = [&](Raw w) -> float4 {
+    if constexpr (BF16) return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+    else return w;
+  };
+  Raw pr{}, pk{}, pv{}, px{};
+  auto fetch = [&](int t0) {
+    if (t0 + st_tt < ntok) {
+      const long e = (tok0 + t0 + st_tt) * C + h * kHead + 4 * st_q;
+      pr = load_raw(p.r, e);
+      pk = load_raw(p.k, e);
+      pv = load_raw(p.v, e);
+      if constexpr (V6) px = load_raw(p.w, e);
+    }
+  };
+  fetch(0);
   for (int t0 = 0; t0 < ntok; t0 += kTB) {
     const int nb = min(kTB, ntok - t0);
-    if (tid < 256) {  // stage kTB tokens of this head as fp32, with each token's bonus
+    {  // stage kTB tokens of this head as fp32, with each token's bonus
       float bon = 0.f;
       if (st_tt < nb) {
-        const long e = (tok0 + t0 + st_tt) * C + h * kHead + 4 * st_q;
-        const float4 r4 = load4<BF16>(p.r, e), k4 = load4<BF16>(p.k, e), v4 = load4<BF16>(p.v, e);
+        const float4 r4 = widen(pr), k4 = widen(pk), v4 = widen(pv);
         s_r[st_tt][st_q] = r4;
         s_k[st_tt][st_q] = k4;
         *reinterpret_cast<float4 *>(&s_v[st_tt][4 * st_q]) = v4;
         if constexpr (V6) {
-          const float4 x = load4<BF16>(p.w, e);
+          const float4 x = widen(px);
           s_d[st_tt][st_q] = f4(decay_of(x.x), decay_of(x.y), decay_of(x.z), decay_of(x.w));
         } else {
           s_d[st_tt][st_q] = dst4;
@@ -139,6 +160,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
       for (int m = 1; m < 16; m <<= 1) bon += __shfl_xor(bon, m);
       if (st_q == 0) s_bon[st_tt] = bon;
     }
+    fetch(t0 + kTB);  // the next block, in flight during this one
     __syncthreads();
 
 #pragma unroll
@@ -162,19 +184,18 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
     }
     __syncthreads();
     {  // sum the wave partials in a fixed order, add the bonus term, store fp32 outputs
-      const int tt = tid >> 5, j = 2 * (tid & 31);
+      const int tt = tid >> 4, j = 4 * (tid & 15);
       if (tt < nb) {
-        float2 o = make_float2(0.f, 0.f);
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float2 a = *reinterpret_cast<const float2 *>(&s_y[tt][w][j]);
-          o.x += a.x;
-          o.y += a.y;
+          const float4 a = *reinterpret_cast<const float4 *>(&s_y[tt][w][j]);
+          o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
         }
         const float b = s_bon[tt];
-        o.x = fmaf(b, s_v[tt][j], o.x);
-        o.y = fmaf(b, s_v[tt][j + 1], o.y);
-        *reinterpret_cast<float2 *>(p.y + (tok0 + t0 + tt) * C + h * kHead + j) = o;
+        const float4 v4 = *reinterpret_cast<const float4 *>(&s_v[tt][j]);
+        o = f4(fmaf(b, v4.x, o.x), fmaf(b, v4.y, o.y), fmaf(b, v4.z, o.z), fmaf(b, v4.w, o.w));
+        *reinterpret_cast<float4 *>(p.y + (tok0 + t0 + tt) * C + h * kHead + j) = o;
       }
     }
     // The next staging writes s_r..s_bon after this block's reads (ordered by the barrier
