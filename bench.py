@@ -36,7 +36,7 @@ KERNEL_SOURCES = {
     "wkv56_scan_kernel": ["wkv56_scan.hip"],
     "wkv56_chunked_kernel": ["wkv56_chunked.hip"],
     "wkv4_scan_kernel": ["wkv4_scan.hip"],
-    "wkv6_varlen_short_kernel": ["wkv56_scan.hip"],
+    "wkv6_varlen_short_kernel": ["wkv6_decode.hip"],
 }
 SHORT_MAX = 8  # varlen calls with max_len up to this run the few-token kernel
 TC = "tokens·channels/s"
@@ -103,6 +103,21 @@ def measured_traffic(kernel, workload):
     if not rec or rec.get("kernel_digest") != kernel_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def measured_mfma(kernel, workload):
+    """MFMA busy fraction and bf16 MFMA work per launch from the committed
+    rocprofv3 SQ counter summary, if it was taken on the kernel source as it
+    stands (else None)."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}:{workload}")
+    if not rec or rec.get("kernel_digest") != kernel_digest(kernel):
+        return None
+    return {"busy": rec["mfma_busy"], "gflop_per_launch": rec["mfma_gflop_per_launch"], "source": rec["source"]}
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -514,6 +529,12 @@ def main():
     if traffic is not None:
         # measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) over the same time
         roofline["traffic_GBs"] = round(traffic / avg_s / 1e9, 1)
+    mfma = measured_mfma(D["kernel"], W["workload_key"])
+    if mfma is not None:
+        # SQ_VALU_MFMA_BUSY_CYCLES over the active cycles of all 1024 SIMDs, and the bf16 MFMA rate at this
+        # run's kernel time (the busy fraction is clock-independent; the rate is not)
+        roofline["mfma_busy"] = mfma["busy"]
+        roofline["mfma_bf16_TFLOPs"] = round(mfma["gflop_per_launch"] / avg_s / 1e3, 1)
     if D["kernel"] == "wkv56_scan_kernel" and dom == "forward":
         # The dense token-sequential scan is bound by the vector ALUs: 3 fp32 FMA-class ops per state element
         # and token, packed FP32 off, against the unpacked fp32 peak.  The HBM figures stay alongside.

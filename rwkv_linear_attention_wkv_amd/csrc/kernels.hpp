@@ -31,6 +31,11 @@ struct ScanParams {
 
 hipError_t launch_wkv56_scan(const ScanParams &p, bool v6, bool bf16, bool varlen, hipStream_t s);
 
+// v6 varlen calls whose slots consume at most kShortMax tokens (decode steps):
+// one wave per (slot, head), state column per lane.
+constexpr int kShortMax = 8;
+hipError_t launch_wkv6_varlen_short(const ScanParams &p, bool bf16, hipStream_t s);
+
 // v5 / v6 64-token chunked form with MFMA contractions (dense rows only).
 hipError_t launch_wkv56_chunked(const ScanParams &p, bool v6, bool bf16, hipStream_t s);
 

@@ -216,7 +216,10 @@ wkv_status wkv6_forward_varlen(int num_slots, int H, int N, const int32_t *lengt
   p.lengths = lengths;
   p.max_len = max_len;
   p.total_tokens = total_tokens;
-  return launched(wkv::launch_wkv56_scan(p, true, in_dtype == WKV_BF16, true, static_cast<hipStream_t>(stream)), fn);
+  const bool bf16 = in_dtype == WKV_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_len <= wkv::kShortMax) return launched(wkv::launch_wkv6_varlen_short(p, bf16, s), fn);
+  return launched(wkv::launch_wkv56_scan(p, true, bf16, true, s), fn);
 }
 
 wkv_status wkv_schedule_round_robin(int num_slots, const int32_t *remaining, int budget, int32_t *take,
