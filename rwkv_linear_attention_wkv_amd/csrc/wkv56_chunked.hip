@@ -264,11 +264,13 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   // carried from phase 1 to phase 2 of a chunk (one pipeline step apart)
   float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f;
 
-  // producer phase 1 of chunk c: decay, in-thread prefix, wave totals; loads chunk c + 1
+  // producer phase 1 of chunk c: decay, in-thread prefix, wave totals; loads chunk c + 1.
+  // The tail masks are applied to every chunk: with a single code path the words loaded
+  // for the next chunk land in their final registers and are not copied (a copy would
+  // wait for the load right after issuing it).
   const int lane_x32 = (lane ^ 32) << 2;  // ds_bpermute address of the other half-wave
-  auto produce1 = [&](int c, auto set_c, auto tail_c) {
+  auto produce1 = [&](int c, auto set_c) {
     constexpr int S = decltype(set_c)::value;
-    constexpr bool TAIL = decltype(tail_c)::value;  // the chunk ends past the last token
     const int nvalid = min(L, T - c * L);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -280,7 +282,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) nx[t] = ldx[t];
     }
-    if (V6 && TAIL) {  // tokens past the end do not decay (x = -inf)
+    if (V6) {  // tokens past the end do not decay (x = -inf)
 #pragma unroll
       for (int t = 0; t < 4; ++t) nx[t] = 4 * tg + t < nvalid ? nx[t] : 0xff80ff80u;
     }
@@ -298,13 +300,12 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       cum0[t] = run0;
       cum1[t] = run1;
     }
-    if (!V6 && TAIL) {  // static decay: tokens past the end must not decay the prefix
+    if (!V6) {  // static decay: tokens past the end must not decay the prefix
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (4 * tg + t >= nvalid) {
-          cum0[t] = t ? cum0[t - 1] : 0.f;
-          cum1[t] = t ? cum1[t - 1] : 0.f;
-        }
+        const bool past = 4 * tg + t >= nvalid;
+        cum0[t] = past ? (t ? cum0[t - 1] : 0.f) : cum0[t];
+        cum1[t] = past ? (t ? cum1[t - 1] : 0.f) : cum1[t];
       }
       run0 = cum0[3];
       run1 = cum1[3];
@@ -562,10 +563,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     auto step = [&](int i, auto par) {
       constexpr int P = decltype(par)::value;
       if (i >= -1 && i + 1 < nchunks) produce2(i + 1, std::integral_constant<int, P ^ 1>{});
-      if (i + 3 < nchunks || (i + 3 == nchunks && T % L == 0))
-        produce1(i + 2, std::integral_constant<int, P>{}, std::false_type{});
-      else if (i + 2 < nchunks)
-        produce1(i + 2, std::integral_constant<int, P>{}, std::true_type{});
+      if (i + 2 < nchunks) produce1(i + 2, std::integral_constant<int, P>{});
     };
     prefetch(0, std::integral_constant<int, 0>{});
     // the producers' vector-ALU chain is the longest per step: let them issue first
