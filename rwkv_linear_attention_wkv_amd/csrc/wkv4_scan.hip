@@ -27,6 +27,13 @@
 // holding the round's last token posts the state it ends with, which every
 // wave picks up after the second barrier as the next round's entry state.
 // k, v and r are read once.
+//
+// Rounds whose tokens all exist (and 64 | C) take a straight-line path: the
+// tokens are read with buffer loads whose per-token offsets are scalar; the
+// next round's k and v are requested right after the first barrier, into a
+// second register set, so their latency hides behind the fold and the
+// rescan, and a round's r (needed only by the rescan) is requested as the
+// round starts.  The last, partial round takes the guarded path.
 #include <algorithm>
 
 #include "common.hpp"
@@ -63,12 +70,32 @@ __device__ __forceinline__ void fold(float &a, float &b, float &p, float lam_seg
   p = dbig ? wd : sp;
 }
 
+// y for one token from the state before it: the weighted average with the
+// bonus u on the current token, times sigmoid(r) (one reciprocal for both).
+template <bool HAS_R>
+__device__ __forceinline__ float wkv_out(float a, float b, float p, float u, float k, float v, float r) {
+  const float ww = u + k;
+  const float ex = fast_exp(-fabsf(p - ww));  // e^(min - max)
+  const bool pbig = p >= ww;
+  const float e1 = pbig ? 1.f : ex;
+  const float e2 = pbig ? ex : 1.f;
+  float den = e1 * b + e2;
+  if (HAS_R) den *= 1.f + fast_exp(-r);
+  return (e1 * a + e2 * v) * fast_rcp(den);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  if constexpr (BF16) return bf16_lo(__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0));
+  else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+}
+
 template <bool BF16, bool HAS_R>
 __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p) {
   __shared__ float agg[kMaxSeg][3][kLanes];
   __shared__ float rstate[3][kLanes];
   const int lane = threadIdx.x & (kLanes - 1);
-  const int g = threadIdx.x / kLanes;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);  // wave-uniform
   const int G = blockDim.x / kLanes;
   const int c = blockIdx.x * kLanes + lane;
   const int b = blockIdx.y;
@@ -77,6 +104,7 @@ __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p)
   const float lam = live ? -fast_exp(p.tau[c]) : 0.f;
   const float u = live ? p.u[c] : 0.f;
   const long base = (long)b * p.T * C + c;
+  const long base_ld = (long)b * p.T * C + (live ? c : p.C - 1);
 
   // entry state of the current round (the same in every wave)
   float ra = 0.f, rb = 0.f, rp = -1e38f;
@@ -86,16 +114,88 @@ __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p)
     rp = p.state_in[(3L * b + 2) * C + c];
   }
   const int per_round = G * kSeg;
-  for (int r0 = 0; r0 < p.T; r0 += per_round) {
+  int r_begin = 0;  // first token the guarded path handles
+  if (p.C % kLanes == 0 && (long)per_round * C * 4 <= 0x7fffffffL) {
+    constexpr int kElt = BF16 ? 2 : 4;
+    const int full_rounds = p.T / per_round;
+    const int voff = c * kElt;                         // this lane's channel
+    const int soff_g = g * kSeg * (int)C * kElt;       // this wave's first token in a round
+    const int tstride = (int)C * kElt;                 // one token row
+    // resources covering one round of one batch row
+    auto rsrc = [&](const void *base, int r0) {
+      const char *q = static_cast<const char *>(base) + ((long)b * p.T + r0) * C * kElt;
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(q), 0, per_round * (int)C * kElt, 0x00020000);
+    };
+    float ka[kSeg], va[kSeg], kb[kSeg], vb[kSeg];
+    auto load_kv = [&](int r0, float (&kk)[kSeg], float (&vv)[kSeg]) {
+      const auto rk = rsrc(p.k, r0), rv = rsrc(p.v, r0);
+#pragma unroll
+      for (int j = 0; j < kSeg; ++j) {
+        kk[j] = buf_load<BF16>(rk, voff, soff_g + j * tstride);
+        vv[j] = buf_load<BF16>(rv, voff, soff_g + j * tstride);
+      }
+    };
+    // one full round from the registers (kk, vv); requests the next round's k, v into (nk, nv)
+    auto full_round = [&](int r0, float (&kk)[kSeg], float (&vv)[kSeg], float (&nk)[kSeg], float (&nv)[kSeg],
+                          bool more) {
+      float rr[kSeg];
+      if (HAS_R) {
+        const auto rr_ = rsrc(p.r, r0);
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) rr[j] = buf_load<BF16>(rr_, voff, soff_g + j * tstride);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // issue the r loads now, ahead of the segment aggregate
+      float a = vv[0], bb = 1.f, pp = kk[0];  // the first token absorbed into a zero state
+#pragma unroll
+      for (int j = 1; j < kSeg; ++j) absorb(a, bb, pp, lam, kk[j], vv[j]);
+      agg[g][0][lane] = a;
+      agg[g][1][lane] = bb;
+      agg[g][2][lane] = pp;
+      __syncthreads();
+      if (more) load_kv(r0 + per_round, nk, nv);
+      a = ra; bb = rb; pp = rp;
+      const float lam_seg = lam * (float)kSeg;
+      for (int w = 0; w < g; ++w) fold(a, bb, pp, lam_seg, agg[w][0][lane], agg[w][1][lane], agg[w][2][lane]);
+      const auto ry = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<char *>(p.y) + ((long)b * p.T + r0) * C * 4, 0, per_round * (int)C * 4, 0x00020000);
+      const int soff_y = g * kSeg * (int)C * 4;
+#pragma unroll
+      for (int j = 0; j < kSeg; ++j) {
+        const float out = wkv_out<HAS_R>(a, bb, pp, u, kk[j], vv[j], HAS_R ? rr[j] : 0.f);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ry, c * 4, soff_y + j * (int)C * 4, 0);
+        absorb(a, bb, pp, lam, kk[j], vv[j]);
+      }
+      if (g == G - 1) {  // this wave holds the round's last token
+        rstate[0][lane] = a;
+        rstate[1][lane] = bb;
+        rstate[2][lane] = pp;
+      }
+      __syncthreads();
+      ra = rstate[0][lane];
+      rb = rstate[1][lane];
+      rp = rstate[2][lane];
+    };
+    if (full_rounds > 0) load_kv(0, ka, va);
+    int r = 0;
+    for (; r + 2 <= full_rounds; r += 2) {
+      full_round(r * per_round, ka, va, kb, vb, true);
+      full_round((r + 1) * per_round, kb, vb, ka, va, r + 2 < full_rounds);
+    }
+    if (r < full_rounds) full_round(r * per_round, ka, va, kb, vb, false);
+    r_begin = full_rounds * per_round;
+  }
+  for (int r0 = r_begin; r0 < p.T; r0 += per_round) {
     const int t0 = r0 + g * kSeg;
     const int n = max(0, min(kSeg, p.T - t0));
     float kk[kSeg], vv[kSeg], rr[kSeg];
 #pragma unroll
     for (int j = 0; j < kSeg; ++j) {
-      const long e = base + (long)min(t0 + j, p.T - 1) * C;  // rows past the end: reread the last, unused
-      kk[j] = live ? load1<BF16>(p.k, e) : 0.f;
-      vv[j] = live ? load1<BF16>(p.v, e) : 0.f;
-      rr[j] = (HAS_R && live) ? load1<BF16>(p.r, e) : 0.f;
+      // rows past the end reread the last one and lanes past C read channel C - 1: unused,
+      // and the loads need no branch
+      const long e = base_ld + (long)min(t0 + j, p.T - 1) * C;
+      kk[j] = load1<BF16>(p.k, e);
+      vv[j] = load1<BF16>(p.v, e);
+      rr[j] = HAS_R ? load1<BF16>(p.r, e) : 0.f;
     }
     // segment aggregate from a zero state
     float a = 0.f, bb = 0.f, pp = -1e38f;
@@ -113,17 +213,11 @@ __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p)
       for (int w = 0; w < g; ++w) fold(a, bb, pp, lam_seg, agg[w][0][lane], agg[w][1][lane], agg[w][2][lane]);
 #pragma unroll
       for (int j = 0; j < kSeg; ++j) {
-        if (j >= n) break;
-        const float kt = kk[j], vt = vv[j];
-        const float ww = u + kt;
-        const float ex = fast_exp(-fabsf(pp - ww));  // e^(min - max)
-        const bool pbig = pp >= ww;
-        const float e1 = pbig ? 1.f : ex;
-        const float e2 = pbig ? ex : 1.f;
-        float out = (e1 * a + e2 * vt) * fast_rcp(e1 * bb + e2);
-        if (HAS_R) out *= fast_rcp(1.f + fast_exp(-rr[j]));
-        if (live) p.y[base + (long)(t0 + j) * C] = out;
-        absorb(a, bb, pp, lam, kt, vt);
+        if (j < n) {  // n is wave-uniform
+          const float out = wkv_out<HAS_R>(a, bb, pp, u, kk[j], vv[j], rr[j]);
+          if (live) p.y[base + (long)(t0 + j) * C] = out;
+          absorb(a, bb, pp, lam, kk[j], vv[j]);
+        }
       }
       if (t0 + n == min(p.T, r0 + per_round)) {  // this wave holds the round's last token
         rstate[0][lane] = a;

@@ -64,7 +64,8 @@ def test_v4_full_config_with_decode():
 
 
 @pytest.mark.parametrize("B,T,C,dtype,with_r", [(2, 1, 100, "f32", False), (3, 37, 100, "bf16", True),
-                                                (1, 300, 64, "f32", True)])
+                                                (1, 300, 64, "f32", True), (2, 773, 128, "bf16", True),
+                                                (1, 512, 64, "f32", False), (1, 1024, 192, "bf16", False)])
 def test_v4_ragged_and_initial_state(B, T, C, dtype, with_r):
     inp = wkv4_inputs(B, T, C, seed=7, with_r=with_r, dtype=dtype, init_state=True)
     st0 = dev(inp["state"])
