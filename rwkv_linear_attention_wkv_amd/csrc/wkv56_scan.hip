@@ -11,13 +11,24 @@
 // key rows 8w..8w+7 of the fp32 state and lane j owns value column j, so the
 // state is read and written as coalesced 256-byte rows and stays in
 // registers for the whole call (8 values per lane).  Tokens are staged 32 at
-// a time through LDS as fp32 (decay already exponentiated), together with
-// each token's bonus r . (u * k); the raw words of the next block are loaded
-// into registers while the current one is computed.  Per token a lane updates its 8 state
-// values and forms its wave's partial output over the wave's rows, reading
-// the row factors r, k, d as LDS broadcasts; the eight partials and the bonus
-// term are then summed through LDS in a fixed order, so results are
-// deterministic.
+// a time through LDS as fp32 with each token's bonus r . (u * k); the next
+// block's tokens are loaded while the current one is computed.  Per token a
+// lane updates its 8 state values and forms its wave's partial output over
+// the wave's rows, reading the row factors as LDS broadcasts; the eight
+// partials and the bonus term are then summed through LDS in a fixed order,
+// so results are deterministic.
+//
+// Rescaled frame.  Inside a block let D_t[i] be the decay product from the
+// block start through token t.  The registers carry St = S / D, for which
+//   y_t[j] = sum_i (r_t[i] D_{t-1}[i]) St[i][j] + bonus,
+//   St[i][j] += (k_t[i] / D_t[i]) v_t[j],
+// two FMAs per state element and token instead of three; S = D St at the
+// block end.  The row factors are formed once per (token, channel) while
+// staging, from a log2-decay prefix over the block.  Rounding stays relative
+// to the terms of the true state, since every term is scaled by a power of
+// the decay and scaled back.  A block whose decay product in some channel
+// falls below 2^-80 (where 1 / D would leave the fp32 range) takes the direct
+// form S <- d S + k v instead.
 #include <type_traits>
 
 #include "common.hpp"
@@ -31,7 +42,9 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = kHead / kWaves;  // key rows per wave
 constexpr int kTB = 32;                 // tokens staged per block
-static_assert(16 * kTB == kThreads, "one staging thread per (token, channel quad)");
+static_assert(4 * kWaves == kTB && 16 * kTB == kThreads, "staging: four tokens per wave; reduce: one (token, quad) per thread");
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFrameLog2 = 80.f;  // largest log2 decay of one block the rescaled frame takes
 
 template <bool V6, bool BF16, bool VARLEN>
 __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
@@ -39,14 +52,18 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   const int unit = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;  // value column j
-  const int wave = tid >> 6;  // key rows kRows*wave ..
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // key rows kRows*wave ..
   const long C = (long)p.H * kHead;
 
-  __shared__ float4 s_r[kTB][16], s_k[kTB][16], s_d[kTB][16];  // per token, channels 4q..4q+3
-  __shared__ float s_v[kTB][kHead];
-  __shared__ float s_bon[kTB];                 // r . (u * k) per token
-  __shared__ float s_y[kTB][kWaves][kHead];    // per-wave partial outputs
+  __shared__ __align__(16) float s_r[kTB][kHead], s_k[kTB][kHead], s_d[kTB][kHead];  // direct form
+  __shared__ __align__(16) float s_rh[kTB][kHead], s_kh[kTB][kHead];              // rescaled frame
+  __shared__ __align__(16) float s_v[kTB][kHead];
+  __shared__ __align__(16) float s_dend[kHead];   // decay product of the block per key row
+  __shared__ float s_tot[kWaves][kHead];          // log2 decay of each staging wave's tokens
+  __shared__ float s_bon[kTB];                    // r . (u * k) per token
+  __shared__ __align__(16) float s_y[kTB][kWaves][kHead];  // per-wave partial outputs
   __shared__ int s_meta[3];
+  __shared__ int s_frame;  // 1: the current block takes the direct form
 
   long tok0;
   int ntok;
@@ -107,80 +124,123 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
 #pragma unroll
     for (int a = 0; a < kRows; ++a) s[a] = 0.f;
   }
-  // staging role: thread (token tt, channel quad q)
-  const int st_tt = tid >> 4, st_q = tid & 15;
-  float4 u4 = make_float4(0.f, 0.f, 0.f, 0.f), dst4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  {
-    u4 = *reinterpret_cast<const float4 *>(p.u + h * kHead + 4 * st_q);
-    if constexpr (!V6) {
-      const float4 x = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + h * kHead + 4 * st_q);
-      dst4 = f4(decay_of(x.x), decay_of(x.y), decay_of(x.z), decay_of(x.w));
-    }
-  }
-
-  // staged token rows are loaded one block ahead, as raw words
-  typedef typename std::conditional<BF16, uint2, float4>::type Raw;
-  auto load_raw = [&](const void *base, long idx) -> Raw {
-    if constexpr (BF16) return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
-    else return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
-  };
-  auto widen = [&](Raw w) -> float4 {
-    if constexpr (BF16) return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-    else return w;
-  };
-  Raw pr{}, pk{}, pv{}, px{};
+  // Staging role: wave sw stages tokens 4 sw .. 4 sw + 3 of a block and lane
+  // j channel j.  Decays are kept as log2 (lam = log2 d); cum is this thread's
+  // running sum over its four tokens.
+  const float uc = p.u[h * kHead + lane];
+  float lam_static = 0.f;
+  if constexpr (!V6) lam_static = -fast_exp(static_cast<const float *>(p.w)[h * kHead + lane]) * kLog2e;
+  // the next block's tokens, loaded one block ahead (rows past the end reread the last row)
+  float pr[4], pk[4], pv[4], px[4];
   auto fetch = [&](int t0) {
-    if (t0 + st_tt < ntok) {
-      const long e = (tok0 + t0 + st_tt) * C + h * kHead + 4 * st_q;
-      pr = load_raw(p.r, e);
-      pk = load_raw(p.k, e);
-      pv = load_raw(p.v, e);
-      if constexpr (V6) px = load_raw(p.w, e);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const long e = (tok0 + min(t0 + 4 * wave + t4, ntok - 1)) * C + h * kHead + lane;
+      pr[t4] = load1<BF16>(p.r, e);
+      pk[t4] = load1<BF16>(p.k, e);
+      pv[t4] = load1<BF16>(p.v, e);
+      px[t4] = V6 ? load1<BF16>(p.w, e) : 0.f;
     }
   };
-  fetch(0);
+  if (ntok > 0) fetch(0);
   for (int t0 = 0; t0 < ntok; t0 += kTB) {
     const int nb = min(kTB, ntok - t0);
-    {  // stage kTB tokens of this head as fp32, with each token's bonus
-      float bon = 0.f;
-      if (st_tt < nb) {
-        const float4 r4 = widen(pr), k4 = widen(pk), v4 = widen(pv);
-        s_r[st_tt][st_q] = r4;
-        s_k[st_tt][st_q] = k4;
-        *reinterpret_cast<float4 *>(&s_v[st_tt][4 * st_q]) = v4;
-        if constexpr (V6) {
-          const float4 x = widen(px);
-          s_d[st_tt][st_q] = f4(decay_of(x.x), decay_of(x.y), decay_of(x.z), decay_of(x.w));
-        } else {
-          s_d[st_tt][st_q] = dst4;
-        }
-        bon = fmaf(r4.x * u4.x, k4.x, fmaf(r4.y * u4.y, k4.y, fmaf(r4.z * u4.z, k4.z, r4.w * u4.w * k4.w)));
-      }
-      // sum over the 16 channel quads of the token (lanes differing in bits 0..3)
+    // -- stage r, k, v, d and the bonus; in-thread log-decay prefix
+    float rr[4], kk[4], cum[4], bon[4];
+    float run = 0.f;
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) bon += __shfl_xor(bon, m);
-      if (st_q == 0) s_bon[st_tt] = bon;
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int tt = 4 * wave + t4;
+      const bool valid = tt < nb;
+      const float lam = valid ? (V6 ? -fast_exp(px[t4]) * kLog2e : lam_static) : 0.f;  // no decay past the end
+      run += lam;
+      cum[t4] = run;
+      rr[t4] = pr[t4];
+      kk[t4] = pk[t4];
+      s_r[tt][lane] = pr[t4];
+      s_k[tt][lane] = pk[t4];
+      s_d[tt][lane] = __builtin_amdgcn_exp2f(lam);
+      s_v[tt][lane] = pv[t4];
+      bon[t4] = pr[t4] * uc * pk[t4];
     }
+    s_tot[wave][lane] = run;
+    if (tid == 0) s_frame = 0;
     fetch(t0 + kTB);  // the next block, in flight during this one
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {  // bonus: sum over the 64 channels of the token
+      float x = bon[t4];
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+      bon[t4] = x;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) s_bon[4 * wave + t4] = bon[t4];
+    }
+    __syncthreads();
+    // -- rescaled frame operands: with Lam_t the log2 decay from the block start
+    //    through token t, rh_t = r_t 2^Lam_{t-1} and kh_t = k_t 2^-Lam_t.
+    {
+      float pre = 0.f;
+      for (int w = 0; w < wave; ++w) pre += s_tot[w][lane];
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int tt = 4 * wave + t4;
+        const float lprev = pre + (t4 ? cum[t4 - 1] : 0.f), lcur = pre + cum[t4];
+        s_rh[tt][lane] = rr[t4] * __builtin_amdgcn_exp2f(lprev);
+        s_kh[tt][lane] = kk[t4] * __builtin_amdgcn_exp2f(-lcur);
+      }
+      if (wave == kWaves - 1) {
+        const float lend = pre + cum[3];
+        s_dend[lane] = __builtin_amdgcn_exp2f(lend);
+        if (lend < -kFrameLog2) s_frame = 1;  // too much decay in one block for the frame
+      }
+    }
     __syncthreads();
 
-#pragma unroll
-    for (int tt = 0; tt < kTB; ++tt) {
-      if (tt < nb) {
+    if (s_frame == 0) {
+      // Rescaled frame: the registers hold St = S / D (D = decay product from the block
+      // start), so per token y += rh . St and St += kh v: two FMAs per state element.
+#pragma unroll 4
+      for (int tt = 0; tt < nb; ++tt) {
         const float vj = s_v[tt][lane];
-        float yp = 0.f;
+        const float4 r0 = *reinterpret_cast<const float4 *>(&s_rh[tt][kRows * wave]);
+        const float4 r1 = *reinterpret_cast<const float4 *>(&s_rh[tt][kRows * wave + 4]);
+        const float4 k0 = *reinterpret_cast<const float4 *>(&s_kh[tt][kRows * wave]);
+        const float4 k1 = *reinterpret_cast<const float4 *>(&s_kh[tt][kRows * wave + 4]);
+        float y0 = r0.x * s[0];
+        s[0] = fmaf(k0.x, vj, s[0]);
+        float y1 = r0.y * s[1];
+        s[1] = fmaf(k0.y, vj, s[1]);
+        y0 = fmaf(r0.z, s[2], y0); s[2] = fmaf(k0.z, vj, s[2]);
+        y1 = fmaf(r0.w, s[3], y1); s[3] = fmaf(k0.w, vj, s[3]);
+        y0 = fmaf(r1.x, s[4], y0); s[4] = fmaf(k1.x, vj, s[4]);
+        y1 = fmaf(r1.y, s[5], y1); s[5] = fmaf(k1.y, vj, s[5]);
+        y0 = fmaf(r1.z, s[6], y0); s[6] = fmaf(k1.z, vj, s[6]);
+        y1 = fmaf(r1.w, s[7], y1); s[7] = fmaf(k1.w, vj, s[7]);
+        s_y[tt][wave][lane] = y0 + y1;
+      }
+      // back to S at the block end
+      const float4 d0 = *reinterpret_cast<const float4 *>(&s_dend[kRows * wave]);
+      const float4 d1 = *reinterpret_cast<const float4 *>(&s_dend[kRows * wave + 4]);
+      s[0] *= d0.x; s[1] *= d0.y; s[2] *= d0.z; s[3] *= d0.w;
+      s[4] *= d1.x; s[5] *= d1.y; s[6] *= d1.z; s[7] *= d1.w;
+    } else {
+      // direct form: S <- d S + k v
+      for (int tt = 0; tt < nb; ++tt) {
+        const float vj = s_v[tt][lane];
+        float y0 = 0.f, y1 = 0.f;
 #pragma unroll
-        for (int g = 0; g < kRows / 4; ++g) {
-          const float4 r4 = s_r[tt][2 * wave + g], k4 = s_k[tt][2 * wave + g], d4 = s_d[tt][2 * wave + g];
-          const float rr[4] = {r4.x, r4.y, r4.z, r4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
-          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            yp = fmaf(rr[a], s[4 * g + a], yp);
-            s[4 * g + a] = fmaf(dd[a], s[4 * g + a], kk[a] * vj);
-          }
+        for (int g = 0; g < 2; ++g) {  // (the rare path: not tuned)
+          const float4 r4 = *reinterpret_cast<const float4 *>(&s_r[tt][kRows * wave + 4 * g]);
+          const float4 k4 = *reinterpret_cast<const float4 *>(&s_k[tt][kRows * wave + 4 * g]);
+          const float4 d4 = *reinterpret_cast<const float4 *>(&s_d[tt][kRows * wave + 4 * g]);
+          y0 = fmaf(r4.x, s[4 * g], y0); s[4 * g] = fmaf(d4.x, s[4 * g], k4.x * vj);
+          y1 = fmaf(r4.y, s[4 * g + 1], y1); s[4 * g + 1] = fmaf(d4.y, s[4 * g + 1], k4.y * vj);
+          y0 = fmaf(r4.z, s[4 * g + 2], y0); s[4 * g + 2] = fmaf(d4.z, s[4 * g + 2], k4.z * vj);
+          y1 = fmaf(r4.w, s[4 * g + 3], y1); s[4 * g + 3] = fmaf(d4.w, s[4 * g + 3], k4.w * vj);
         }
-        s_y[tt][wave][lane] = yp;
+        s_y[tt][wave][lane] = y0 + y1;
       }
     }
     __syncthreads();
@@ -199,8 +259,8 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
         *reinterpret_cast<float4 *>(p.y + (tok0 + t0 + tt) * C + h * kHead + j) = o;
       }
     }
-    // The next staging writes s_r..s_bon after this block's reads (ordered by the barrier
-    // above); s_y is written again only after the next staging barrier.
+    // The next staging writes the token arrays after this block's reads (ordered by this
+    // barrier); s_y is written again only after the next staging barrier.
     __syncthreads();
   }
 
