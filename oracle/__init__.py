@@ -19,6 +19,9 @@ from):
   ``d_t = exp(-exp(x_t))``.
 * :func:`wkv6_varlen` — each slot runs :func:`wkv56` over its own packed token
   rows starting from ``state[state_map[s]]`` and writes that row back.
+* :func:`wkv6_backward` — gradients of the v6 recurrence with respect to r,
+  k, v, x, u and the initial state, by reverse-mode differentiation of the
+  definition, one token at a time.
 """
 from __future__ import annotations
 
@@ -69,6 +72,8 @@ def _bind(lib):
     lib.oracle_wkv56_head.restype = None
     lib.oracle_wkv56_head.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_long,
                                       _dp, _dp, _dp, _dp, ctypes.c_long, _dp, _dp, _dp, _dp]
+    lib.oracle_wkv6_head_bwd.restype = None
+    lib.oracle_wkv6_head_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_long] + [_dp] * 14
     return lib
 
 
@@ -197,6 +202,46 @@ def wkv6_varlen(lengths, r, k, v, x, u, H, N, state, state_map=None, threads=Non
 
     _fan_out(run, units, threads)
     return y, out_state
+
+
+def wkv6_backward(r, k, v, x, u, H, N, dy, state=None, state_map=None, d_state_out=None, units=None,
+                  threads=None, lib=None):
+    """Gradients of the v6 recurrence in fp64 (reverse mode through :func:`wkv56`).
+
+    With ``L = sum(dy * y) + sum(d_state_out * S_final)`` for the outputs
+    ``(y, S_final)`` of ``wkv56(r, k, v, x, u, H, N, state, state_map)``,
+    returns ``(dr, dk, dv, dx [B, T, H*N], du [H*N], du_rows [B, H*N],
+    d_state [B, H, N, N])``: ``d_state[b]`` is the gradient with respect to the
+    initial state row ``b`` started from, ``du_rows[b]`` batch row ``b``'s
+    share of ``du``.  ``units`` restricts the work to (b, h) pairs (others
+    stay zero).
+    """
+    lib = lib or load()
+    r, k, v, x, u = _f64(r), _f64(k), _f64(v), _f64(x), _f64(u)
+    dy, dso = _f64(dy), _f64(d_state_out)
+    B, T, C = r.shape
+    assert C == H * N and x.shape == r.shape
+    st = _f64(state)
+    if st is not None and state_map is None:
+        state_map = np.arange(B) if st.shape[0] == B else np.zeros(B, dtype=np.int64)
+    dr, dk, dv, dx = (np.zeros((B, T, C)) for _ in range(4))
+    du_rows = np.zeros((B, C))
+    dS = np.zeros((B, H, N, N))
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(H)]
+
+    def run(unit):
+        b, h = unit
+        base = b * T * C + h * N
+        s0 = _ptr(st, (int(state_map[b]) * H + h) * N * N) if st is not None else None
+        ds = _ptr(dso, (b * H + h) * N * N) if dso is not None else None
+        lib.oracle_wkv6_head_bwd(T, N, C, _ptr(r, base), _ptr(k, base), _ptr(v, base), _ptr(x, base),
+                                 _ptr(u, h * N), s0, _ptr(dy, base), ds,
+                                 _ptr(dr, base), _ptr(dk, base), _ptr(dv, base), _ptr(dx, base),
+                                 _ptr(du_rows, b * C + h * N), _ptr(dS, (b * H + h) * N * N))
+
+    _fan_out(run, units, threads)
+    return dr, dk, dv, dx, du_rows.sum(axis=0), du_rows, dS
 
 
 def _fan_out(fn, units, threads):

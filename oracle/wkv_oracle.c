@@ -124,3 +124,84 @@ void oracle_wkv56_head(int T, int N, long ts,
         memcpy(S_out, S, sizeof(double) * (size_t)N * (size_t)N);
     free(S);
 }
+
+/*
+ * v6 backward, one (batch row, head) unit: the gradients of
+ *   L = sum_t sum_j dy_t[j] y_t[j] + sum_ij dS_T[i][j] S_T[i][j]
+ * with respect to r, k, v, x, u and the initial state, where y and the final
+ * state S_T come from oracle_wkv56_head (same arguments).  This is reverse-mode
+ * differentiation of the forward definition, one token at a time: the forward
+ * states before every token are kept, then the tokens are walked backwards
+ * with G = dL/dS_t (G = dS_T after the last token):
+ *   dr_t[i] = sum_j dy_t[j] (S_{t-1}[i][j] + u[i] k_t[i] v_t[j])
+ *   dk_t[i] = sum_j G[i][j] v_t[j] + u[i] r_t[i] (dy_t . v_t)
+ *   dv_t[j] = sum_i G[i][j] k_t[i] + (sum_i r_t[i] u[i] k_t[i]) dy_t[j]
+ *   du[i]  += r_t[i] k_t[i] (dy_t . v_t)
+ *   dx_t[i] = (sum_j G[i][j] S_{t-1}[i][j]) * d_t[i] * (-exp(x_t[i]))
+ *   G[i][j] <- d_t[i] G[i][j] + r_t[i] dy_t[j]        (now dL/dS_{t-1})
+ * and dS_0 = G at the end.  du accumulates (+=) into the caller's array.
+ * dy, dr, dk, dv, dx use token stride ts like r; dST may be NULL (zero).
+ * The gradient of the decay parameter is per token (v6: x of shape [B,T,C]).
+ */
+void oracle_wkv6_head_bwd(int T, int N, long ts,
+                          const double *r, const double *k, const double *v,
+                          const double *x, const double *u, const double *S0,
+                          const double *dy, const double *dST,
+                          double *dr, double *dk, double *dv, double *dx,
+                          double *du, double *dS0)
+{
+    size_t NN = (size_t)N * (size_t)N;
+    double *hist = (double *)malloc(sizeof(double) * NN * (size_t)(T + 1));
+    double *G = (double *)malloc(sizeof(double) * NN);
+    if (!hist || !G) { free(hist); free(G); return; }
+    /* forward: hist[t] is the state before token t */
+    if (S0) memcpy(hist, S0, sizeof(double) * NN);
+    else memset(hist, 0, sizeof(double) * NN);
+    for (int t = 0; t < T; t++) {
+        const double *kt = k + (long)t * ts, *vt = v + (long)t * ts, *xt = x + (long)t * ts;
+        const double *Sp = hist + (size_t)t * NN;
+        double *Sn = hist + (size_t)(t + 1) * NN;
+        for (int i = 0; i < N; i++) {
+            double d = exp(-exp(xt[i]));
+            for (int j = 0; j < N; j++)
+                Sn[i * N + j] = d * Sp[i * N + j] + kt[i] * vt[j];
+        }
+    }
+    if (dST) memcpy(G, dST, sizeof(double) * NN);
+    else memset(G, 0, sizeof(double) * NN);
+    for (int t = T - 1; t >= 0; t--) {
+        const double *rt = r + (long)t * ts, *kt = k + (long)t * ts, *vt = v + (long)t * ts;
+        const double *xt = x + (long)t * ts, *dyt = dy + (long)t * ts;
+        const double *Sp = hist + (size_t)t * NN;
+        double dyv = 0.0, bonus = 0.0;
+        for (int j = 0; j < N; j++) dyv += dyt[j] * vt[j];
+        for (int i = 0; i < N; i++) bonus += rt[i] * u[i] * kt[i];
+        for (int i = 0; i < N; i++) {
+            double a = 0.0, b = 0.0, c = 0.0;
+            for (int j = 0; j < N; j++) {
+                a += dyt[j] * (Sp[i * N + j] + u[i] * kt[i] * vt[j]);
+                b += G[i * N + j] * vt[j];
+                c += G[i * N + j] * Sp[i * N + j];
+            }
+            double ex = exp(xt[i]);
+            double d = exp(-ex);
+            dr[(long)t * ts + i] = a;
+            dk[(long)t * ts + i] = b + u[i] * rt[i] * dyv;
+            dx[(long)t * ts + i] = c * d * (-ex);
+            du[i] += rt[i] * kt[i] * dyv;
+        }
+        for (int j = 0; j < N; j++) {
+            double a = 0.0;
+            for (int i = 0; i < N; i++) a += G[i * N + j] * kt[i];
+            dv[(long)t * ts + j] = a + bonus * dyt[j];
+        }
+        for (int i = 0; i < N; i++) {
+            double d = exp(-exp(xt[i]));
+            for (int j = 0; j < N; j++)
+                G[i * N + j] = d * G[i * N + j] + rt[i] * dyt[j];
+        }
+    }
+    if (dS0) memcpy(dS0, G, sizeof(double) * NN);
+    free(hist);
+    free(G);
+}

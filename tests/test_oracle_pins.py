@@ -402,3 +402,118 @@ def test_pins_catch_planted_mistakes(name):
                                  inp["u"].astype(np.float64), inp["state"][0, 0].astype(np.float64))
         caught |= relerr(y[0], yc) > 1e-9 or relerr(S[0, 0], Sc) > 1e-9
         assert caught, f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------- v6 backward pins
+
+def _bwd_case(seed, B=2, H=1, N=4, T=7, shared_state=False):
+    rng = np.random.default_rng(seed)
+    C = H * N
+    case = {
+        "r": rng.standard_normal((B, T, C)), "k": rng.standard_normal((B, T, C)),
+        "v": rng.standard_normal((B, T, C)), "x": rng.uniform(-3.0, 1.0, (B, T, C)),
+        "u": rng.standard_normal(C) * 0.5,
+        "state": rng.standard_normal((1 if shared_state else B, H, N, N)) * 0.3,
+        "dy": rng.standard_normal((B, T, C)), "dso": rng.standard_normal((B, H, N, N)),
+    }
+    case["map"] = np.zeros(B, dtype=np.int64) if shared_state else np.arange(B)
+    return case, H, N
+
+
+def _loss(c, H, N):
+    """L = sum(dy * y) + sum(dso * S_final) through the forward oracle."""
+    y, S = oracle.wkv56(c["r"], c["k"], c["v"], c["x"], c["u"], H, N, state=c["state"],
+                        state_map=c["map"], threads=1)
+    return float(np.sum(c["dy"] * y) + np.sum(c["dso"] * S))
+
+
+def _fd_grads(c, H, N, h=1e-6):
+    """Central differences of the forward oracle's loss, element by element."""
+    out = {}
+    for name in ("r", "k", "v", "x", "u", "state"):
+        g = np.zeros_like(c[name])
+        flat = c[name].reshape(-1)
+        gf = g.reshape(-1)
+        for e in range(flat.size):
+            keep = flat[e]
+            flat[e] = keep + h
+            lp = _loss(c, H, N)
+            flat[e] = keep - h
+            lm = _loss(c, H, N)
+            flat[e] = keep
+            gf[e] = (lp - lm) / (2 * h)
+        out[name] = g
+    return out
+
+
+def _check_bwd_against_fd(c, H, N, lib=None, tol=1e-6):
+    dr, dk, dv, dx, du, du_rows, dS = oracle.wkv6_backward(
+        c["r"], c["k"], c["v"], c["x"], c["u"], H, N, c["dy"], state=c["state"], state_map=c["map"],
+        d_state_out=c["dso"], threads=1, lib=lib)
+    fd = _fd_grads(c, H, N)
+    # the gradient of a shared initial state row is the sum over the batch rows that started from it
+    dstate = np.zeros_like(c["state"])
+    for b, row in enumerate(c["map"]):
+        dstate[row] += dS[b]
+    errs = {"r": relerr(dr, fd["r"]), "k": relerr(dk, fd["k"]), "v": relerr(dv, fd["v"]),
+            "x": relerr(dx, fd["x"]), "u": relerr(du, fd["u"]), "state": relerr(dstate, fd["state"])}
+    return errs, du_rows
+
+
+@pytest.mark.parametrize("shared_state", [False, True])
+def test_v6_backward_matches_finite_differences(shared_state):
+    """Every gradient of the backward oracle equals central differences of the forward oracle's
+    loss sum(dy * y) + sum(dS * S_final) (fp64, step 1e-6: agreement to about 1e-8)."""
+    c, H, N = _bwd_case(5, shared_state=shared_state)
+    errs, du_rows = _check_bwd_against_fd(c, H, N)
+    assert max(errs.values()) < 1e-6, errs
+    assert np.allclose(du_rows.sum(axis=0), oracle.wkv6_backward(
+        c["r"], c["k"], c["v"], c["x"], c["u"], H, N, c["dy"], state=c["state"], state_map=c["map"],
+        d_state_out=c["dso"], threads=1)[4], rtol=0, atol=0)
+
+
+def test_v6_backward_two_heads_and_no_state():
+    """Two heads (the per-head channel offsets) and a zero initial state with no state gradient in."""
+    c, H, N = _bwd_case(8, B=1, H=2, N=3, T=5)
+    c["state"] = np.zeros_like(c["state"])
+    c["dso"] = np.zeros_like(c["dso"])
+    errs, _ = _check_bwd_against_fd(c, H, N)
+    assert max(errs.values()) < 1e-6, errs
+
+
+def test_v6_backward_is_linear_in_upstream_gradients():
+    c, H, N = _bwd_case(11, N=5, T=9)
+    args = (c["r"], c["k"], c["v"], c["x"], c["u"], H, N)
+    g1 = oracle.wkv6_backward(*args, c["dy"], state=c["state"], d_state_out=c["dso"], threads=1)
+    g2 = oracle.wkv6_backward(*args, 2.0 * c["dy"], state=c["state"], d_state_out=2.0 * c["dso"], threads=1)
+    for a, b2 in zip(g1, g2):
+        assert np.array_equal(2.0 * a, b2)  # scaling by 2 is exact in binary floating point
+
+
+_BWD_MUTANTS = {
+    "dk_drops_bonus": ("dk[(long)t * ts + i] = b + u[i] * rt[i] * dyv;", "dk[(long)t * ts + i] = b;"),
+    "G_not_decayed": ("G[i * N + j] = d * G[i * N + j] + rt[i] * dyt[j];", "G[i * N + j] = G[i * N + j] + rt[i] * dyt[j];"),
+    "dx_missing_d": ("dx[(long)t * ts + i] = c * d * (-ex);", "dx[(long)t * ts + i] = c * (-ex);"),
+    "dv_transposed": ("for (int i = 0; i < N; i++) a += G[i * N + j] * kt[i];", "for (int i = 0; i < N; i++) a += G[j * N + i] * kt[i];"),
+    "dr_state_after": ("a += dyt[j] * (Sp[i * N + j] + u[i] * kt[i] * vt[j]);", "a += dyt[j] * (Sp[NN + i * N + j] + u[i] * kt[i] * vt[j]);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_BWD_MUTANTS))
+def test_backward_pins_catch_planted_mistakes(name):
+    """A mistake planted in a copy of the backward oracle must fail the finite-difference pin."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "wkv_oracle.c")).read()
+    old, new = _BWD_MUTANTS[name]
+    assert src.count(old) == 1, name
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        so = os.path.join(d, "mutant.so")
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", path, "-o", so, "-lm"])
+        lib = oracle.load(so)
+        c, H, N = _bwd_case(5)
+        errs, _ = _check_bwd_against_fd(c, H, N, lib=lib)
+        assert max(errs.values()) > 1e-4, f"mutant {name} passed the pin: {errs}"
