@@ -365,7 +365,8 @@ def test_varlen_call_split_is_bitwise():
 _MUTANTS = {
     "dropped_bonus": ("rt[i] * (S[i * N + j] + u[i] * kt[i] * vt[j])", "rt[i] * (S[i * N + j])"),
     "transposed_state": ("rt[i] * (S[i * N + j] +", "rt[i] * (S[j * N + i] +"),
-    "decay_sign": ("double d = exp(-exp(xt[i]));", "double d = exp(exp(xt[i]) * -0.5);"),
+    "decay_sign": ("double d = exp(-exp(xt[i]));\n            for (int j = 0; j < N; j++)\n                S[i * N + j]",
+                   "double d = exp(exp(xt[i]) * -0.5);\n            for (int j = 0; j < N; j++)\n                S[i * N + j]"),
     "decay_index": ("const double *xt = x + (long)t * xs;", "const double *xt = x + (long)(t > 0 ? t - 1 : 0) * xs;"),
     "v4_bonus_on_k": ("double bonus = exp(u[c] + kt);", "double bonus = exp(u[c]);"),
     "v4_decay_twice": ("A = decay * A + ek * vt;", "A = decay * decay * A + ek * vt;"),
