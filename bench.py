@@ -16,6 +16,8 @@ Other workloads (same JSON layout, not the headline):
   decode   one T=1 v6 step for 64 slots in place on [64, 32, 64, 64] fp32 states
   serving  64 slots with prompts ~ U{1..2048} fed through a 128-token budget per
            call (round robin), then 256 T=1 decode steps
+  wkv6_bwd v6 backward of the headline shape: dr, dk, dv, dw, du and the
+           initial-state gradient for upstream gradients of y and the final state
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload wkv6] [--algo auto|scan|chunked]
 """
@@ -37,6 +39,7 @@ KERNEL_SOURCES = {
     "wkv56_chunked_kernel": ["wkv56_chunked.hip"],
     "wkv4_scan_kernel": ["wkv4_scan.hip"],
     "wkv6_varlen_short_kernel": ["wkv6_decode.hip"],
+    "wkv6_bwd_sweep_kernel": ["wkv6_backward.hip"],
 }
 SHORT_MAX = 8  # varlen calls with max_len up to this run the few-token kernel
 TC = "tokens·channels/s"
@@ -48,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20; 200 for the short decode step, 5 for the serving pass)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving"])
+    ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving", "wkv6_bwd"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
     ap.add_argument("--B", type=int, default=None)
     ap.add_argument("--T", type=int, default=None)
@@ -217,6 +220,75 @@ def workload_wkv56(args, version):
                 "; fp32 u; zero initial state)",
         "config": {"workload": f"{name} forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
                    "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
+                   "parallelism": "single GPU"},
+        "cpu": cpu,
+    }
+
+
+def workload_wkv6_bwd(args):
+    """v6 backward: the gradients of one forward call of the headline shape (B=8 T=4096 H=32
+    N=64, bf16 inputs) for upstream gradients of y and of the final state."""
+    import numpy as np
+    import torch
+    import rwkv_linear_attention_wkv_amd as wkv
+    from wkv_inputs import wkv6_inputs, wkv6_upstream
+
+    B, T, H, N = args.B or 8, args.T or 4096, args.H, 64
+    C = H * N
+    inp = wkv6_inputs(B, T, H, N, seed=args.seed)
+    up = wkv6_upstream(B, T, H, N, seed=args.seed + 1)
+    r, k, v, x = (_bf16_dev(inp[n]) for n in ("r", "k", "v", "x"))
+    u = torch.from_numpy(inp["u"]).cuda()
+    dy = torch.from_numpy(up["dy"]).cuda()
+    dS = torch.from_numpy(up["d_state"]).cuda()
+    _, S_final = wkv.wkv6_forward(r, k, v, x, u, H)
+    torch.cuda.synchronize()
+    out = {}
+    tc = B * T * C
+    # read r, k, v, x (bf16), dy, u, the final state and its gradient; write dr, dk, dv, dw, du,
+    # du_rows and the initial-state gradient
+    alg_bytes = 8 * tc + 4 * tc + 4 * C + 2 * 4 * B * H * N * N + 16 * tc + 4 * C + 4 * B * C + 4 * B * H * N * N
+    flops = 3 * 2 * 3 * N * tc  # three sweeps, each 3 FMA-class ops per state element and token
+
+    def run():
+        out["g"] = wkv.wkv6_backward(r, k, v, x, u, H, dy, state_final=S_final, d_state=dS)
+
+    def cpu(target_s):
+        import oracle
+        oracle.load()
+        units_all = [(b, h) for b in range(B) for h in range(H)]
+
+        def run_units(units, threads):
+            return oracle.wkv6_backward(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, up["dy"],
+                                        d_state_out=up["d_state"], units=units, threads=threads)
+        res, units, ref = _oracle_units_baseline(inp, target_s, units_all, run_units, T * N,
+                                                 f"(batch row, head) units x T={T} x N={N}, all gradients")
+        got = [t.cpu().numpy() for t in out["g"][:4]]
+        worst = {}
+        for name, g, o in zip(("dr", "dk", "dv", "dw"), got, ref[:4]):
+            gs = np.stack([g[b, :, h * N:(h + 1) * N] for b, h in units])
+            os_ = np.stack([o[b, :, h * N:(h + 1) * N] for b, h in units])
+            scale = max(float(np.sqrt(np.mean(os_ ** 2))), 1e-30)
+            worst[name + "_max_rel"] = float(np.max(np.abs(gs - os_) / np.maximum(np.abs(os_), scale)))
+        dSg = out["g"][5].cpu().numpy()
+        gs = np.stack([dSg[b, h] for b, h in units])
+        os_ = np.stack([ref[6][b, h] for b, h in units])
+        scale = max(float(np.sqrt(np.mean(os_ ** 2))), 1e-30)
+        worst["d_state_max_rel"] = float(np.max(np.abs(gs - os_) / np.maximum(np.abs(os_), scale)))
+        worst["units"] = len(units)
+        return res, worst
+
+    return {
+        "metric": f"WKV6 backward tokens·channels/s, B={B} T={T} H={H} N={N}",
+        "workload_key": f"wkv6bwd_B{B}_T{T}_H{H}_N{N}_bf16",
+        "launches": [("backward", "wkv6_bwd_sweep_kernel", run, alg_bytes, flops)],
+        "tc": tc,
+        "dtype": "fp32",
+        "compute": "fp32 vector ALU (three token-sequential sweeps)",
+        "data": "synthetic (seeded numpy PCG64; bf16 r,k,v,x; fp32 u; fp32 dy ~ N(0,1) and final-state "
+                "gradient ~ N(0,0.1); zero initial state)",
+        "config": {"workload": f"WKV6 backward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 gradients",
+                   "B": B, "T": T, "H": H, "N": N, "global_batch": B, "seq_len": T,
                    "parallelism": "single GPU"},
         "cpu": cpu,
     }
@@ -461,6 +533,8 @@ def main():
         W = workload_wkv56(args, 6 if args.workload == "wkv6" else 5)
     elif args.workload == "wkv4":
         W = workload_wkv4(args)
+    elif args.workload == "wkv6_bwd":
+        W = workload_wkv6_bwd(args)
     else:
         W = workload_serving(args, decode_only=args.workload == "decode")
     gen_s = time.perf_counter() - t0
@@ -543,9 +617,10 @@ def main():
         # run's kernel time (the busy fraction is clock-independent; the rate is not)
         roofline["mfma_busy"] = mfma["busy"]
         roofline["mfma_bf16_TFLOPs"] = round(mfma["gflop_per_launch"] / avg_s / 1e3, 1)
-    if D["kernel"] == "wkv56_scan_kernel" and dom == "forward":
-        # The dense token-sequential scan is bound by the vector ALUs: 3 fp32 FMA-class ops per state element
-        # and token, packed FP32 off, against the unpacked fp32 peak.  The HBM figures stay alongside.
+    if D["kernel"] in ("wkv56_scan_kernel", "wkv6_bwd_sweep_kernel") and D["flops"] > 0:
+        # The token-sequential scan (and each sweep of the backward) is bound by the vector ALUs: 3 fp32
+        # FMA-class ops per state element and token by the recurrence's definition, packed FP32 off, against
+        # the unpacked fp32 peak.  The HBM figures stay alongside.
         ach = D["flops"] / D["s"] / 1e12
         roofline = {"bound": "alu", "achieved": round(ach, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / VALU_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": D["kernel"],

@@ -173,6 +173,37 @@ WKV_API wkv_status wkv6_forward_varlen(int num_slots, int H, int N,
                                int32_t *dev_status, void *stream);
 
 /*
+ * v6 backward: gradients for training (the RWKV-6 recurrence of wkv6_forward,
+ * the rwkv_ops page's RWKV6_OP call, differentiated in reverse mode).
+ * With the loss L = sum(dy * y) + sum(d_state_out * S_final) of a forward
+ * call with the same r, k, v, w, u, state_in, state_map, n_state:
+ *   dy           [B,T,H*N] fp32 gradient of y
+ *   state_final  [B,H,N,N] fp32 the forward call's final state (its
+ *                state_out); required when d_state_out is given, else unused
+ *   d_state_out  [B,H,N,N] fp32 gradient of the final state, or NULL (zero)
+ *   dr, dk, dv   [B,T,H*N] fp32 gradients of r, k, v
+ *   dw           [B,T,H*N] fp32 gradient of the raw decay parameter w
+ *   du           [H*N] fp32 gradient of u (summed over the batch)
+ *   du_rows      [B,H*N] fp32 each batch row's share of du (also the staging
+ *                for du; the caller provides it)
+ *   d_state_in   [B,H,N,N] fp32 or NULL: gradient with respect to the initial
+ *                state row b started from (rows that share a state_in row are
+ *                not summed: the caller adds them)
+ * All pointers are device pointers owned by the caller; the library
+ * allocates nothing.  Outputs are written, not accumulated.  Three
+ * token-sequential sweeps plus a small reduction are enqueued on `stream`.
+ * N must be 64.  Deterministic (no atomics on data).
+ */
+WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
+                         const void *r, const void *k, const void *v, const void *w,
+                         wkv_dtype in_dtype, const float *u, const float *dy,
+                         const float *state_in, const int32_t *state_map, int n_state,
+                         const float *state_final, const float *d_state_out,
+                         float *dr, float *dk, float *dv, float *dw,
+                         float *du, float *du_rows, float *d_state_in,
+                         int32_t *dev_status, void *stream);
+
+/*
  * Host-side token-budget split for the varlen serving loop (HOST arrays).
  * Hands one token at a time to every slot with tokens left, in slot order,
  * until `budget` tokens are given out or no slot has tokens left.

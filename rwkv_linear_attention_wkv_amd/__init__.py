@@ -26,7 +26,7 @@ _lib = _native.load()
 
 _ALGOS = {"auto": WKV_ALGO_AUTO, "scan": WKV_ALGO_SCAN, "chunked": WKV_ALGO_CHUNKED}
 
-__all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_forward_varlen", "varlen_plan", "VarlenPlan",
+__all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_backward", "wkv6_forward_varlen", "varlen_plan", "VarlenPlan",
            "schedule_round_robin", "resolve_algo", "WkvError", "library"]
 
 
@@ -151,6 +151,48 @@ def wkv6_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y
     Returns ``(y [B, T, H*N] fp32, state_out [B, H, N, N] fp32 or None)``.
     """
     return _dense56(6, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status)
+
+
+def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_final=None, d_state=None,
+                  return_d_state=True, dev_status=None):
+    """Gradients of :func:`wkv6_forward` (same r, k, v, w, u, H, state, state_map).
+
+    ``dy`` [B, T, H*N] fp32 is the gradient of y; ``d_state`` [B, H, N, N] fp32
+    (optional) the gradient of the final state, which then also needs
+    ``state_final``, the forward call's final state.  Returns ``(dr, dk, dv,
+    dw [B, T, H*N], du [H*N], d_state_in [B, H, N, N] or None)`` in fp32;
+    ``d_state_in[b]`` is the gradient with respect to the initial state row b
+    started from.
+    """
+    B, T, C = r.shape
+    if C % H:
+        raise ValueError(f"C={C} is not a multiple of H={H}")
+    N = C // H
+    _same_dtype([("r", r), ("k", k), ("v", v), ("w", w)])
+    for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
+        _dev(t, name, shape=(B, T, C))
+    _dev(u.reshape(-1) if u.dim() == 2 else u, "u", torch.float32, (C,))
+    _dev(dy, "dy", torch.float32, (B, T, C))
+    n_state = 0
+    if state is not None:
+        _dev(state, "state", torch.float32)
+        if state.dim() != 4 or tuple(state.shape[1:]) != (H, N, N):
+            raise ValueError(f"state must be [n_state, {H}, {N}, {N}], got {tuple(state.shape)}")
+        n_state = state.shape[0]
+    _dev(state_map, "state_map", torch.int32, (B,))
+    _dev(d_state, "d_state", torch.float32, (B, H, N, N))
+    _dev(state_final, "state_final", torch.float32, (B, H, N, N))
+    _dev(dev_status, "dev_status", torch.int32, (1,))
+    f32 = dict(dtype=torch.float32, device=r.device)
+    dr, dk, dv, dw = (torch.empty((B, T, C), **f32) for _ in range(4))
+    du = torch.empty((C,), **f32)
+    du_rows = torch.empty((B, C), **f32)
+    d_state_in = torch.empty((B, H, N, N), **f32) if return_d_state else None
+    check(_lib.wkv6_backward(B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r), _ptr(u), _ptr(dy),
+                             _ptr(state), _ptr(state_map), n_state, _ptr(state_final), _ptr(d_state),
+                             _ptr(dr), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), _ptr(du_rows), _ptr(d_state_in),
+                             _ptr(dev_status), _stream(r)))
+    return dr, dk, dv, dw, du, d_state_in
 
 
 class VarlenPlan:

@@ -25,6 +25,8 @@ SIGNATURES = {
     "wkv4_forward": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]),
     "wkv5_forward": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp]),
     "wkv6_forward": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp]),
+    "wkv6_backward": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "wkv6_forward_varlen": (_i, [_i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i,
                                  _vp, _vp]),
     "wkv_schedule_round_robin": (_i, [_i, _i32p, _i, _i32p, _i32p]),

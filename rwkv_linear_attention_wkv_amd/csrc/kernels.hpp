@@ -39,6 +39,22 @@ hipError_t launch_wkv6_varlen_short(const ScanParams &p, bool bf16, hipStream_t 
 // v5 / v6 64-token chunked form with MFMA contractions (dense rows only).
 hipError_t launch_wkv56_chunked(const ScanParams &p, bool v6, bool bf16, hipStream_t s);
 
+// v6 backward: three token-sequential sweeps (dr and du, dk and dw, dv and the
+// initial-state gradient) and the sum of du over the batch.
+struct BwdParams {
+  int B, T, H;
+  const void *r, *k, *v, *w;  // [B, T, H*64] inputs of the forward call
+  const float *u, *dy;
+  const float *state_in;
+  const int32_t *state_map;
+  int n_state;
+  const float *state_final, *d_state_out;  // [B, H, 64, 64]
+  float *dr, *dk, *dv, *dw, *du, *du_rows, *d_state_in;
+  int32_t *dev_status;
+};
+
+hipError_t launch_wkv6_backward(const BwdParams &p, bool bf16, hipStream_t s);
+
 // v4 channel-wise scan.
 struct V4Params {
   int B, T, C;

@@ -175,6 +175,39 @@ wkv_status wkv6_forward(int B, int T, int H, int N, const void *r, const void *k
                  dev_status, stream);
 }
 
+wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *k, const void *v, const void *w,
+                         wkv_dtype in_dtype, const float *u, const float *dy, const float *state_in,
+                         const int32_t *state_map, int n_state, const float *state_final,
+                         const float *d_state_out, float *dr, float *dk, float *dv, float *dw, float *du,
+                         float *du_rows, float *d_state_in, int32_t *dev_status, void *stream) {
+  const char *fn = "wkv6_backward";
+  wkv_status st = check_dense56(fn, B, T, H, N, r, k, v, w, in_dtype, u, dr, state_in, state_map, n_state,
+                                nullptr, WKV_ALGO_AUTO);
+  if (st != WKV_OK) return st;
+  if (T > 0) {
+    REQUIRE(dy && dk && dv && dw, "%s: dy, dk, dv and dw must be non-NULL", fn);
+    REQUIRE(aligned(dy, 4) && aligned(dk, 16) && aligned(dv, 16) && aligned(dw, 4),
+            "%s: dk and dv must be 16-byte aligned, dy and dw 4-byte aligned", fn);
+  }
+  REQUIRE(u && du && du_rows, "%s: u, du and du_rows must be non-NULL", fn);
+  REQUIRE(aligned(du, 4) && aligned(du_rows, 4), "%s: du and du_rows must be 4-byte aligned", fn);
+  REQUIRE(!d_state_in || aligned(d_state_in, 4), "%s: d_state_in must be 4-byte aligned", fn);
+  if (d_state_out) {
+    REQUIRE(state_final, "%s: state_final (the forward call's final state) is needed with d_state_out", fn);
+    REQUIRE(aligned(d_state_out, 4) && aligned(state_final, 4), "%s: d_state_out and state_final misaligned", fn);
+  }
+  REQUIRE(!dev_status || aligned(dev_status, 4), "%s: dev_status must be 4-byte aligned", fn);
+  wkv::BwdParams p{};
+  p.B = B; p.T = T; p.H = H;
+  p.r = r; p.k = k; p.v = v; p.w = w;
+  p.u = u; p.dy = dy;
+  p.state_in = state_in; p.state_map = state_map; p.n_state = n_state;
+  p.state_final = state_final; p.d_state_out = d_state_out;
+  p.dr = dr; p.dk = dk; p.dv = dv; p.dw = dw; p.du = du; p.du_rows = du_rows; p.d_state_in = d_state_in;
+  p.dev_status = dev_status;
+  return launched(wkv::launch_wkv6_backward(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
+}
+
 wkv_status wkv6_forward_varlen(int num_slots, int H, int N, const int32_t *lengths, int max_len, int total_tokens,
                                const void *r, const void *k, const void *v, const void *w, wkv_dtype in_dtype,
                                const float *u, float *y, const float *state_in, float *state_out,

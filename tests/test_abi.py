@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(nat.SIGNATURES)
@@ -181,3 +181,24 @@ def test_resolve_algo(lib):
 def test_chunked_needs_bf16(lib):
     assert v6(lib, dt=nat.WKV_F32, algo=nat.WKV_ALGO_CHUNKED) == nat.WKV_ERR_UNSUPPORTED
     assert b"bf16" in lib.wkv_last_error()
+
+
+def bwd(lib, B=2, T=8, H=2, N=64, dt=1, dy=P, si=None, sm=None, ns=0, sf=None, dso=None, dr=P, dk=P, dv=P,
+        dw=P, du=P, dur=P, dsi=None):
+    return lib.wkv6_backward(B, T, H, N, P, P, P, P, dt, P, dy, si, sm, ns, sf, dso, dr, dk, dv, dw, du, dur, dsi,
+                             None, None)
+
+
+def test_v6_backward_validation(lib):
+    """Host-side checks of wkv6_backward (no launch happens for any of these)."""
+    assert bwd(lib, N=32) == 2                 # head size other than 64
+    assert bwd(lib, dt=7) == 2                 # unknown dtype
+    assert bwd(lib, B=0) == 1
+    assert bwd(lib, dy=None) == 1              # dy needed when T > 0
+    assert bwd(lib, dk=MIS) == 1               # dk must be 16-byte aligned
+    assert bwd(lib, du=None) == 1
+    assert bwd(lib, dur=None) == 1
+    assert bwd(lib, dso=P) == 1                # d_state_out without the forward's final state
+    assert b"state_final" in lib.wkv_last_error()
+    assert bwd(lib, sm=P) == 1                 # state_map without state_in
+    assert bwd(lib, si=P, ns=3) == 1           # n_state must be 1 or B without a map

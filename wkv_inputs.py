@@ -19,6 +19,9 @@ Distributions follow the workloads the WKV operator is run on:
   ``(batch, seq, hidden)``, u of ``(heads, head_size)``): as v5 but the decay
   parameter is per token and channel, ``x ~ U(-6, 0)`` rounded to bf16 like
   r, k, v.
+* v6 backward: upstream gradients ``dy ~ N(0, 1)`` fp32 of the output and
+  ``dS ~ N(0, 0.1)`` fp32 of the final state (a training step's incoming
+  gradients; drawn by their own generator, after the forward inputs).
 * varlen serving (the web-rwkv batched-inference section: slots, a per-call
   ``token_chunk_size`` budget): prompt lengths ``~ U{1..2048}`` per slot,
   initial states ``~ N(0, 0.1)`` fp32, per-token inputs as v6.
@@ -33,7 +36,7 @@ import numpy as np
 
 __all__ = [
     "bf16_round", "bf16_to_f32", "stored_f32",
-    "wkv4_inputs", "wkv5_inputs", "wkv6_inputs", "varlen_inputs",
+    "wkv4_inputs", "wkv5_inputs", "wkv6_inputs", "varlen_inputs", "wkv6_upstream",
 ]
 
 
@@ -177,3 +180,12 @@ def varlen_inputs(num_slots, H, N, seed=0, max_prompt=2048, decode_steps=256,
     return dict(S=num_slots, H=H, N=N, lengths=lengths, x=x, u=u, r=r, k=k, v=v,
                 state=state, decode=dec, dtype=dtype)
 
+
+
+def wkv6_upstream(B, T, H, N, seed=0, with_state=True):
+    """Upstream gradients of a v6 forward call: ``dy`` [B, T, H*N] ``~ N(0, 1)`` and
+    (optionally) ``d_state`` [B, H, N, N] ``~ N(0, 0.1)``, both fp32."""
+    rng = np.random.default_rng(seed)
+    dy = _normal(rng, (B, T, H * N), 1.0)
+    ds = _normal(rng, (B, H, N, N), 0.1) if with_state else None
+    return dict(dy=dy, d_state=ds)
