@@ -28,10 +28,14 @@
 //       P = k, Q = r, R = dy, a = d[i]  -> dv, and dS_0 at the end
 //   TBWD (time reversed, X = G^T, rows j, columns i, column decay):
 //       P = v, Q = dy, R = r, a = d[i]  -> dk, and dx from dr (TFWD's output)
-// 32 tokens at a time are staged through LDS as fp32 (wave w stages tokens
-// 4w..4w+3, lane = channel), per-wave partial outputs are summed through LDS
-// in a fixed order (deterministic), and the per-channel sums over time (du,
-// the dlam running sums) are walked by wave 0, one token after the other.
+// Tokens are staged through LDS as fp32 in blocks (wave w stages a run of
+// consecutive tokens of the block, lane = channel), per-wave partial outputs
+// are summed through LDS in a fixed order (deterministic), and the
+// per-channel sums over time (du, the dlam running sums) are walked by wave
+// 0, one token after the other.  TFWD and BWD do not depend on each other:
+// they run as one launch (blockIdx.z picks the sweep) with 16-token blocks, so
+// that two workgroups (64 KiB of LDS each) share a CU and each SIMD holds four
+// waves; TBWD reads TFWD's dr and runs after it with 32-token blocks.
 #include <type_traits>
 
 #include "common.hpp"
@@ -44,31 +48,36 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = kHead / kWaves;  // state rows per wave
-constexpr int kTB = 32;                 // tokens staged per block
-static_assert(4 * kWaves == kTB && 16 * kTB == kThreads, "staging: four tokens per wave; reduce: (token, quad)");
 
 enum Sweep { TFWD = 0, BWD = 1, TBWD = 2 };
 
-template <int MODE, bool BF16>
-__global__ void __launch_bounds__(kThreads) wkv6_bwd_sweep_kernel(BwdParams p) {
+template <int KTB>
+struct Smem {
+  float p[KTB][kHead], q[KTB][kHead];  // row factors
+  float al[KTB][kHead];                // decay d per (token, channel)
+  float r[KTB][kHead];                 // column factor R
+  float e0[KTB][kHead], e1[KTB][kHead], e2[KTB][kHead];  // per-sweep extras
+  float w[KTB][kHead];                 // per (token, channel) terms of the time sums
+  float y[KTB][kWaves][kHead];         // per-wave partial outputs
+  float bon[KTB];
+};
+
+template <int MODE, bool BF16, int KTB>
+__device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, int b) {
   constexpr bool REV = MODE != TFWD;      // tokens walked from the last one
   constexpr bool COLDECAY = MODE != BWD;  // decay on the state's columns (transposed state)
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  constexpr int TPW = KTB / kWaves;       // tokens each wave stages per block
+  constexpr int CPT = kHead * KTB / kThreads;  // channels per thread in the reduction
+  static_assert(TPW * kWaves == KTB && CPT * kThreads == kHead * KTB && (CPT == 2 || CPT == 4), "block shape");
+  auto &s_p = sm.p; auto &s_q = sm.q; auto &s_al = sm.al; auto &s_r = sm.r;
+  auto &s_e0 = sm.e0; auto &s_e1 = sm.e1; auto &s_e2 = sm.e2; auto &s_w = sm.w; auto &s_y = sm.y;
+  auto &s_bon = sm.bon;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long C = (long)p.H * kHead;
   const int T = p.T;
   const long row0 = (long)b * T;  // first token row of this batch row
-
-  __shared__ __align__(16) float s_p[kTB][kHead], s_q[kTB][kHead];  // row factors
-  __shared__ __align__(16) float s_al[kTB][kHead];                  // decay d per (token, channel)
-  __shared__ __align__(16) float s_r[kTB][kHead];                   // column factor R
-  __shared__ __align__(16) float s_e0[kTB][kHead], s_e1[kTB][kHead], s_e2[kTB][kHead];  // per-mode extras
-  __shared__ float s_bon[kTB];
-  __shared__ __align__(16) float s_y[kTB][kWaves][kHead];
-  __shared__ __align__(16) float s_w[kTB][kHead];  // per (token, channel) terms of the time sums
 
   // ---- initial state
   float X[kRows];
@@ -113,11 +122,11 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwd_sweep_kernel(BwdParams p) {
   // token of processing step q (0 .. T-1)
   auto tok = [&](int q) -> long { return row0 + (REV ? (T - 1 - q) : q); };
   // the next block's inputs, loaded one block ahead (steps past the end reread the last one)
-  float pr[4], pk[4], pv[4], px[4], pdy[4], pdr[4];
+  float pr[TPW], pk[TPW], pv[TPW], px[TPW], pdy[TPW], pdr[TPW];
   auto fetch = [&](int q0) {
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const long e = tok(min(q0 + 4 * wave + t4, T - 1)) * C + h * kHead + lane;
+    for (int t4 = 0; t4 < TPW; ++t4) {
+      const long e = tok(min(q0 + TPW * wave + t4, T - 1)) * C + h * kHead + lane;
       pr[t4] = load1<BF16>(p.r, e);
       pk[t4] = load1<BF16>(p.k, e);
       pv[t4] = load1<BF16>(p.v, e);
@@ -127,13 +136,13 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwd_sweep_kernel(BwdParams p) {
     }
   };
   if (T > 0) fetch(0);
-  for (int q0 = 0; q0 < T; q0 += kTB) {
-    const int nb = min(kTB, T - q0);
+  for (int q0 = 0; q0 < T; q0 += KTB) {
+    const int nb = min(KTB, T - q0);
     // ---- stage this block (token of step q0 + tt at row tt)
-    float bon[4];
+    float bon[TPW];
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int tt = 4 * wave + t4;
+    for (int t4 = 0; t4 < TPW; ++t4) {
+      const int tt = TPW * wave + t4;
       const float ex = fast_exp(px[t4]);
       s_al[tt][lane] = fast_exp(-ex);
       if (MODE == TFWD) {
@@ -157,9 +166,9 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwd_sweep_kernel(BwdParams p) {
         bon[t4] = pv[t4] * pdy[t4];
       }
     }
-    fetch(q0 + kTB);  // in flight during this block
+    fetch(q0 + KTB);  // in flight during this block
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {  // bonus scalar: sum over the 64 channels of the token
+    for (int t4 = 0; t4 < TPW; ++t4) {  // bonus scalar: sum over the 64 channels of the token
       float x = bon[t4];
 #pragma unroll
       for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
@@ -167,7 +176,7 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwd_sweep_kernel(BwdParams p) {
     }
     if (lane == 0) {
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) s_bon[4 * wave + t4] = bon[t4];
+      for (int t4 = 0; t4 < TPW; ++t4) s_bon[TPW * wave + t4] = bon[t4];
     }
     __syncthreads();
 
@@ -204,39 +213,42 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwd_sweep_kernel(BwdParams p) {
 
     // ---- sum the wave partials in a fixed order, add the u terms, store
     {
-      const int tt = tid >> 4, c = 4 * (tid & 15);
+      const int tt = tid / (kHead / CPT), c = CPT * (tid % (kHead / CPT));
       if (tt < nb) {
-        float o[4] = {0.f, 0.f, 0.f, 0.f};
+        float o[CPT];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float4 a = *reinterpret_cast<const float4 *>(&s_y[tt][w][c]);
-          o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
-        }
+        for (int m = 0; m < CPT; ++m) o[m] = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+          for (int m = 0; m < CPT; ++m) o[m] += s_y[tt][w][c + m];
         const float bt = s_bon[tt];
-        const float uu[4] = {p.u[h * kHead + c], p.u[h * kHead + c + 1], p.u[h * kHead + c + 2],
-                             p.u[h * kHead + c + 3]};
-        const float4 r4 = *reinterpret_cast<const float4 *>(&s_r[tt][c]);
-        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-        float res[4], wt[4];
+        float res[CPT], wt[CPT];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < CPT; ++m) {
+          const float um = p.u[h * kHead + c + m], rm = s_r[tt][c + m];
           if (MODE == TFWD) {  // dr; time-sum term of du: r k (dy . v)
-            res[m] = fmaf(uu[m] * rr[m], bt, o[m]);
-            wt[m] = s_e0[tt][c + m] * rr[m] * bt;
+            res[m] = fmaf(um * rm, bt, o[m]);
+            wt[m] = s_e0[tt][c + m] * rm * bt;
           } else if (MODE == BWD) {  // dv
-            res[m] = fmaf(bt, rr[m], o[m]);
+            res[m] = fmaf(bt, rm, o[m]);
             wt[m] = 0.f;
           } else {  // dk; decay-gradient term r dr~ (next steps) and k dk~ (this step)
             const float kk = s_e0[tt][c + m];
-            res[m] = fmaf(uu[m] * rr[m], bt, o[m]);
-            const float drt = s_e1[tt][c + m] - uu[m] * kk * bt;  // dr without its u term
-            s_e1[tt][c + m] = rr[m] * drt;
+            res[m] = fmaf(um * rm, bt, o[m]);
+            const float drt = s_e1[tt][c + m] - um * kk * bt;  // dr without its u term
+            s_e1[tt][c + m] = rm * drt;
             wt[m] = kk * o[m];
           }
         }
-        float *out = MODE == TFWD ? p.dr : (MODE == BWD ? p.dv : p.dk);
-        *reinterpret_cast<float4 *>(out + tok(q0 + tt) * C + h * kHead + c) = make_float4(res[0], res[1], res[2], res[3]);
-        if (MODE != BWD) *reinterpret_cast<float4 *>(&s_w[tt][c]) = make_float4(wt[0], wt[1], wt[2], wt[3]);
+        float *out = (MODE == TFWD ? p.dr : (MODE == BWD ? p.dv : p.dk)) + tok(q0 + tt) * C + h * kHead + c;
+        if constexpr (CPT == 4) {
+          *reinterpret_cast<float4 *>(out) = make_float4(res[0], res[1], res[2], res[3]);
+          if (MODE != BWD) *reinterpret_cast<float4 *>(&s_w[tt][c]) = make_float4(wt[0], wt[1], wt[2], wt[3]);
+        } else {
+          *reinterpret_cast<float2 *>(out) = make_float2(res[0], res[1]);
+          if (MODE != BWD) *reinterpret_cast<float2 *>(&s_w[tt][c]) = make_float2(wt[0], wt[1]);
+        }
       }
     }
     __syncthreads();
@@ -265,6 +277,19 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwd_sweep_kernel(BwdParams p) {
   }
 }
 
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads, 2) wkv6_bwd_pair_kernel(BwdParams p) {
+  __shared__ __align__(16) Smem<16> sm;
+  if (blockIdx.z == 0) sweep<TFWD, BF16, 16>(p, sm, blockIdx.x, blockIdx.y);
+  else sweep<BWD, BF16, 16>(p, sm, blockIdx.x, blockIdx.y);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) wkv6_bwd_tbwd_kernel(BwdParams p) {
+  __shared__ __align__(16) Smem<32> sm;
+  sweep<TBWD, BF16, 32>(p, sm, blockIdx.x, blockIdx.y);
+}
+
 // du[c] = sum over batch rows of du_rows[b][c], in row order.
 __global__ void __launch_bounds__(256) wkv6_du_sum_kernel(const float *du_rows, float *du, int B, int C) {
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -274,23 +299,17 @@ __global__ void __launch_bounds__(256) wkv6_du_sum_kernel(const float *du_rows, 
   du[c] = s;
 }
 
-template <int MODE>
-hipError_t launch_sweep(const BwdParams &p, bool bf16, hipStream_t s) {
-  dim3 grid(p.H, p.B);
-  if (bf16) hipLaunchKernelGGL((wkv6_bwd_sweep_kernel<MODE, true>), grid, dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((wkv6_bwd_sweep_kernel<MODE, false>), grid, dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_wkv6_backward(const BwdParams &p, bool bf16, hipStream_t s) {
-  // dr first: the dk / dx sweep reads it
-  hipError_t e = launch_sweep<TFWD>(p, bf16, s);
+  // TFWD and BWD together, then TBWD (it reads TFWD's dr)
+  if (bf16) hipLaunchKernelGGL(wkv6_bwd_pair_kernel<true>, dim3(p.H, p.B, 2), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(wkv6_bwd_pair_kernel<false>, dim3(p.H, p.B, 2), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_sweep<TBWD>(p, bf16, s);
-  if (e != hipSuccess) return e;
-  e = launch_sweep<BWD>(p, bf16, s);
+  if (bf16) hipLaunchKernelGGL(wkv6_bwd_tbwd_kernel<true>, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(wkv6_bwd_tbwd_kernel<false>, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int C = p.H * kHead;
   hipLaunchKernelGGL(wkv6_du_sum_kernel, dim3((C + 255) / 256), dim3(256), 0, s, p.du_rows, p.du, p.B, C);
