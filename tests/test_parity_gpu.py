@@ -253,3 +253,30 @@ def test_v6_split_carry_matches_single_pass(split):
         # elsewhere the blocks differ and so does the rounding, at the fp32 level
         assert_fp32(host(y2), host(y), "split y vs one pass")
         assert_fp32(host(Sb), host(S), "split state vs one pass")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("side", ["left", "right"])
+def test_v6_padding_by_decay_mask(algo, side):
+    """The rwkv_ops page's padding convention: padded tokens carry zero r, k, v and a decay
+    parameter of -1e9 (decay exactly 1), so they leave the state as it is.  The real tokens'
+    outputs and the final state then equal those of the unpadded call."""
+    T, P = 100, 37
+    inp = wkv6_inputs(2, T, 2, 64, seed=77, init_state=2)
+    pad = {}
+    for n in ("r", "k", "v", "x"):
+        a = inp[n]
+        fill = np.zeros((2, P, a.shape[2]), dtype=a.dtype)
+        if n == "x":
+            fill[:] = 0xCE6E  # bf16 bits of -9.98e8 (the -1e9 mask rounded into bf16)
+        pad[n] = np.concatenate([fill, a] if side == "left" else [a, fill], axis=1)
+    padded = dict(inp, **pad, T=T + P)
+    y, S = _run56(6, inp, algo, state=dev(inp["state"]))
+    yp, Sp = _run56(6, padded, algo, state=dev(inp["state"]))
+    torch.cuda.synchronize()
+    real = yp[:, P:] if side == "left" else yp[:, :T]
+    # the two calls group the real tokens into different blocks / chunks, so they agree to the
+    # algorithm's own rounding: fp32 for the scan, the bf16-input tolerance for the chunked form
+    check = assert_fp32 if algo == "scan" else assert_bf16
+    check(host(real), host(y), f"{side} padding y")
+    check(host(Sp), host(S), f"{side} padding state")
