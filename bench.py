@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving", "wkv6_bwd"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
+    ap.add_argument("--head-first", action="store_true",
+                    help="wkv5/wkv6: head-first [B,H,T,N] token arrays instead of [B,T,H,N]")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
+                    help="wkv5/wkv6: dtype of y (bf16 = the fp32 result rounded to nearest even)")
     ap.add_argument("--B", type=int, default=None)
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--H", type=int, default=32)
@@ -172,22 +176,29 @@ def workload_wkv56(args, version):
 
     B, T, H, N = args.B or 8, args.T or 4096, args.H, 64
     C = H * N
+    hf = args.head_first
+    ybf = args.out_dtype == "bf16"
     inp = (wkv6_inputs if version == 6 else wkv5_inputs)(B, T, H, N, seed=args.seed)
-    r, k, v = (_bf16_dev(inp[n]) for n in ("r", "k", "v"))
-    x = _bf16_dev(inp["x"]) if version == 6 else torch.from_numpy(inp["x"]).cuda()
+
+    def tok(a):  # device copy in the chosen token layout
+        t = _bf16_dev(a)
+        return t.view(B, T, H, N).permute(0, 2, 1, 3).contiguous() if hf else t
+    r, k, v = (tok(inp[n]) for n in ("r", "k", "v"))
+    x = tok(inp["x"]) if version == 6 else torch.from_numpy(inp["x"]).cuda()
     u = torch.from_numpy(inp["u"]).cuda()
-    y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
+    y = torch.empty((B, H, T, N) if hf else (B, T, C), dtype=torch.bfloat16 if ybf else torch.float32,
+                    device="cuda")
     S = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
     algo = wkv.resolve_algo(version, B, T, H, N, args.algo)
     fwd = wkv.wkv6_forward if version == 6 else wkv.wkv5_forward
     kernel = "wkv56_chunked_kernel" if algo == "chunked" else "wkv56_scan_kernel"
     tc = B * T * C
     in_bytes = (4 if version == 6 else 3) * 2 * tc + (0 if version == 6 else 4 * C)
-    alg_bytes = in_bytes + 4 * tc + 4 * B * H * N * N + 4 * C  # inputs + y + state_out + u
+    alg_bytes = in_bytes + (2 if ybf else 4) * tc + 4 * B * H * N * N + 4 * C  # inputs + y + state_out + u
     flops = 2 * 3 * N * tc  # scan: 3 FMA per state element and token
 
     def run():
-        fwd(r, k, v, x, u, H, algo=algo, y=y, state_out=S)
+        fwd(r, k, v, x, u, H, algo=algo, y=y, state_out=S, head_first=hf)
 
     def cpu(target_s):
         import oracle
@@ -199,7 +210,8 @@ def workload_wkv56(args, version):
                                 threads=threads)
         res, units, (yo, So) = _oracle_units_baseline(inp, target_s, units_all, run_units, T * N,
                                                       f"(batch row, head) units x T={T} x N={N}")
-        yg, Sg = y.cpu().numpy(), S.cpu().numpy()
+        yt = y.permute(0, 2, 1, 3).reshape(B, T, C) if hf else y
+        yg, Sg = yt.float().cpu().numpy(), S.cpu().numpy()
         ys = np.stack([yg[b, :, h * N:(h + 1) * N] for b, h in units])
         yos = np.stack([yo[b, :, h * N:(h + 1) * N] for b, h in units])
         ymax, ymean = _err(ys, yos)
@@ -208,9 +220,11 @@ def workload_wkv56(args, version):
                      "state_max_abs": smax, "state_mean_abs": smean}
 
     name = f"WKV{version}"
+    variant = ("_headfirst" if hf else "") + ("_ybf16" if ybf else "")
+    layout = "head-first [B,H,T,N]" if hf else "[B,T,H,N]"
     return {
         "metric": f"{name} fwd tokens·channels/s + % HBM peak (rocprof), B={B} T={T} H={H} N={N}",
-        "workload_key": f"wkv{version}_B{B}_T{T}_H{H}_N{N}_bf16",
+        "workload_key": f"wkv{version}_B{B}_T{T}_H{H}_N{N}_bf16{variant}",
         "launches": [("forward", kernel, run, alg_bytes, flops)],
         "tc": tc,
         "dtype": "bf16" if algo == "chunked" else "fp32",
@@ -218,9 +232,10 @@ def workload_wkv56(args, version):
                     else "fp32 vector ALU"),
         "data": "synthetic (seeded numpy PCG64; bf16 r,k,v" + (",x" if version == 6 else "; fp32 x") +
                 "; fp32 u; zero initial state)",
-        "config": {"workload": f"{name} forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
-                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
-                   "parallelism": "single GPU"},
+        "config": {"workload": f"{name} forward B={B} T={T} H={H} N={N}, bf16 inputs {layout}, fp32 state, "
+                               f"{'bf16' if ybf else 'fp32'} output",
+                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "layout": "BHTN" if hf else "BTHN",
+                   "y_dtype": args.out_dtype, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "cpu": cpu,
     }
 

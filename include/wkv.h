@@ -38,7 +38,9 @@
  *   - Every array argument is a DEVICE pointer owned by the caller, row-major
  *     and contiguous, aligned to at least 16 bytes.  The library never
  *     allocates, frees or copies caller memory between host and device.
- *   - Token arrays are [B, T, C] (C = H*N, not head-first).  y is always fp32.
+ *   - Token arrays are [B, T, C] (C = H*N) and y is fp32, except in the _ex
+ *     entry points, which also take head-first [B, H, T, N] arrays and a bf16
+ *     y.
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
  *     and return before it completes.  Results are valid once the stream has
  *     been synchronised.
@@ -76,6 +78,10 @@ typedef int32_t wkv_dtype;
 #define WKV_F32   0             /* 32-bit IEEE float inputs                       */
 #define WKV_BF16  1             /* bfloat16 inputs (upper half of an fp32)        */
 
+typedef int32_t wkv_layout;
+#define WKV_LAYOUT_BTHN 0       /* [B,T,H,N]: token rows hold every head          */
+#define WKV_LAYOUT_BHTN 1       /* [B,H,T,N]: head-first, a head's tokens adjacent */
+
 typedef int32_t wkv_algo;
 #define WKV_ALGO_AUTO     0     /* library picks                                  */
 #define WKV_ALGO_SCAN     1     /* token-sequential scan on the vector ALUs       */
@@ -112,6 +118,20 @@ WKV_API wkv_status wkv4_forward(int B, int T, int C,
                         void *stream);
 
 /*
+ * v4 forward with a choice of output dtype: as wkv4_forward, with
+ *   y          [B,T,C]    out_dtype: WKV_F32, or WKV_BF16 (the fp32 result
+ *                         rounded to nearest even; the rwkv_ops page's
+ *                         single-step operator returns its output in the
+ *                         input dtype)
+ */
+WKV_API wkv_status wkv4_forward_ex(int B, int T, int C,
+                           const float *time_decay, const float *time_first,
+                           const void *k, const void *v, const void *r,
+                           wkv_dtype in_dtype, void *y, wkv_dtype out_dtype,
+                           const float *state_in, float *state_out,
+                           void *stream);
+
+/*
  * v5 forward (static decay).
  *   r, k, v    [B,T,H*N]  in_dtype
  *   w          [H*N] fp32 raw decay parameter; decay exp(-exp(w))
@@ -146,6 +166,33 @@ WKV_API wkv_status wkv6_forward(int B, int T, int H, int N,
                         void *stream);
 
 /*
+ * v5 / v6 forward with a choice of token layout and output dtype (the
+ * rwkv_ops page's generalized_delta_rule interface takes both layouts through
+ * its head_first flag, and its single-step operator returns the input dtype):
+ *   layout     WKV_LAYOUT_BTHN: r, k, v, w (v6) and y are [B,T,H,N];
+ *              WKV_LAYOUT_BHTN: they are [B,H,T,N]
+ *   y          out_dtype: WKV_F32, or WKV_BF16 (the fp32 result rounded to
+ *              nearest even)
+ * Everything else as wkv5_forward / wkv6_forward (states are [.., H, N, N]
+ * in both layouts; v5's w and u are [H*N]).  Both layouts give bitwise the
+ * same values, and the bf16 output is bitwise the fp32 output rounded.
+ */
+WKV_API wkv_status wkv5_forward_ex(int B, int T, int H, int N,
+                           const void *r, const void *k, const void *v,
+                           wkv_dtype in_dtype, wkv_layout layout,
+                           const float *w, const float *u, void *y, wkv_dtype out_dtype,
+                           const float *state_in, const int32_t *state_map, int n_state,
+                           float *state_out, wkv_algo algo, int32_t *dev_status,
+                           void *stream);
+WKV_API wkv_status wkv6_forward_ex(int B, int T, int H, int N,
+                           const void *r, const void *k, const void *v, const void *w,
+                           wkv_dtype in_dtype, wkv_layout layout,
+                           const float *u, void *y, wkv_dtype out_dtype,
+                           const float *state_in, const int32_t *state_map, int n_state,
+                           float *state_out, wkv_algo algo, int32_t *dev_status,
+                           void *stream);
+
+/*
  * v6 varlen forward for batched serving.
  *   lengths      [num_slots] int32 DEVICE: tokens slot s consumes this call
  *                (0 = empty slot: no work, its state row is untouched, or
@@ -171,6 +218,16 @@ WKV_API wkv_status wkv6_forward_varlen(int num_slots, int H, int N,
                                const float *state_in, float *state_out,
                                const int32_t *state_map, int n_state,
                                int32_t *dev_status, void *stream);
+
+/* wkv6_forward_varlen with y [total_tokens, H*N] in out_dtype (WKV_F32 or
+ * WKV_BF16, the fp32 result rounded to nearest even). */
+WKV_API wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N,
+                                  const int32_t *lengths, int max_len, int total_tokens,
+                                  const void *r, const void *k, const void *v, const void *w,
+                                  wkv_dtype in_dtype, const float *u, void *y, wkv_dtype out_dtype,
+                                  const float *state_in, float *state_out,
+                                  const int32_t *state_map, int n_state,
+                                  int32_t *dev_status, void *stream);
 
 /*
  * v6 backward: gradients for training (the RWKV-6 recurrence of wkv6_forward,

@@ -7,8 +7,10 @@ no CPU or PyTorch fallback, and importing the package fails if the library
 has not been built.
 
 Tensors are row-major and contiguous, token arrays [B, T, C] with C = H*N
-(varlen: packed [total_tokens, C]); inputs are torch.bfloat16 or
-torch.float32; outputs and states are float32.  Calls are asynchronous on
+(varlen: packed [total_tokens, C]), or head-first [B, H, T, N] for v5 / v6
+with ``head_first=True``; inputs are torch.bfloat16 or torch.float32; y is
+float32, or bfloat16 with ``out_dtype=torch.bfloat16`` (the fp32 result
+rounded to nearest even); states are float32.  Calls are asynchronous on
 torch's current stream.
 """
 from __future__ import annotations
@@ -67,6 +69,16 @@ def _stream(ref):
     return ctypes.c_void_p(torch.cuda.current_stream(ref.device).cuda_stream)
 
 
+def _out_code(y, out_dtype):
+    """Output dtype code: that of a given y, else out_dtype (float32 or bfloat16)."""
+    dt = y.dtype if y is not None else out_dtype
+    if dt == torch.float32:
+        return _native.WKV_F32, dt
+    if dt == torch.bfloat16:
+        return _native.WKV_BF16, dt
+    raise TypeError(f"unsupported output dtype {dt} (float32 or bfloat16)")
+
+
 def _same_dtype(name_tensors):
     dts = {t.dtype for _, t in name_tensors if t is not None}
     if len(dts) != 1:
@@ -75,37 +87,52 @@ def _same_dtype(name_tensors):
 
 
 def wkv4_forward(time_decay, time_first, k, v, r=None, state=None, *, y=None, state_out=None,
-                 return_state=True):
+                 return_state=True, out_dtype=torch.float32):
     """v4 WKV.  k, v, r: [B, T, C]; time_decay, time_first: [C] fp32; state: [B, 3, C] fp32 (a, b, p).
 
-    Returns ``(y, state_out)`` (``state_out`` None unless ``return_state``).
+    Returns ``(y, state_out)`` (``state_out`` None unless ``return_state``); y is
+    ``out_dtype`` (float32 or bfloat16) unless given.
     """
     B, T, C = k.shape
     _same_dtype([("k", k), ("v", v), ("r", r)])
     _dev(k, "k", shape=(B, T, C)); _dev(v, "v", shape=(B, T, C)); _dev(r, "r", shape=(B, T, C))
     _dev(time_decay, "time_decay", torch.float32, (C,)); _dev(time_first, "time_first", torch.float32, (C,))
     _dev(state, "state", torch.float32, (B, 3, C))
+    oc, odt = _out_code(y, out_dtype)
     if y is None:
-        y = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
-    _dev(y, "y", torch.float32, (B, T, C))
+        y = torch.empty((B, T, C), dtype=odt, device=k.device)
+    _dev(y, "y", odt, (B, T, C))
     if return_state and state_out is None:
         state_out = torch.empty((B, 3, C), dtype=torch.float32, device=k.device)
     _dev(state_out, "state_out", torch.float32, (B, 3, C))
-    check(_lib.wkv4_forward(B, T, C, _ptr(time_decay), _ptr(time_first), _ptr(k), _ptr(v), _ptr(r),
-                            _dtype_code(k), _ptr(y), _ptr(state), _ptr(state_out), _stream(k)))
+    head = (B, T, C, _ptr(time_decay), _ptr(time_first), _ptr(k), _ptr(v), _ptr(r), _dtype_code(k), _ptr(y))
+    tail = (_ptr(state), _ptr(state_out), _stream(k))
+    if oc == _native.WKV_F32:
+        check(_lib.wkv4_forward(*head, *tail))
+    else:
+        check(_lib.wkv4_forward_ex(*head, oc, *tail))
     return y, state_out
 
 
-def _dense56(version, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status):
-    B, T, C = r.shape
-    if C % H:
-        raise ValueError(f"C={C} is not a multiple of H={H}")
-    N = C // H
+def _dense56(version, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status,
+             head_first=False, out_dtype=torch.float32):
+    if head_first:
+        if r.dim() != 4 or r.shape[1] != H:
+            raise ValueError(f"head-first r must be [B, {H}, T, N], got {tuple(r.shape)}")
+        B, _, T, N = r.shape
+        C = H * N
+        tok_shape = (B, H, T, N)
+    else:
+        B, T, C = r.shape
+        if C % H:
+            raise ValueError(f"C={C} is not a multiple of H={H}")
+        N = C // H
+        tok_shape = (B, T, C)
     _same_dtype([("r", r), ("k", k), ("v", v)] + ([("w", w)] if version == 6 else []))
     for name, t in (("r", r), ("k", k), ("v", v)):
-        _dev(t, name, shape=(B, T, C))
+        _dev(t, name, shape=tok_shape)
     if version == 6:
-        _dev(w, "w", shape=(B, T, C))
+        _dev(w, "w", shape=tok_shape)
     else:
         _dev(w, "w", torch.float32, (C,))
     _dev(u.reshape(-1) if u.dim() == 2 else u, "u", torch.float32, (C,))
@@ -116,41 +143,55 @@ def _dense56(version, r, k, v, w, u, H, state, state_map, algo, y, state_out, re
             raise ValueError(f"state must be [n_state, {H}, {N}, {N}], got {tuple(state.shape)}")
         n_state = state.shape[0]
     _dev(state_map, "state_map", torch.int32, (B,))
+    oc, odt = _out_code(y, out_dtype)
     if y is None:
-        y = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
-    _dev(y, "y", torch.float32, (B, T, C))
+        y = torch.empty(tok_shape, dtype=odt, device=r.device)
+    _dev(y, "y", odt, tok_shape)
     if return_state and state_out is None:
         state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
     _dev(state_out, "state_out", torch.float32, (B, H, N, N))
     _dev(dev_status, "dev_status", torch.int32, (1,))
-    fn = _lib.wkv5_forward if version == 5 else _lib.wkv6_forward
     a = _ALGOS[algo] if isinstance(algo, str) else int(algo)
-    common = (_ptr(u), _ptr(y), _ptr(state), _ptr(state_map), n_state, _ptr(state_out), a,
-              _ptr(dev_status), _stream(r))
-    if version == 5:
-        check(fn(B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _dtype_code(r), _ptr(w), *common))
+    tail = (_ptr(state), _ptr(state_map), n_state, _ptr(state_out), a, _ptr(dev_status), _stream(r))
+    toks = (_ptr(r), _ptr(k), _ptr(v)) if version == 5 else (_ptr(r), _ptr(k), _ptr(v), _ptr(w))
+    if oc == _native.WKV_F32 and not head_first:
+        if version == 5:
+            check(_lib.wkv5_forward(B, T, H, N, *toks, _dtype_code(r), _ptr(w), _ptr(u), _ptr(y), *tail))
+        else:
+            check(_lib.wkv6_forward(B, T, H, N, *toks, _dtype_code(r), _ptr(u), _ptr(y), *tail))
     else:
-        check(fn(B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r), *common))
+        layout = _native.WKV_LAYOUT_BHTN if head_first else _native.WKV_LAYOUT_BTHN
+        if version == 5:
+            check(_lib.wkv5_forward_ex(B, T, H, N, *toks, _dtype_code(r), layout, _ptr(w), _ptr(u), _ptr(y), oc,
+                                       *tail))
+        else:
+            check(_lib.wkv6_forward_ex(B, T, H, N, *toks, _dtype_code(r), layout, _ptr(u), _ptr(y), oc, *tail))
     return y, state_out
 
 
 def wkv5_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y=None, state_out=None,
-                 return_state=True, dev_status=None):
-    """v5 WKV (static decay).  r, k, v: [B, T, H*N]; w, u: [H*N] fp32 (w = raw decay parameter).
+                 return_state=True, dev_status=None, head_first=False, out_dtype=torch.float32):
+    """v5 WKV (static decay).  r, k, v: [B, T, H*N] ([B, H, T, N] with ``head_first``);
+    w, u: [H*N] fp32 (w = raw decay parameter).
 
     ``state``: [n_state, H, N, N] fp32 initial states; ``state_map``: [B] int32.
-    Returns ``(y [B, T, H*N] fp32, state_out [B, H, N, N] fp32 or None)``.
+    Returns ``(y, state_out [B, H, N, N] fp32 or None)``; y has the token layout
+    of r and dtype ``out_dtype`` (float32 or bfloat16) unless given.
     """
-    return _dense56(5, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status)
+    return _dense56(5, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status,
+                    head_first, out_dtype)
 
 
 def wkv6_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y=None, state_out=None,
-                 return_state=True, dev_status=None):
-    """v6 WKV (per-token decay).  r, k, v, w: [B, T, H*N] (same dtype); u: [H*N] or [H, N] fp32.
+                 return_state=True, dev_status=None, head_first=False, out_dtype=torch.float32):
+    """v6 WKV (per-token decay).  r, k, v, w: [B, T, H*N] ([B, H, T, N] with ``head_first``), one
+    dtype; u: [H*N] or [H, N] fp32.
 
-    Returns ``(y [B, T, H*N] fp32, state_out [B, H, N, N] fp32 or None)``.
+    Returns ``(y, state_out [B, H, N, N] fp32 or None)``; y has the token layout
+    of r and dtype ``out_dtype`` (float32 or bfloat16) unless given.
     """
-    return _dense56(6, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status)
+    return _dense56(6, r, k, v, w, u, H, state, state_map, algo, y, state_out, return_state, dev_status,
+                    head_first, out_dtype)
 
 
 def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_final=None, d_state=None,
@@ -203,18 +244,19 @@ class VarlenPlan:
     the same call on the same buffers).  ``y`` is the output tensor.
     """
 
-    def __init__(self, args, y, tensors):
+    def __init__(self, fn, args, y, tensors):
+        self._fn = fn
         self._args = args
         self._tensors = tensors  # the plan holds raw pointers: keep their tensors alive
         self.y = y
 
     def __call__(self):
-        check(_lib.wkv6_forward_varlen(*self._args))
+        check(self._fn(*self._args))
         return self.y
 
 
 def varlen_plan(lengths, r, k, v, w, u, H, state, *, max_len, state_out=None, state_map=None, y=None,
-                dev_status=None):
+                dev_status=None, out_dtype=torch.float32):
     """Validate and marshal a varlen call once; see :func:`wkv6_forward_varlen` for the arguments."""
     S = lengths.shape[0]
     total, C = r.shape
@@ -233,26 +275,31 @@ def varlen_plan(lengths, r, k, v, w, u, H, state, *, max_len, state_out=None, st
         state_out = state
     _dev(state_out, "state_out", torch.float32, tuple(state.shape))
     _dev(state_map, "state_map", torch.int32, (S,))
+    oc, odt = _out_code(y, out_dtype)
     if y is None:
-        y = torch.empty((total, C), dtype=torch.float32, device=r.device)
-    _dev(y, "y", torch.float32, (total, C))
+        y = torch.empty((total, C), dtype=odt, device=r.device)
+    _dev(y, "y", odt, (total, C))
     _dev(dev_status, "dev_status", torch.int32, (1,))
-    args = (S, H, N, _ptr(lengths), int(max_len), total, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r),
-            _ptr(u), _ptr(y), _ptr(state), _ptr(state_out), _ptr(state_map), state.shape[0], _ptr(dev_status),
-            _stream(r))
-    return VarlenPlan(args, y, (lengths, r, k, v, w, u, y, state, state_out, state_map, dev_status))
+    head = (S, H, N, _ptr(lengths), int(max_len), total, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r),
+            _ptr(u), _ptr(y))
+    tail = (_ptr(state), _ptr(state_out), _ptr(state_map), state.shape[0], _ptr(dev_status), _stream(r))
+    if oc == _native.WKV_F32:
+        fn, args = _lib.wkv6_forward_varlen, head + tail
+    else:
+        fn, args = _lib.wkv6_forward_varlen_ex, head + (oc,) + tail
+    return VarlenPlan(fn, args, y, (lengths, r, k, v, w, u, y, state, state_out, state_map, dev_status))
 
 
 def wkv6_forward_varlen(lengths, r, k, v, w, u, H, state, *, max_len, state_out=None, state_map=None,
-                        y=None, dev_status=None):
+                        y=None, dev_status=None, out_dtype=torch.float32):
     """Varlen v6 over packed token rows; updates ``state_out`` (default: ``state`` in place).
 
     ``lengths``: [S] int32 device tensor (tokens each slot consumes); ``r, k, v, w``:
     [total_tokens, H*N]; ``state``: [n_state, H, N, N] fp32; ``state_map``: [S] int32.
-    Returns ``y`` [total_tokens, H*N] fp32.
+    Returns ``y`` [total_tokens, H*N] in ``out_dtype`` (float32 or bfloat16) unless given.
     """
     return varlen_plan(lengths, r, k, v, w, u, H, state, max_len=max_len, state_out=state_out,
-                       state_map=state_map, y=y, dev_status=dev_status)()
+                       state_map=state_map, y=y, dev_status=dev_status, out_dtype=out_dtype)()
 
 
 def schedule_round_robin(remaining, budget):

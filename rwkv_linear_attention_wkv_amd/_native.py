@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(PKG, "lib", "libwkv.so")
 WKV_OK, WKV_ERR_INVALID_ARG, WKV_ERR_UNSUPPORTED, WKV_ERR_DEVICE = 0, 1, 2, 3
 WKV_F32, WKV_BF16 = 0, 1
 WKV_ALGO_AUTO, WKV_ALGO_SCAN, WKV_ALGO_CHUNKED = 0, 1, 2
+WKV_LAYOUT_BTHN, WKV_LAYOUT_BHTN = 0, 1
 WKV_DEV_BAD_STATE_MAP = 1
 WKV_DEV_BAD_LENGTH = 2
 WKV_DEV_TOKEN_OVERFLOW = 4
@@ -23,12 +24,19 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 # name -> (restype, argtypes); mirrors include/wkv.h
 SIGNATURES = {
     "wkv4_forward": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "wkv4_forward_ex": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp]),
     "wkv5_forward": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp]),
+    "wkv5_forward_ex": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _i,
+                             _vp, _vp]),
     "wkv6_forward": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp]),
+    "wkv6_forward_ex": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _vp, _i, _vp, _i,
+                             _vp, _vp]),
     "wkv6_backward": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "wkv6_forward_varlen": (_i, [_i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i,
                                  _vp, _vp]),
+    "wkv6_forward_varlen_ex": (_i, [_i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
+                                    _vp, _i, _vp, _vp]),
     "wkv_schedule_round_robin": (_i, [_i, _i32p, _i, _i32p, _i32p]),
     "wkv_resolve_algo": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "wkv_status_string": (ctypes.c_char_p, [_i]),

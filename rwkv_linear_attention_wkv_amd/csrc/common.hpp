@@ -16,6 +16,18 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 // Four consecutive input elements starting at element `idx`, widened to fp32.
 // bf16 reads 8 bytes, fp32 reads 16 bytes; idx must be a multiple of 4.
+// Two floats -> packed bf16 pair (round to nearest even): low half = a.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(a);
+  v[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// One float -> bf16 bits (round to nearest even).
+__device__ __forceinline__ uint16_t bf16_bits(float a) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a)); }
+
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void *base, long idx) {
   if constexpr (BF16) {

@@ -17,7 +17,13 @@ struct ScanParams {
   int H;
   const void *r, *k, *v, *w;  // w: [H*N] fp32 (v5) or token array (v6)
   const float *u;
-  float *y;
+  void *y;          // fp32, or bf16 when y_bf16
+  bool y_bf16;      // y rounded to bf16 (nearest even) instead of fp32
+  // Dense layout: element (row b, token t, head h, channel i) of r, k, v, w
+  // (v6) and y sits at b * row_stride + t * tok_stride + h * head_stride + i.
+  // [B,T,H,N]: (T*H*N, H*N, N); head-first [B,H,T,N]: (H*T*N, N, T*N).
+  // Varlen rows are packed [total_tokens, H*N]: tok_stride H*N, head_stride N.
+  long row_stride, tok_stride, head_stride;
   const float *state_in;
   const int32_t *state_map;
   int n_state;
@@ -60,7 +66,8 @@ struct V4Params {
   int B, T, C;
   const float *tau, *u;
   const void *k, *v, *r;
-  float *y;
+  void *y;       // fp32, or bf16 when y_bf16
+  bool y_bf16;   // y rounded to bf16 (nearest even) instead of fp32
   const float *state_in;
   float *state_out;
 };

@@ -90,7 +90,7 @@ __device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t rs, int voff, i
   else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
 }
 
-template <bool BF16, bool HAS_R>
+template <bool BF16, bool HAS_R, bool OUTB>
 __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p) {
   __shared__ float agg[kMaxSeg][3][kLanes];
   __shared__ float rstate[3][kLanes];
@@ -156,13 +156,17 @@ __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p)
       a = ra; bb = rb; pp = rp;
       const float lam_seg = lam * (float)kSeg;
       for (int w = 0; w < g; ++w) fold(a, bb, pp, lam_seg, agg[w][0][lane], agg[w][1][lane], agg[w][2][lane]);
+      constexpr int kOut = OUTB ? 2 : 4;
       const auto ry = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<char *>(p.y) + ((long)b * p.T + r0) * C * 4, 0, per_round * (int)C * 4, 0x00020000);
-      const int soff_y = g * kSeg * (int)C * 4;
+          reinterpret_cast<char *>(p.y) + ((long)b * p.T + r0) * C * kOut, 0, per_round * (int)C * kOut, 0x00020000);
+      const int soff_y = g * kSeg * (int)C * kOut;
 #pragma unroll
       for (int j = 0; j < kSeg; ++j) {
         const float out = wkv_out<HAS_R>(a, bb, pp, u, kk[j], vv[j], HAS_R ? rr[j] : 0.f);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ry, c * 4, soff_y + j * (int)C * 4, 0);
+        if constexpr (OUTB)
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(out), ry, c * 2, soff_y + j * (int)C * 2, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), ry, c * 4, soff_y + j * (int)C * 4, 0);
         absorb(a, bb, pp, lam, kk[j], vv[j]);
       }
       if (g == G - 1) {  // this wave holds the round's last token
@@ -215,7 +219,10 @@ __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p)
       for (int j = 0; j < kSeg; ++j) {
         if (j < n) {  // n is wave-uniform
           const float out = wkv_out<HAS_R>(a, bb, pp, u, kk[j], vv[j], rr[j]);
-          if (live) p.y[base + (long)(t0 + j) * C] = out;
+          if (live) {
+            if constexpr (OUTB) static_cast<uint16_t *>(p.y)[base + (long)(t0 + j) * C] = bf16_bits(out);
+            else static_cast<float *>(p.y)[base + (long)(t0 + j) * C] = out;
+          }
           absorb(a, bb, pp, lam, kk[j], vv[j]);
         }
       }
@@ -238,7 +245,7 @@ __global__ void __launch_bounds__(kLanes * kMaxSeg) wkv4_scan_kernel(V4Params p)
   }
 }
 
-template <bool BF16, bool HAS_R>
+template <bool BF16, bool HAS_R, bool OUTB>
 hipError_t launch(const V4Params &p, hipStream_t s) {
   const int cblocks = (p.C + kLanes - 1) / kLanes;
   // Enough waves to cover the chip (about 16 per CU on 256 CUs), but no more segments than tokens need.
@@ -246,16 +253,21 @@ hipError_t launch(const V4Params &p, hipStream_t s) {
   int G = (int)std::min<long>(kMaxSeg, std::max<long>(1, want));
   G = std::max(1, std::min(G, (p.T + kSeg - 1) / kSeg));
   dim3 grid(cblocks, p.B);
-  hipLaunchKernelGGL((wkv4_scan_kernel<BF16, HAS_R>), grid, dim3(kLanes * G), 0, s, p);
+  hipLaunchKernelGGL((wkv4_scan_kernel<BF16, HAS_R, OUTB>), grid, dim3(kLanes * G), 0, s, p);
   return hipGetLastError();
+}
+
+template <bool OUTB>
+hipError_t launch_out(const V4Params &p, bool bf16, hipStream_t s) {
+  const bool r = p.r != nullptr;
+  if (bf16) return r ? launch<true, true, OUTB>(p, s) : launch<true, false, OUTB>(p, s);
+  return r ? launch<false, true, OUTB>(p, s) : launch<false, false, OUTB>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_wkv4(const V4Params &p, bool bf16, hipStream_t s) {
-  const bool r = p.r != nullptr;
-  if (bf16) return r ? launch<true, true>(p, s) : launch<true, false>(p, s);
-  return r ? launch<false, true>(p, s) : launch<false, false>(p, s);
+  return p.y_bf16 ? launch_out<true>(p, bf16, s) : launch_out<false>(p, bf16, s);
 }
 
 }  // namespace wkv

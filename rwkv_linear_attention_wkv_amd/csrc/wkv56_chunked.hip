@@ -85,14 +85,6 @@ struct Smem {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Two floats -> packed bf16 pair (round to nearest even): low half = a.
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v;
-  v[0] = static_cast<__bf16>(a);
-  v[1] = static_cast<__bf16>(b);
-  return __builtin_bit_cast(uint32_t, v);
-}
 // Split two floats into packed hi and lo bf16 pairs.
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
   hi = pack_bf16(a, b);
@@ -155,7 +147,7 @@ __device__ __forceinline__ long uniform64(long x) {
 // point, so the wait for the load lands here.
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
-template <bool V6>
+template <bool V6, bool OUTB>
 __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
@@ -172,9 +164,9 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   const int hh = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform role selector
   const bool producer = wave_u < 8;
-  const long C = (long)p.H * kHead;
   const int T = p.T;
-  const long tok0 = (long)b * T;
+  const long ts = p.tok_stride;                                // elements between tokens
+  const long base = b * p.row_stride + h * p.head_stride;      // (row b, head h), token 0, channel 0
   const int nchunks = (T + L - 1) / L;
 
   int row_in = -1;
@@ -230,13 +222,13 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   }
   // Token rows are read with buffer loads: one resource per input array and
   // chunk (wave-uniform, in scalar registers) whose record count ends at the
-  // batch row's last token, so rows past it read as zero (r = k = v = 0 adds
-  // nothing); per-thread offsets are fixed.  Loaded words of chunk c live in register set c & 1 from the load
+  // head's last channel of the row's last token, so tokens past it read as
+  // zero (r = k = v = 0 adds nothing); per-thread offsets are fixed.  Loaded words of chunk c live in register set c & 1 from the load
   // (issued one step ahead) until phase 2 of chunk c, one step after phase 1.
   uint32_t roff[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) roff[t] = (uint32_t)(((4 * tg + t) * C + h * kHead + 2 * cp) * 2);
-  const unsigned long long row_end = (unsigned long long)(tok0 + T) * C * 2;  // end of this batch row
+  for (int t = 0; t < 4; ++t) roff[t] = (uint32_t)(((4 * tg + t) * ts + 2 * cp) * 2);
+  const unsigned long long row_end = (unsigned long long)(base + (long)(T - 1) * ts + kHead) * 2;  // end of this head's row
   auto rsrc_at = [&](const void *base, unsigned long long off) {
     const unsigned long long rem = off < row_end ? row_end - off : 0ull;
     const int n = (int)(rem > 0x7fffffffull ? 0x7fffffffull : rem);
@@ -247,7 +239,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   uint32_t ldx[4];       // x words: consumed in phase 1, before the next chunk's load reuses them
   auto prefetch = [&](int c, auto set_c) {
     constexpr int S = decltype(set_c)::value;
-    const unsigned long long off = (unsigned long long)uniform64((tok0 + (long)c * L) * C * 2);
+    const unsigned long long off = (unsigned long long)uniform64((base + (long)c * L * ts) * 2);
     const auto rr = rsrc_at(p.r, off), rk = rsrc_at(p.k, off), rv = rsrc_at(p.v, off);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -508,15 +500,22 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
           }
         }
         // Y^T accumulators: lane (token trow, hh) holds y[trow][32 tc + 8m + 4hh + 0..3] in
-        // Y[tc][4m .. 4m+3], four 16-byte stores per lane and column block
-        char *yb = reinterpret_cast<char *>(p.y) + uniform64(((tok0 + (long)c * L) * C + h * kHead) * 4);
-        float4 *yrow = reinterpret_cast<float4 *>(yb + (uint32_t)((trow * C + 4 * hh) * 4));
+        // Y[tc][4m .. 4m+3], four 16-byte (fp32) or 8-byte (bf16) stores per lane and column block
+        constexpr int ESZ = OUTB ? 2 : 4;
+        char *yb = reinterpret_cast<char *>(p.y) + uniform64((base + (long)c * L * ts) * ESZ);
+        char *yrow = yb + (uint32_t)((trow * ts + 4 * hh) * ESZ);
         if (nvalid == L || trow < nvalid) {
 #pragma unroll
           for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-              yrow[8 * tc + 2 * m] = make_float4(Y[tc][4 * m], Y[tc][4 * m + 1], Y[tc][4 * m + 2], Y[tc][4 * m + 3]);
+            for (int m = 0; m < 4; ++m) {
+              if constexpr (OUTB)
+                reinterpret_cast<uint2 *>(yrow)[8 * tc + 2 * m] =
+                    make_uint2(pack_bf16(Y[tc][4 * m], Y[tc][4 * m + 1]), pack_bf16(Y[tc][4 * m + 2], Y[tc][4 * m + 3]));
+              else
+                reinterpret_cast<float4 *>(yrow)[8 * tc + 2 * m] =
+                    make_float4(Y[tc][4 * m], Y[tc][4 * m + 1], Y[tc][4 * m + 2], Y[tc][4 * m + 3]);
+            }
         }
       };
       // output waves 0 and 1 own token blocks 0 and 1 with all 64 value columns, so each A^T
@@ -596,7 +595,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
   }
 }
 
-template <bool V6>
+template <bool V6, bool OUTB>
 hipError_t launch(const ScanParams &p, hipStream_t s) {
   // The dynamic-LDS limit is a per-device function attribute: set it once per device.
   static std::atomic<unsigned long long> configured{0};
@@ -606,13 +605,13 @@ hipError_t launch(const ScanParams &p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const unsigned long long bit = 1ull << (dev & 63);
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&wkv56_chunked_kernel<V6>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&wkv56_chunked_kernel<V6, OUTB>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
   dim3 grid(p.H * p.units);
-  hipLaunchKernelGGL((wkv56_chunked_kernel<V6>), grid, dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((wkv56_chunked_kernel<V6, OUTB>), grid, dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
@@ -620,7 +619,8 @@ hipError_t launch(const ScanParams &p, hipStream_t s) {
 
 hipError_t launch_wkv56_chunked(const ScanParams &p, bool v6, bool bf16, hipStream_t s) {
   if (!bf16) return hipErrorInvalidValue;  // the ABI layer routes fp32 inputs to the scan
-  return v6 ? launch<true>(p, s) : launch<false>(p, s);
+  if (p.y_bf16) return v6 ? launch<true, true>(p, s) : launch<false, true>(p, s);
+  return v6 ? launch<true, false>(p, s) : launch<false, false>(p, s);
 }
 
 }  // namespace wkv

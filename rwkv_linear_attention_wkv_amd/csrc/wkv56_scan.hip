@@ -53,7 +53,6 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;  // value column j
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // key rows kRows*wave ..
-  const long C = (long)p.H * kHead;
 
   __shared__ __align__(16) float s_r[kTB][kHead], s_k[kTB][kHead], s_d[kTB][kHead];  // direct form
   __shared__ __align__(16) float s_rh[kTB][kHead], s_kh[kTB][kHead];              // rescaled frame
@@ -65,7 +64,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   __shared__ int s_meta[3];
   __shared__ int s_frame;  // 1: the current block takes the direct form
 
-  long tok0;
+  long tok0;  // varlen: packed row of the slot's first token
   int ntok;
   int row_in = -1;
   int row_out;
@@ -102,7 +101,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
     row_in = my_row;
     row_out = my_row;
   } else {
-    tok0 = (long)unit * p.T;
+    tok0 = 0;
     ntok = p.T;
     row_out = unit;
     if (p.state_in) {
@@ -113,6 +112,10 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
       }
     }
   }
+
+  // element offset of this unit's token 0 in this head; tokens are tok_stride apart
+  const long ts = p.tok_stride;
+  const long base = VARLEN ? tok0 * ts + h * p.head_stride : unit * p.row_stride + h * p.head_stride;
 
   // ---- this lane's column of the wave's key rows, in registers
   float s[kRows];
@@ -135,7 +138,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
-      const long e = (tok0 + min(t0 + 4 * wave + t4, ntok - 1)) * C + h * kHead + lane;
+      const long e = base + min(t0 + 4 * wave + t4, ntok - 1) * ts + lane;
       pr[t4] = load1<BF16>(p.r, e);
       pk[t4] = load1<BF16>(p.k, e);
       pv[t4] = load1<BF16>(p.v, e);
@@ -256,7 +259,11 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
         const float b = s_bon[tt];
         const float4 v4 = *reinterpret_cast<const float4 *>(&s_v[tt][j]);
         o = f4(fmaf(b, v4.x, o.x), fmaf(b, v4.y, o.y), fmaf(b, v4.z, o.z), fmaf(b, v4.w, o.w));
-        *reinterpret_cast<float4 *>(p.y + (tok0 + t0 + tt) * C + h * kHead + j) = o;
+        const long ye = base + (t0 + tt) * ts + j;
+        if (p.y_bf16)
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + ye) = make_uint2(pack_bf16(o.x, o.y), pack_bf16(o.z, o.w));
+        else
+          *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + ye) = o;
       }
     }
     // The next staging writes the token arrays after this block's reads (ordered by this

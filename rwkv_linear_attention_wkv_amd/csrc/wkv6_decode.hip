@@ -99,7 +99,8 @@ __global__ void __launch_bounds__(64) wkv6_varlen_short_kernel(ScanParams p) {
       yj = fmaf(ri, s[i], yj);
       s[i] = fmaf(di, s[i], ki * vj);
     }
-    p.y[e] = yj;
+    if (p.y_bf16) static_cast<uint16_t *>(p.y)[e] = bf16_bits(yj);
+    else static_cast<float *>(p.y)[e] = yj;
   }
 
   if (p.state_out) {

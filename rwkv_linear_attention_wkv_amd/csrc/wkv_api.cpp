@@ -38,6 +38,8 @@ wkv_status launched(hipError_t e, const char *what) {
 
 constexpr int kMaxGridY = 65535;
 constexpr int kChunk = 64;
+// The chunked kernel addresses a chunk's token rows with 32-bit offsets.
+constexpr int kChunkedMaxRow = 1 << 23;
 
 #define REQUIRE(cond, ...)                                        \
   do {                                                            \
@@ -47,7 +49,7 @@ constexpr int kChunk = 64;
 // Shared validation of the dense v5 / v6 calls.
 wkv_status check_dense56(const char *fn, int B, int T, int H, int N, const void *r, const void *k,
                          const void *v, const void *w, wkv_dtype in_dtype, const float *u,
-                         const float *y, const float *state_in, const int32_t *state_map,
+                         const void *y, const float *state_in, const int32_t *state_map,
                          int n_state, const float *state_out, wkv_algo algo) {
   REQUIRE(B >= 1 && T >= 0 && H >= 1, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn, B, T, H);
   if (N != wkv::kHeadSize) return fail(WKV_ERR_UNSUPPORTED, "%s: head size N=%d is not supported (only 64)", fn, N);
@@ -56,6 +58,9 @@ wkv_status check_dense56(const char *fn, int B, int T, int H, int N, const void 
     return fail(WKV_ERR_UNSUPPORTED, "%s: unknown algorithm %d", fn, algo);
   if (algo == WKV_ALGO_CHUNKED && in_dtype != WKV_BF16)
     return fail(WKV_ERR_UNSUPPORTED, "%s: the chunked algorithm needs bf16 inputs", fn);
+  if (algo == WKV_ALGO_CHUNKED && (int64_t)H * N > kChunkedMaxRow)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: the chunked algorithm takes at most %d channels per token (H*N=%lld)",
+                fn, kChunkedMaxRow, (long long)H * N);
   REQUIRE(B <= kMaxGridY, "%s: B=%d exceeds %d", fn, B, kMaxGridY);
   REQUIRE((int64_t)H * N <= (int64_t)1 << 30, "%s: H*N too large", fn);
   if (T > 0) {
@@ -105,16 +110,18 @@ wkv_algo wkv_resolve_algo(int version, int B, int T, int H, int N, wkv_dtype in_
   (void)B; (void)H; (void)N;
   if (requested == WKV_ALGO_SCAN || requested == WKV_ALGO_CHUNKED) return requested;
   if ((version != 5 && version != 6) || in_dtype != WKV_BF16) return WKV_ALGO_SCAN;
+  if ((int64_t)H * N > kChunkedMaxRow) return WKV_ALGO_SCAN;
   // Chunks only pay off once a row holds at least one full chunk.
   return T >= kChunk ? WKV_ALGO_CHUNKED : WKV_ALGO_SCAN;
 }
 
-wkv_status wkv4_forward(int B, int T, int C, const float *time_decay, const float *time_first, const void *k,
-                        const void *v, const void *r, wkv_dtype in_dtype, float *y, const float *state_in,
-                        float *state_out, void *stream) {
+wkv_status wkv4_forward_ex(int B, int T, int C, const float *time_decay, const float *time_first, const void *k,
+                           const void *v, const void *r, wkv_dtype in_dtype, void *y, wkv_dtype out_dtype,
+                           const float *state_in, float *state_out, void *stream) {
   const char *fn = "wkv4_forward";
   REQUIRE(B >= 1 && T >= 0 && C >= 1, "%s: need B >= 1, T >= 0, C >= 1 (got B=%d T=%d C=%d)", fn, B, T, C);
   if (!dtype_ok(in_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown input dtype %d", fn, in_dtype);
+  if (!dtype_ok(out_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown output dtype %d", fn, out_dtype);
   REQUIRE(B <= kMaxGridY, "%s: B=%d exceeds %d", fn, B, kMaxGridY);
   REQUIRE(time_decay && time_first, "%s: time_decay and time_first must be non-NULL", fn);
   REQUIRE(aligned(time_decay, 4) && aligned(time_first, 4), "%s: time_decay/time_first misaligned", fn);
@@ -126,18 +133,28 @@ wkv_status wkv4_forward(int B, int T, int C, const float *time_decay, const floa
   REQUIRE(!state_in || aligned(state_in, 16), "%s: state_in must be 16-byte aligned", fn);
   REQUIRE(!state_out || aligned(state_out, 16), "%s: state_out must be 16-byte aligned", fn);
   if (T == 0 && (!state_out || state_out == state_in)) return ok();
-  wkv::V4Params p{B, T, C, time_decay, time_first, k, v, r, y, state_in, state_out};
+  wkv::V4Params p{B, T, C, time_decay, time_first, k, v, r, y, out_dtype == WKV_BF16, state_in, state_out};
   return launched(wkv::launch_wkv4(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
 }
 
+wkv_status wkv4_forward(int B, int T, int C, const float *time_decay, const float *time_first, const void *k,
+                        const void *v, const void *r, wkv_dtype in_dtype, float *y, const float *state_in,
+                        float *state_out, void *stream) {
+  return wkv4_forward_ex(B, T, C, time_decay, time_first, k, v, r, in_dtype, y, WKV_F32, state_in, state_out,
+                         stream);
+}
+
 static wkv_status dense56(int version, int B, int T, int H, int N, const void *r, const void *k, const void *v,
-                          const void *w, wkv_dtype in_dtype, const float *u, float *y, const float *state_in,
-                          const int32_t *state_map, int n_state, float *state_out, wkv_algo algo,
-                          int32_t *dev_status, void *stream) {
+                          const void *w, wkv_dtype in_dtype, wkv_layout layout, const float *u, void *y,
+                          wkv_dtype out_dtype, const float *state_in, const int32_t *state_map, int n_state,
+                          float *state_out, wkv_algo algo, int32_t *dev_status, void *stream) {
   const char *fn = version == 5 ? "wkv5_forward" : "wkv6_forward";
   wkv_status st = check_dense56(fn, B, T, H, N, r, k, v, w, in_dtype, u, y, state_in, state_map, n_state,
                                 state_out, algo);
   if (st != WKV_OK) return st;
+  if (!dtype_ok(out_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown output dtype %d", fn, out_dtype);
+  if (layout != WKV_LAYOUT_BTHN && layout != WKV_LAYOUT_BHTN)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: unknown layout %d", fn, layout);
   REQUIRE(!dev_status || aligned(dev_status, 4), "%s: dev_status must be 4-byte aligned", fn);
   if (T == 0 && !state_out) return ok();
   wkv::ScanParams p{};
@@ -147,6 +164,13 @@ static wkv_status dense56(int version, int B, int T, int H, int N, const void *r
   p.r = r; p.k = k; p.v = v; p.w = w;
   p.u = u;
   p.y = y;
+  p.y_bf16 = out_dtype == WKV_BF16;
+  const long C = (long)H * N;
+  if (layout == WKV_LAYOUT_BTHN) {
+    p.row_stride = (long)T * C; p.tok_stride = C; p.head_stride = N;
+  } else {
+    p.row_stride = (long)H * T * N; p.tok_stride = N; p.head_stride = (long)T * N;
+  }
   p.state_in = state_in;
   p.state_map = state_map;
   p.n_state = n_state;
@@ -160,19 +184,35 @@ static wkv_status dense56(int version, int B, int T, int H, int N, const void *r
   return launched(wkv::launch_wkv56_scan(p, version == 6, bf16, false, s), fn);
 }
 
+wkv_status wkv5_forward_ex(int B, int T, int H, int N, const void *r, const void *k, const void *v,
+                           wkv_dtype in_dtype, wkv_layout layout, const float *w, const float *u, void *y,
+                           wkv_dtype out_dtype, const float *state_in, const int32_t *state_map, int n_state,
+                           float *state_out, wkv_algo algo, int32_t *dev_status, void *stream) {
+  return dense56(5, B, T, H, N, r, k, v, w, in_dtype, layout, u, y, out_dtype, state_in, state_map, n_state,
+                 state_out, algo, dev_status, stream);
+}
+
 wkv_status wkv5_forward(int B, int T, int H, int N, const void *r, const void *k, const void *v, wkv_dtype in_dtype,
                         const float *w, const float *u, float *y, const float *state_in, const int32_t *state_map,
                         int n_state, float *state_out, wkv_algo algo, int32_t *dev_status, void *stream) {
-  return dense56(5, B, T, H, N, r, k, v, w, in_dtype, u, y, state_in, state_map, n_state, state_out, algo,
-                 dev_status, stream);
+  return dense56(5, B, T, H, N, r, k, v, w, in_dtype, WKV_LAYOUT_BTHN, u, y, WKV_F32, state_in, state_map,
+                 n_state, state_out, algo, dev_status, stream);
+}
+
+wkv_status wkv6_forward_ex(int B, int T, int H, int N, const void *r, const void *k, const void *v, const void *w,
+                           wkv_dtype in_dtype, wkv_layout layout, const float *u, void *y, wkv_dtype out_dtype,
+                           const float *state_in, const int32_t *state_map, int n_state, float *state_out,
+                           wkv_algo algo, int32_t *dev_status, void *stream) {
+  return dense56(6, B, T, H, N, r, k, v, w, in_dtype, layout, u, y, out_dtype, state_in, state_map, n_state,
+                 state_out, algo, dev_status, stream);
 }
 
 wkv_status wkv6_forward(int B, int T, int H, int N, const void *r, const void *k, const void *v, const void *w,
                         wkv_dtype in_dtype, const float *u, float *y, const float *state_in,
                         const int32_t *state_map, int n_state, float *state_out, wkv_algo algo,
                         int32_t *dev_status, void *stream) {
-  return dense56(6, B, T, H, N, r, k, v, w, in_dtype, u, y, state_in, state_map, n_state, state_out, algo,
-                 dev_status, stream);
+  return dense56(6, B, T, H, N, r, k, v, w, in_dtype, WKV_LAYOUT_BTHN, u, y, WKV_F32, state_in, state_map,
+                 n_state, state_out, algo, dev_status, stream);
 }
 
 wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *k, const void *v, const void *w,
@@ -208,15 +248,17 @@ wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *
   return launched(wkv::launch_wkv6_backward(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
 }
 
-wkv_status wkv6_forward_varlen(int num_slots, int H, int N, const int32_t *lengths, int max_len, int total_tokens,
-                               const void *r, const void *k, const void *v, const void *w, wkv_dtype in_dtype,
-                               const float *u, float *y, const float *state_in, float *state_out,
-                               const int32_t *state_map, int n_state, int32_t *dev_status, void *stream) {
+wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N, const int32_t *lengths, int max_len,
+                                  int total_tokens, const void *r, const void *k, const void *v, const void *w,
+                                  wkv_dtype in_dtype, const float *u, void *y, wkv_dtype out_dtype,
+                                  const float *state_in, float *state_out, const int32_t *state_map, int n_state,
+                                  int32_t *dev_status, void *stream) {
   const char *fn = "wkv6_forward_varlen";
   REQUIRE(num_slots >= 0 && H >= 1 && max_len >= 0 && total_tokens >= 0,
           "%s: need num_slots >= 0, H >= 1, max_len >= 0, total_tokens >= 0", fn);
   if (N != wkv::kHeadSize) return fail(WKV_ERR_UNSUPPORTED, "%s: head size N=%d is not supported (only 64)", fn, N);
   if (!dtype_ok(in_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown input dtype %d", fn, in_dtype);
+  if (!dtype_ok(out_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown output dtype %d", fn, out_dtype);
   REQUIRE(num_slots <= kMaxGridY, "%s: num_slots=%d exceeds %d", fn, num_slots, kMaxGridY);
   if (num_slots == 0) return ok();
   REQUIRE(lengths && aligned(lengths, 4), "%s: lengths must be a non-NULL, 4-byte aligned device array", fn);
@@ -241,6 +283,8 @@ wkv_status wkv6_forward_varlen(int num_slots, int H, int N, const int32_t *lengt
   p.r = r; p.k = k; p.v = v; p.w = w;
   p.u = u;
   p.y = y;
+  p.y_bf16 = out_dtype == WKV_BF16;
+  p.row_stride = 0; p.tok_stride = (long)H * N; p.head_stride = N;  // packed [total_tokens, H*N]
   p.state_in = state_in;
   p.state_map = state_map;
   p.n_state = n_state;
@@ -253,6 +297,14 @@ wkv_status wkv6_forward_varlen(int num_slots, int H, int N, const int32_t *lengt
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (max_len <= wkv::kShortMax) return launched(wkv::launch_wkv6_varlen_short(p, bf16, s), fn);
   return launched(wkv::launch_wkv56_scan(p, true, bf16, true, s), fn);
+}
+
+wkv_status wkv6_forward_varlen(int num_slots, int H, int N, const int32_t *lengths, int max_len, int total_tokens,
+                               const void *r, const void *k, const void *v, const void *w, wkv_dtype in_dtype,
+                               const float *u, float *y, const float *state_in, float *state_out,
+                               const int32_t *state_map, int n_state, int32_t *dev_status, void *stream) {
+  return wkv6_forward_varlen_ex(num_slots, H, N, lengths, max_len, total_tokens, r, k, v, w, in_dtype, u, y,
+                                WKV_F32, state_in, state_out, state_map, n_state, dev_status, stream);
 }
 
 wkv_status wkv_schedule_round_robin(int num_slots, const int32_t *remaining, int budget, int32_t *take,

@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(nat.SIGNATURES)
@@ -176,6 +176,49 @@ def test_resolve_algo(lib):
     assert lib.wkv_resolve_algo(6, 8, 1, 32, 64, bf, A) == S           # decode stays on the scan
     assert lib.wkv_resolve_algo(6, 8, 4096, 32, 64, f32, A) == S       # fp32 inputs: scan
     assert lib.wkv_resolve_algo(4, 8, 4096, 32, 64, bf, A) == S
+
+
+def v6x(lib, B=2, T=8, H=2, N=64, dt=1, lay=0, y=P, odt=0, algo=0):
+    return lib.wkv6_forward_ex(B, T, H, N, P, P, P, P, dt, lay, P, y, odt, None, None, 0, None, algo, None, None)
+
+
+def v5x(lib, B=2, T=8, H=2, N=64, dt=1, lay=0, y=P, odt=0, algo=0):
+    return lib.wkv5_forward_ex(B, T, H, N, P, P, P, dt, lay, P, P, y, odt, None, None, 0, None, algo, None, None)
+
+
+@pytest.mark.parametrize("fn", [v5x, v6x])
+def test_ex_validation(lib, fn):
+    """Layout and output-dtype checks of the _ex entry points (host only)."""
+    E, U = nat.WKV_ERR_INVALID_ARG, nat.WKV_ERR_UNSUPPORTED
+    assert fn(lib, lay=2) == U and b"layout" in lib.wkv_last_error()
+    assert fn(lib, lay=-1) == U
+    assert fn(lib, odt=5) == U and b"output dtype" in lib.wkv_last_error()
+    assert fn(lib, N=32) == U
+    assert fn(lib, y=None) == E
+    assert fn(lib, y=MIS) == E
+    assert fn(lib, B=0) == E
+    # more channels per token than the chunked kernel's 32-bit row offsets take
+    assert fn(lib, H=(1 << 23) // 64 + 1, algo=nat.WKV_ALGO_CHUNKED) == U
+    for lay in (nat.WKV_LAYOUT_BTHN, nat.WKV_LAYOUT_BHTN):
+        for odt in (nat.WKV_F32, nat.WKV_BF16):
+            assert fn(lib, T=0, lay=lay, odt=odt) == nat.WKV_OK
+
+
+def test_ex_v4_and_varlen_validation(lib):
+    U = nat.WKV_ERR_UNSUPPORTED
+    assert lib.wkv4_forward_ex(2, 8, 64, P, P, P, P, None, 0, P, 7, None, None, None) == U
+    assert b"output dtype" in lib.wkv_last_error()
+    assert lib.wkv4_forward_ex(2, 0, 64, P, P, None, None, None, 0, None, 1, None, None, None) == nat.WKV_OK
+    assert lib.wkv6_forward_varlen_ex(4, 2, 64, P, 16, 32, P, P, P, P, 1, P, P, 9, P, P, None, 4, None,
+                                      None) == U
+    assert lib.wkv6_forward_varlen_ex(0, 2, 64, None, 16, 32, P, P, P, P, 1, P, P, 1, None, None, None, 4, None,
+                                      None) == nat.WKV_OK
+
+
+def test_resolve_algo_wide_rows(lib):
+    bf = nat.WKV_BF16
+    assert lib.wkv_resolve_algo(6, 1, 4096, (1 << 23) // 64, 64, bf, nat.WKV_ALGO_AUTO) == nat.WKV_ALGO_CHUNKED
+    assert lib.wkv_resolve_algo(6, 1, 4096, (1 << 23) // 64 + 1, 64, bf, nat.WKV_ALGO_AUTO) == nat.WKV_ALGO_SCAN
 
 
 def test_chunked_needs_bf16(lib):
