@@ -46,6 +46,18 @@ static_assert(4 * kWaves == kTB && 16 * kTB == kThreads, "staging: four tokens p
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFrameLog2 = 80.f;  // largest log2 decay of one block the rescaled frame takes
 
+struct __align__(16) ScanSmem {
+  float rk[2][kTB][kHead];       // rescaled frame operands: [0] = rh, [1] = kh
+  float v[kTB][kHead];
+  float y[kWaves][kTB][kHead];   // per-wave partial outputs
+  float r[kTB][kHead], k[kTB][kHead], d[kTB][kHead];  // direct form
+  float dend[kHead];             // decay product of the block per key row
+  float tot[kWaves][kHead];      // log2 decay of each staging wave's tokens
+  float bon[kTB];                // r . (u * k) per token
+  int meta[3];
+  int frame;                     // 1: the current block takes the direct form
+};
+
 template <bool V6, bool BF16, bool VARLEN>
 __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   const int h = blockIdx.x;
@@ -54,15 +66,18 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   const int lane = tid & 63;  // value column j
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // key rows kRows*wave ..
 
-  __shared__ __align__(16) float s_r[kTB][kHead], s_k[kTB][kHead], s_d[kTB][kHead];  // direct form
-  __shared__ __align__(16) float s_rh[kTB][kHead], s_kh[kTB][kHead];              // rescaled frame
-  __shared__ __align__(16) float s_v[kTB][kHead];
-  __shared__ __align__(16) float s_dend[kHead];   // decay product of the block per key row
-  __shared__ float s_tot[kWaves][kHead];          // log2 decay of each staging wave's tokens
-  __shared__ float s_bon[kTB];                    // r . (u * k) per token
-  __shared__ __align__(16) float s_y[kTB][kWaves][kHead];  // per-wave partial outputs
-  __shared__ int s_meta[3];
-  __shared__ int s_frame;  // 1: the current block takes the direct form
+  // One LDS object, the arrays of the token loop first: their offsets stay below 64 KiB, so the
+  // loop's reads and writes are a per-thread base register plus an instruction offset.
+  __shared__ ScanSmem sm;
+  auto &s_rk = sm.rk;
+  auto &s_v = sm.v;
+  auto &s_y = sm.y;
+  auto &s_r = sm.r, &s_k = sm.k, &s_d = sm.d;
+  auto &s_dend = sm.dend;
+  auto &s_tot = sm.tot;
+  auto &s_bon = sm.bon;
+  auto &s_meta = sm.meta;
+  auto &s_frame = sm.frame;
 
   long tok0;  // varlen: packed row of the slot's first token
   int ntok;
@@ -190,8 +205,8 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
       for (int t4 = 0; t4 < 4; ++t4) {
         const int tt = 4 * wave + t4;
         const float lprev = pre + (t4 ? cum[t4 - 1] : 0.f), lcur = pre + cum[t4];
-        s_rh[tt][lane] = rr[t4] * __builtin_amdgcn_exp2f(lprev);
-        s_kh[tt][lane] = kk[t4] * __builtin_amdgcn_exp2f(-lcur);
+        s_rk[0][tt][lane] = rr[t4] * __builtin_amdgcn_exp2f(lprev);
+        s_rk[1][tt][lane] = kk[t4] * __builtin_amdgcn_exp2f(-lcur);
       }
       if (wave == kWaves - 1) {
         const float lend = pre + cum[3];
@@ -204,13 +219,19 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
     if (s_frame == 0) {
       // Rescaled frame: the registers hold St = S / D (D = decay product from the block
       // start), so per token y += rh . St and St += kh v: two FMAs per state element.
+      // Per-thread LDS pointers, formed once in vector registers: every read and write of the
+      // loop is then one of them plus a constant offset (no per-token address arithmetic).
+      int w2 = 2 * wave;  // the wave's rows in float4 units
+      asm volatile("" : "+v"(w2));
+      const float4 *rk4 = reinterpret_cast<const float4 *>(&s_rk[0][0][0]) + w2;
+      const float *vp = &s_v[0][lane];
+      float *yp = &s_y[wave][0][lane];
+      constexpr int kRow4 = kHead / 4, kKh4 = kTB * kHead / 4;  // float4 strides: token, rh -> kh
 #pragma unroll 4
       for (int tt = 0; tt < nb; ++tt) {
-        const float vj = s_v[tt][lane];
-        const float4 r0 = *reinterpret_cast<const float4 *>(&s_rh[tt][kRows * wave]);
-        const float4 r1 = *reinterpret_cast<const float4 *>(&s_rh[tt][kRows * wave + 4]);
-        const float4 k0 = *reinterpret_cast<const float4 *>(&s_kh[tt][kRows * wave]);
-        const float4 k1 = *reinterpret_cast<const float4 *>(&s_kh[tt][kRows * wave + 4]);
+        const float vj = vp[tt * kHead];
+        const float4 r0 = rk4[tt * kRow4], r1 = rk4[tt * kRow4 + 1];
+        const float4 k0 = rk4[kKh4 + tt * kRow4], k1 = rk4[kKh4 + tt * kRow4 + 1];
         float y0 = r0.x * s[0];
         s[0] = fmaf(k0.x, vj, s[0]);
         float y1 = r0.y * s[1];
@@ -221,7 +242,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
         y1 = fmaf(r1.y, s[5], y1); s[5] = fmaf(k1.y, vj, s[5]);
         y0 = fmaf(r1.z, s[6], y0); s[6] = fmaf(k1.z, vj, s[6]);
         y1 = fmaf(r1.w, s[7], y1); s[7] = fmaf(k1.w, vj, s[7]);
-        s_y[tt][wave][lane] = y0 + y1;
+        yp[tt * kHead] = y0 + y1;
       }
       // back to S at the block end
       const float4 d0 = *reinterpret_cast<const float4 *>(&s_dend[kRows * wave]);
@@ -243,7 +264,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
           y0 = fmaf(r4.z, s[4 * g + 2], y0); s[4 * g + 2] = fmaf(d4.z, s[4 * g + 2], k4.z * vj);
           y1 = fmaf(r4.w, s[4 * g + 3], y1); s[4 * g + 3] = fmaf(d4.w, s[4 * g + 3], k4.w * vj);
         }
-        s_y[tt][wave][lane] = y0 + y1;
+        s_y[wave][tt][lane] = y0 + y1;
       }
     }
     __syncthreads();
@@ -253,7 +274,7 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float4 a = *reinterpret_cast<const float4 *>(&s_y[tt][w][j]);
+          const float4 a = *reinterpret_cast<const float4 *>(&s_y[w][tt][j]);
           o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
         }
         const float b = s_bon[tt];

@@ -18,8 +18,9 @@
 // (every pair (s, tau) whose decay path crosses token t, counted once).
 //
 // Each sweep is one state recurrence of the same shape: a 64 x 64 fp32 state
-// X in registers (wave w owns rows 8w..8w+7, lane c column c), tokens walked
-// in order (or in reverse), per token
+// X in registers (wave w owns rows 8w..8w+7; lanes 2m and 2m+1 hold the two
+// halves of those rows for columns 2m and 2m+1), tokens walked in order (or in
+// reverse), per token
 //   out[c] = sum_row P[row] X[row][c],   then   X[row][c] <- a X[row][c] + Q[row] R[c]
 // with the decay a on the rows or on the columns:
 //   TFWD (time forward, X = S^T, rows j, columns i, column decay):
@@ -30,12 +31,19 @@
 //       P = v, Q = dy, R = r, a = d[i]  -> dk, and dx from dr (TFWD's output)
 // Tokens are staged through LDS as fp32 in blocks (wave w stages a run of
 // consecutive tokens of the block, lane = channel), per-wave partial outputs
-// are summed through LDS in a fixed order (deterministic), and the
-// per-channel sums over time (du, the dlam running sums) are walked by wave
-// 0, one token after the other.  TFWD and BWD do not depend on each other:
-// they run as one launch (blockIdx.z picks the sweep) with 16-token blocks, so
-// that two workgroups (64 KiB of LDS each) share a CU and each SIMD holds four
-// waves; TBWD reads TFWD's dr and runs after it with 32-token blocks.
+// are summed through LDS in a fixed order (deterministic).  Of the
+// per-channel sums over time, du is walked by wave 0 one token after the
+// other, and the dlam running sums are a prefix over the block (in-wave sums
+// plus the earlier waves' totals) on a compensated carry.  Inside a block
+// the state is carried in a frame rescaled by the block's running decay
+// product, which makes each step two FMAs per state element instead of three
+// (blocks whose decay product underflows the frame take the direct form).
+// The row factors reach every lane as LDS broadcast reads, whose bytes bound
+// a step: the 4 x 2 tile per lane needs 8 of them per step for 8 elements.
+// TFWD and BWD do not depend on each other: they run as one launch
+// (blockIdx.z picks the sweep) with 16-token blocks, so that two workgroups
+// (70 KiB of LDS each) share a CU and each SIMD holds four waves; TBWD reads
+// TFWD's dr and runs after it with 32-token blocks.
 #include <type_traits>
 
 #include "common.hpp"
@@ -48,17 +56,27 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = kHead / kWaves;  // state rows per wave
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFrameLog2 = 80.f;  // largest log2 decay of one block the rescaled frame takes
 
 enum Sweep { TFWD = 0, BWD = 1, TBWD = 2 };
 
+// The value of lane l ^ 1 (quad permute on DPP).
+__device__ __forceinline__ float xor_lane1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
 template <int KTB>
 struct Smem {
-  float p[KTB][kHead], q[KTB][kHead];  // row factors
-  float al[KTB][kHead];                // decay d per (token, channel)
+  float p[KTB][kHead], q[KTB][kHead];  // row factors (rescaled in the frame, row decay)
+  float al[KTB][kHead];                // direct form: decay d; frame, column decay: output factor
   float r[KTB][kHead];                 // column factor R
+  float rt[KTB][kHead];                // frame, column decay: R rescaled
   float e0[KTB][kHead], e1[KTB][kHead], e2[KTB][kHead];  // per-sweep extras
   float w[KTB][kHead];                 // per (token, channel) terms of the time sums
   float y[KTB][kWaves][kHead];         // per-wave partial outputs
+  float tot[kWaves][kHead];            // log2 decay of each staging wave's tokens
+  float dend[kHead];                   // decay product of the block per channel
   float bon[KTB];
 };
 
@@ -69,7 +87,7 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
   constexpr int TPW = KTB / kWaves;       // tokens each wave stages per block
   constexpr int CPT = kHead * KTB / kThreads;  // channels per thread in the reduction
   static_assert(TPW * kWaves == KTB && CPT * kThreads == kHead * KTB && (CPT == 2 || CPT == 4), "block shape");
-  auto &s_p = sm.p; auto &s_q = sm.q; auto &s_al = sm.al; auto &s_r = sm.r;
+  auto &s_p = sm.p; auto &s_q = sm.q; auto &s_al = sm.al; auto &s_r = sm.r; auto &s_rt = sm.rt;
   auto &s_e0 = sm.e0; auto &s_e1 = sm.e1; auto &s_e2 = sm.e2; auto &s_w = sm.w; auto &s_y = sm.y;
   auto &s_bon = sm.bon;
   const int tid = threadIdx.x;
@@ -80,9 +98,15 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
   const long row0 = (long)b * T;  // first token row of this batch row
 
   // ---- initial state
-  float X[kRows];
+  // The state tile of this thread: rows xr0 .. xr0+3 and columns xc0, xc0+1 (lanes 2m and 2m+1
+  // hold the two row halves of wave w's eight rows for the same two columns), so that per step
+  // a lane reads four row factors of each kind and two column factors.
+  const int half = lane & 1;
+  const int xr0 = kRows * wave + 4 * half;
+  const int xc0 = 2 * (lane >> 1);
+  float X[4][2];
 #pragma unroll
-  for (int a = 0; a < kRows; ++a) X[a] = 0.f;
+  for (int a = 0; a < 4; ++a) X[a][0] = X[a][1] = 0.f;
   const long head_off = (long)h * kHead * kHead;
   if (MODE == TFWD) {
     if (p.state_in) {
@@ -93,18 +117,22 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
       }
       const float *s0 = p.state_in + (long)row_in * p.H * kHead * kHead + head_off;
 #pragma unroll
-      for (int a = 0; a < kRows; ++a) X[a] = s0[lane * kHead + kRows * wave + a];  // X[j][i] = S0[i][j]
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) X[a][c] = s0[(xc0 + c) * kHead + xr0 + a];  // X[j][i] = S0[i][j]
     }
   } else if (p.d_state_out) {
     const float *g = p.d_state_out + (long)b * p.H * kHead * kHead + head_off;
 #pragma unroll
-    for (int a = 0; a < kRows; ++a)
-      X[a] = COLDECAY ? g[lane * kHead + kRows * wave + a] : g[(kRows * wave + a) * kHead + lane];
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        X[a][c] = COLDECAY ? g[(xc0 + c) * kHead + xr0 + a] : g[(xr0 + a) * kHead + xc0 + c];
   }
-  // TBWD: the decay gradient of channel `lane` as one running difference (walked by wave 0).
-  // The two sums over the sequence grow with its length while their difference does not, so
-  // the difference itself is carried, with a compensation term (Kahan): rounding stays
-  // relative to the difference and the per-token terms, not to the sums.
+  // TBWD: the decay gradient of channel `lane` as one running difference (every wave holds the
+  // same copy).  The two sums over the sequence grow with its length while their difference
+  // does not, so the difference itself is carried, with a compensation term (Kahan) across
+  // blocks: rounding stays relative to the difference and the per-block terms, not to the sums.
   float dsum = 0.f, dcomp = 0.f, dusum = 0.f;
   auto dadd = [&](float x) {
     const float yk = x - dcomp;
@@ -112,7 +140,7 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
     dcomp = (t - dsum) - yk;
     dsum = t;
   };
-  if (MODE == TBWD && wave == 0 && p.d_state_out && p.state_final) {
+  if (MODE == TBWD && p.d_state_out && p.state_final) {
     const float *g = p.d_state_out + (long)b * p.H * kHead * kHead + head_off + lane * kHead;
     const float *sf = p.state_final + (long)b * p.H * kHead * kHead + head_off + lane * kHead;
     for (int j = 0; j < kHead; ++j) dadd(g[j] * sf[j]);
@@ -138,27 +166,33 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
   if (T > 0) fetch(0);
   for (int q0 = 0; q0 < T; q0 += KTB) {
     const int nb = min(KTB, T - q0);
-    // ---- stage this block (token of step q0 + tt at row tt)
-    float bon[TPW];
+    // ---- stage this block (token of step q0 + tt at row tt).  Part 1: the factors that do
+    // not depend on the frame, the bonus scalars, and the log2 decays (lam2 = log2 d) with
+    // this thread's running sums in processing order (exclusive cex, inclusive cin).
+    float bon[TPW], lam2[TPW], cex[TPW], cin[TPW], fp[TPW], fq[TPW];
+    float run = 0.f;
 #pragma unroll
     for (int t4 = 0; t4 < TPW; ++t4) {
       const int tt = TPW * wave + t4;
       const float ex = fast_exp(px[t4]);
-      s_al[tt][lane] = fast_exp(-ex);
+      lam2[t4] = -ex * kLog2e;
+      cex[t4] = run;
+      run += lam2[t4];
+      cin[t4] = run;
       if (MODE == TFWD) {
-        s_p[tt][lane] = pdy[t4];
-        s_q[tt][lane] = pv[t4];
+        fp[t4] = pdy[t4];
+        fq[t4] = pv[t4];
         s_r[tt][lane] = pk[t4];
         s_e0[tt][lane] = pr[t4];
         bon[t4] = pdy[t4] * pv[t4];
       } else if (MODE == BWD) {
-        s_p[tt][lane] = pk[t4];
-        s_q[tt][lane] = pr[t4];
+        fp[t4] = pk[t4];
+        fq[t4] = pr[t4];
         s_r[tt][lane] = pdy[t4];
         bon[t4] = pk[t4] * uc * pr[t4];
       } else {
-        s_p[tt][lane] = pv[t4];
-        s_q[tt][lane] = pdy[t4];
+        fp[t4] = pv[t4];
+        fq[t4] = pdy[t4];
         s_r[tt][lane] = pr[t4];
         s_e0[tt][lane] = pk[t4];
         s_e1[tt][lane] = pdr[t4];
@@ -166,7 +200,7 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
         bon[t4] = pv[t4] * pdy[t4];
       }
     }
-    fetch(q0 + KTB);  // in flight during this block
+    sm.tot[wave][lane] = run;
 #pragma unroll
     for (int t4 = 0; t4 < TPW; ++t4) {  // bonus scalar: sum over the 64 channels of the token
       float x = bon[t4];
@@ -179,35 +213,117 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
       for (int t4 = 0; t4 < TPW; ++t4) s_bon[TPW * wave + t4] = bon[t4];
     }
     __syncthreads();
-
-    // ---- the recurrence over the block's tokens
-    for (int tt = 0; tt < nb; ++tt) {
-      const float rc = s_r[tt][lane];
-      float y0 = 0.f, y1 = 0.f;
-      if (COLDECAY) {
-        const float ac = s_al[tt][lane];
+    // Part 2.  With D_t the decay product from the block start through step t (per channel,
+    // processing order), the registers carry X / D in the rescaled frame, so each step is two
+    // FMAs per state element: out += P' X', X' += Q' R', and X = D_last X' at the block end.
+    //   row decay (BWD):     P' = P D_{t-1},  Q' = Q / D_t,  R' = R
+    //   column decay:        P' = P,  Q' = Q,  R' = R / D_t, and out is scaled by D_{t-1}
+    // A block whose decay product falls below 2^-kFrameLog2 in some channel takes the direct
+    // form X <- d X + Q R (the same decision in every wave: each sums all waves' totals).
+    float before = 0.f, total = 0.f;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const float4 p4 = *reinterpret_cast<const float4 *>(&s_p[tt][kRows * wave + 4 * g]);
-          const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[tt][kRows * wave + 4 * g]);
-          y0 = fmaf(p4.x, X[4 * g], y0); X[4 * g] = fmaf(ac, X[4 * g], q4.x * rc);
-          y1 = fmaf(p4.y, X[4 * g + 1], y1); X[4 * g + 1] = fmaf(ac, X[4 * g + 1], q4.y * rc);
-          y0 = fmaf(p4.z, X[4 * g + 2], y0); X[4 * g + 2] = fmaf(ac, X[4 * g + 2], q4.z * rc);
-          y1 = fmaf(p4.w, X[4 * g + 3], y1); X[4 * g + 3] = fmaf(ac, X[4 * g + 3], q4.w * rc);
-        }
+    for (int w = 0; w < kWaves; ++w) {
+      const float t = sm.tot[w][lane];
+      before += w < wave ? t : 0.f;
+      total += t;
+    }
+    const bool direct = __any(!(total >= -kFrameLog2));
+#pragma unroll
+    for (int t4 = 0; t4 < TPW; ++t4) {
+      const int tt = TPW * wave + t4;
+      const float ce = before + cex[t4], ci = before + cin[t4];
+      if (direct) {
+        s_p[tt][lane] = fp[t4];
+        s_q[tt][lane] = fq[t4];
+        s_al[tt][lane] = __builtin_amdgcn_exp2f(lam2[t4]);
+      } else if (!COLDECAY) {
+        s_p[tt][lane] = fp[t4] * __builtin_amdgcn_exp2f(ce);
+        s_q[tt][lane] = fq[t4] * __builtin_amdgcn_exp2f(-ci);
       } else {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const float4 p4 = *reinterpret_cast<const float4 *>(&s_p[tt][kRows * wave + 4 * g]);
-          const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[tt][kRows * wave + 4 * g]);
-          const float4 a4 = *reinterpret_cast<const float4 *>(&s_al[tt][kRows * wave + 4 * g]);
-          y0 = fmaf(p4.x, X[4 * g], y0); X[4 * g] = fmaf(a4.x, X[4 * g], q4.x * rc);
-          y1 = fmaf(p4.y, X[4 * g + 1], y1); X[4 * g + 1] = fmaf(a4.y, X[4 * g + 1], q4.y * rc);
-          y0 = fmaf(p4.z, X[4 * g + 2], y0); X[4 * g + 2] = fmaf(a4.z, X[4 * g + 2], q4.z * rc);
-          y1 = fmaf(p4.w, X[4 * g + 3], y1); X[4 * g + 3] = fmaf(a4.w, X[4 * g + 3], q4.w * rc);
-        }
+        s_p[tt][lane] = fp[t4];
+        s_q[tt][lane] = fq[t4];
+        s_rt[tt][lane] = s_r[tt][lane] * __builtin_amdgcn_exp2f(-ci);
+        s_al[tt][lane] = __builtin_amdgcn_exp2f(ce);
       }
-      s_y[tt][wave][lane] = y0 + y1;
+      if (tt == nb - 1) sm.dend[lane] = __builtin_amdgcn_exp2f(ci);
+    }
+    fetch(q0 + KTB);  // in flight during this block
+    __syncthreads();
+
+    // ---- the recurrence over the block's tokens.  ya, yb: this lane's partial outputs of
+    // columns xc0 and xc0 + 1 over its four rows; the two row halves are added across the lane
+    // pair, and lane 2m + half stores column xc0 + half of the wave's partial.
+    auto store_out = [&](int tt, float ya, float yb) {
+      const float send = half ? ya : yb;
+      const float mine = half ? yb : ya;
+      s_y[tt][wave][xc0 + half] = mine + xor_lane1(send);
+    };
+    if (!direct) {
+      auto frame_step = [&](int tt) {
+        const float2 rc = *reinterpret_cast<const float2 *>(COLDECAY ? &s_rt[tt][xc0] : &s_r[tt][xc0]);
+        const float4 p4 = *reinterpret_cast<const float4 *>(&s_p[tt][xr0]);
+        const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[tt][xr0]);
+        const float pp[4] = {p4.x, p4.y, p4.z, p4.w}, qq[4] = {q4.x, q4.y, q4.z, q4.w};
+        float ya = pp[0] * X[0][0], yb = pp[0] * X[0][1];
+        X[0][0] = fmaf(qq[0], rc.x, X[0][0]);
+        X[0][1] = fmaf(qq[0], rc.y, X[0][1]);
+#pragma unroll
+        for (int a = 1; a < 4; ++a) {
+          ya = fmaf(pp[a], X[a][0], ya);
+          yb = fmaf(pp[a], X[a][1], yb);
+          X[a][0] = fmaf(qq[a], rc.x, X[a][0]);
+          X[a][1] = fmaf(qq[a], rc.y, X[a][1]);
+        }
+        store_out(tt, ya, yb);
+      };
+      // four steps per iteration, so that the LDS offsets of the steps are constants
+      int tt = 0;
+      for (; tt + 4 <= nb; tt += 4) {
+        frame_step(tt);
+        frame_step(tt + 1);
+        frame_step(tt + 2);
+        frame_step(tt + 3);
+      }
+      for (; tt < nb; ++tt) frame_step(tt);
+      if (COLDECAY) {
+        const float2 dd = *reinterpret_cast<const float2 *>(&sm.dend[xc0]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) { X[a][0] *= dd.x; X[a][1] *= dd.y; }
+      } else {
+        const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dend[xr0]);
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) { X[a][0] *= dd[a]; X[a][1] *= dd[a]; }
+      }
+    } else {
+      for (int tt = 0; tt < nb; ++tt) {
+        const float2 rc = *reinterpret_cast<const float2 *>(&s_r[tt][xc0]);
+        const float4 p4 = *reinterpret_cast<const float4 *>(&s_p[tt][xr0]);
+        const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[tt][xr0]);
+        const float pp[4] = {p4.x, p4.y, p4.z, p4.w}, qq[4] = {q4.x, q4.y, q4.z, q4.w};
+        float ya = 0.f, yb = 0.f;
+        if (COLDECAY) {
+          const float2 ac = *reinterpret_cast<const float2 *>(&s_al[tt][xc0]);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            ya = fmaf(pp[a], X[a][0], ya);
+            yb = fmaf(pp[a], X[a][1], yb);
+            X[a][0] = fmaf(ac.x, X[a][0], qq[a] * rc.x);
+            X[a][1] = fmaf(ac.y, X[a][1], qq[a] * rc.y);
+          }
+        } else {
+          const float4 a4 = *reinterpret_cast<const float4 *>(&s_al[tt][xr0]);
+          const float aa[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            ya = fmaf(pp[a], X[a][0], ya);
+            yb = fmaf(pp[a], X[a][1], yb);
+            X[a][0] = fmaf(aa[a], X[a][0], qq[a] * rc.x);
+            X[a][1] = fmaf(aa[a], X[a][1], qq[a] * rc.y);
+          }
+        }
+        store_out(tt, ya, yb);
+      }
     }
     __syncthreads();
 
@@ -222,6 +338,10 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
         for (int w = 0; w < kWaves; ++w)
 #pragma unroll
           for (int m = 0; m < CPT; ++m) o[m] += s_y[tt][w][c + m];
+        if (COLDECAY && !direct) {  // the frame's output factor D_{t-1} of column c + m
+#pragma unroll
+          for (int m = 0; m < CPT; ++m) o[m] *= s_al[tt][c + m];
+        }
         const float bt = s_bon[tt];
         float res[CPT], wt[CPT];
 #pragma unroll
@@ -252,17 +372,38 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
       }
     }
     __syncthreads();
-    // ---- sums over time, one channel per lane of wave 0, in processing order
-    if (MODE != BWD && wave == 0) {
-      if (MODE == TFWD) {
-        for (int tt = 0; tt < nb; ++tt) dusum += s_w[tt][lane];
-      } else {
-        for (int tt = 0; tt < nb; ++tt) {
-          dadd(-s_w[tt][lane]);  // - k_t dk~_t: counted from this step on
-          p.dw[tok(q0 + tt) * C + h * kHead + lane] = s_e2[tt][lane] * dsum;
-          dadd(s_e1[tt][lane]);  // + r_t dr~_t: counted for the steps before t
-        }
+    // ---- sums over time, one channel per lane, in processing order
+    if (MODE == TFWD && wave == 0) {
+      for (int tt = 0; tt < nb; ++tt) dusum += s_w[tt][lane];
+    }
+    if (MODE == TBWD) {
+      // dlam at step t = carry + sum over the block's earlier steps m of (r_m dr~_m - k_m dk~_m)
+      // - k_t dk~_t.  Every wave takes TPW consecutive steps: in-wave running sums, the totals of
+      // the earlier waves through LDS, and the block total added to the carry (each wave keeps
+      // the same carry: it adds the same totals in the same order).
+      float ex[TPW], run2 = 0.f;
+#pragma unroll
+      for (int t4 = 0; t4 < TPW; ++t4) {
+        const int tt = TPW * wave + t4;
+        ex[t4] = run2;
+        run2 += tt < nb ? s_e1[tt][lane] - s_w[tt][lane] : 0.f;
       }
+      sm.tot[wave][lane] = run2;
+      __syncthreads();
+      float before = 0.f, total = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float t = sm.tot[w][lane];
+        before += w < wave ? t : 0.f;
+        total += t;
+      }
+      const float carry = dsum + before;
+#pragma unroll
+      for (int t4 = 0; t4 < TPW; ++t4) {
+        const int tt = TPW * wave + t4;
+        if (tt < nb) p.dw[tok(q0 + tt) * C + h * kHead + lane] = s_e2[tt][lane] * ((carry + ex[t4]) - s_w[tt][lane]);
+      }
+      dadd(total);
     }
     // The next staging writes the token arrays after this block's reads (ordered by this
     // barrier); s_y is written again only after the next staging barrier.
@@ -273,7 +414,10 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
   if (MODE == BWD && p.d_state_in) {
     float *g = p.d_state_in + (long)b * p.H * kHead * kHead + head_off;
 #pragma unroll
-    for (int a = 0; a < kRows; ++a) g[(kRows * wave + a) * kHead + lane] = X[a];
+    for (int a = 0; a < 4; ++a) {  // d_state_in is only 4-byte aligned: two 4-byte stores
+      g[(xr0 + a) * kHead + xc0] = X[a][0];
+      g[(xr0 + a) * kHead + xc0 + 1] = X[a][1];
+    }
   }
 }
 

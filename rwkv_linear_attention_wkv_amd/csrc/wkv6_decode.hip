@@ -1,5 +1,5 @@
 // Few-token WKV v6 varlen calls: T = 1 decode steps, or a token budget spread
-// over many slots.  Same recurrence as the token-sequential scan:
+// over many slots.  The recurrence (the token-sequential scan's):
 //   y_t[j] = sum_i r_t[i] (S[i][j] + u[i] k_t[i] v_t[j])
 //   S[i][j] <- d_t[i] S[i][j] + k_t[i] v_t[j],   d_t[i] = exp(-exp(w_t[i]))
 // (the rwkv_ops page's RWKV6_OP call with state_map; the standard RWKV-6
@@ -10,8 +10,8 @@
 // state (S[0..63][j]), so every state load and store is a fully coalesced
 // 256-byte row, the output y_t[j] = sum_i r_t[i] S[i][j] +
 // (r_t . (u * k_t)) v_t[j] is a sum inside the lane, and the row factors
-// r_t[i], k_t[i], d_t[i] reach all lanes as scalar operands (v_readlane).  No
-// workgroup barrier: the state is requested as soon as the slot's row is known
+// r_t[i], k_t[i], d_t[i] reach all lanes through LDS, four at a time as
+// broadcast reads.  The state is requested as soon as the slot's row is known
 // (clamped; an invalid row is rejected before anything is written), and the
 // slot offset is a wave reduction.
 #include "common.hpp"
@@ -77,6 +77,8 @@ __global__ void __launch_bounds__(64) wkv6_varlen_short_kernel(ScanParams p) {
   }
   const int ntok = my_len;
   const float ui = p.u[h * kHead + lane];
+  // the token's row factors r[i], k[i], d[i], read back by every lane as 16-byte broadcasts
+  __shared__ __align__(16) float s_r[kHead], s_k[kHead], s_d[kHead];
 
   // token rows one token ahead
   const long e0 = (long)off * C + h * kHead + lane;
@@ -91,14 +93,25 @@ __global__ void __launch_bounds__(64) wkv6_varlen_short_kernel(ScanParams p) {
       nr = load1<BF16>(p.r, e + C); nk = load1<BF16>(p.k, e + C); nv = load1<BF16>(p.v, e + C); nx = load1<BF16>(p.w, e + C);
     }
     float yj = wave_sum_f(rj * ui * kj) * vj;  // bonus: (r_t . (u * k_t)) v_t[j]
+    s_r[lane] = rj;
+    s_k[lane] = kj;
+    s_d[lane] = dj;
+    __syncthreads();  // one wave: orders the row factors' stores before the broadcast reads
 #pragma unroll
-    for (int i = 0; i < kHead; ++i) {
-      const float ri = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rj), i));
-      const float ki = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kj), i));
-      const float di = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dj), i));
-      yj = fmaf(ri, s[i], yj);
-      s[i] = fmaf(di, s[i], ki * vj);
+    for (int i4 = 0; i4 < kHead / 4; ++i4) {
+      const float4 r4 = *reinterpret_cast<const float4 *>(&s_r[4 * i4]);
+      const float4 k4 = *reinterpret_cast<const float4 *>(&s_k[4 * i4]);
+      const float4 d4 = *reinterpret_cast<const float4 *>(&s_d[4 * i4]);
+      const float rr[4] = {r4.x, r4.y, r4.z, r4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // decay in place, then add k v in place: both update the state register itself
+        yj = fmaf(rr[e], s[4 * i4 + e], yj);
+        s[4 * i4 + e] = fmaf(kk[e], vj, s[4 * i4 + e] * dd[e]);
+      }
     }
+    __syncthreads();  // the reads finish before the next token's factors are stored
     if (p.y_bf16) static_cast<uint16_t *>(p.y)[e] = bf16_bits(yj);
     else static_cast<float *>(p.y)[e] = yj;
   }
