@@ -158,8 +158,20 @@ def _oracle_units_baseline(inp, target_s, units_all, run_units, tc_per_unit, des
     dt = time.perf_counter() - t0
     tc = sum(tc_per_unit(x) for x in units) if callable(tc_per_unit) else n * tc_per_unit
     res = {"value": tc / dt, "unit": TC, "cores": threads, "kind": "oracle",
-           "sample": f"{n} of {len(order)} {describe}, fp64, {dt:.1f} s wall"}
+           "sample": f"{n} of {len(order)} {describe}, fp64, {dt:.1f} s wall",
+           "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
     return res, units, out
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _err(got, ref):
