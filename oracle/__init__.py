@@ -22,6 +22,8 @@ from):
 * :func:`wkv6_backward` — gradients of the v6 recurrence with respect to r,
   k, v, x, u and the initial state, by reverse-mode differentiation of the
   definition, one token at a time.
+* :func:`wkv7` — the RWKV-7 generalized delta rule, ``h <- diag(exp(w_t)) h
+  + b_t (a_t^T h) + k_t v_t^T`` then ``y_t = r_t^T h``, state [key][value].
 """
 from __future__ import annotations
 
@@ -74,6 +76,8 @@ def _bind(lib):
                                       _dp, _dp, _dp, _dp, ctypes.c_long, _dp, _dp, _dp, _dp]
     lib.oracle_wkv6_head_bwd.restype = None
     lib.oracle_wkv6_head_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_long] + [_dp] * 14
+    lib.oracle_wkv7_head.restype = None
+    lib.oracle_wkv7_head.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_long] + [_dp] * 9
     return lib
 
 
@@ -252,3 +256,37 @@ def _fan_out(fn, units, threads):
         return
     with ThreadPoolExecutor(max_workers=n) as ex:
         list(ex.map(fn, units))
+
+
+def wkv7(r, w, k, v, a, b, H, N, state=None, state_map=None, units=None, threads=None, lib=None):
+    """v7 generalized delta rule in fp64.
+
+    ``r, w, k, v, a, b``: [B, T, H*N] (``w`` = log decay); ``state``: [n_state,
+    H, N, N] initial states h[key][value] (None: zero), row ``b`` starting from
+    ``state[state_map[b]]`` (``state_map`` None: ``b`` if n_state == B, else 0).
+    ``units``: optional list of (b, h) pairs to evaluate.  Returns
+    ``(y [B, T, H*N], S [B, H, N, N])``.
+    """
+    lib = lib or load()
+    r, w, k, v, a, b = (_f64(x) for x in (r, w, k, v, a, b))
+    B, T, C = r.shape
+    assert C == H * N
+    st = _f64(state)
+    if st is not None:
+        n_state = st.shape[0]
+        if state_map is None:
+            state_map = np.arange(B) if n_state == B else np.zeros(B, dtype=np.int64)
+    y = np.zeros((B, T, C))
+    S = np.zeros((B, H, N, N))
+    if units is None:
+        units = [(bb, h) for bb in range(B) for h in range(H)]
+
+    def run(unit):
+        bb, h = unit
+        base = bb * T * C + h * N
+        s0 = None if st is None else _ptr(st, (int(state_map[bb]) * H + h) * N * N)
+        lib.oracle_wkv7_head(T, N, C, _ptr(r, base), _ptr(w, base), _ptr(k, base), _ptr(v, base),
+                             _ptr(a, base), _ptr(b, base), s0, _ptr(y, base), _ptr(S, (bb * H + h) * N * N))
+
+    _fan_out(run, units, threads)
+    return y, S

@@ -26,11 +26,22 @@
  *     with d_t[i] = exp(-exp(x_t[i])) (x constant over t for v5), S indexed
  *     [key i][value j].
  *
+  *   - rwkv_ops page, generalized_delta_rule interface (rwkv7 "generalized
+ *     delta rule"): r, w, k, v, a, b of shape [B, T, H, K], w the decay term
+ *     "in log space", initial_state [N, H, K, V].  The page prints no formula;
+ *     the recurrence used here is the standard RWKV-7 one, with the state h
+ *     indexed [key i][value j] as the page's [.., K, V] layout:
+ *         sa[j]    = sum_i a_t[i] h[i][j]
+ *         h[i][j] <- exp(w_t[i]) h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j]
+ *         y_t[j]   = sum_i r_t[i] h[i][j]          (after the update)
+ *
  * Pins (tests/test_oracle_pins.py): closed-form weighted sums, O(T^2 N^2)
  * brute force, exact rational arithmetic on tiny cases, the no-decay case
  * equal to causal linear attention by matrix product, the full-decay case,
  * chunk-carry invariance, linearity, v5 == v6 with constant decay, and the
- * v4 <-> v5(N=1) mapping.
+ * v4 <-> v5(N=1) mapping; for v7, products of explicit transition matrices,
+ * the delta rule's exact recall, v7 with a = 0 against v5, linearity and
+ * chunk-carry invariance.
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no HIP headers).
  */
@@ -204,4 +215,51 @@ void oracle_wkv6_head_bwd(int T, int N, long ts,
     if (dS0) memcpy(dS0, G, sizeof(double) * NN);
     free(hist);
     free(G);
+}
+
+/*
+ * v7 (generalized delta rule), one (batch row, head) unit.
+ *
+ * r, w, k, v, a, b, y point at element [b, 0, h*N] of [B, T, H*N] arrays with
+ * token stride ts.  w is the log decay: the decay of key row i at token t is
+ * exp(w_t[i]).  S0 is the [N][N] initial state h[i][j] (NULL: zero), S_out
+ * receives the state after the last token (NULL: not returned).  Per token,
+ * in this order: sa = a_t^T h (over the key rows), the update
+ *   h[i][j] <- exp(w_t[i]) h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j],
+ * then y_t = r_t^T h with the updated state.
+ */
+void oracle_wkv7_head(int T, int N, long ts,
+                      const double *r, const double *w, const double *k,
+                      const double *v, const double *a, const double *b,
+                      const double *S0, double *y, double *S_out)
+{
+    size_t NN = (size_t)N * (size_t)N;
+    double *S = (double *)malloc(sizeof(double) * NN);
+    double *sa = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!S || !sa) { free(S); free(sa); return; }
+    if (S0) memcpy(S, S0, sizeof(double) * NN);
+    else memset(S, 0, sizeof(double) * NN);
+    for (int t = 0; t < T; t++) {
+        const double *rt = r + (long)t * ts, *wt = w + (long)t * ts, *kt = k + (long)t * ts;
+        const double *vt = v + (long)t * ts, *at = a + (long)t * ts, *bt = b + (long)t * ts;
+        double *yt = y + (long)t * ts;
+        for (int j = 0; j < N; j++) {
+            double acc = 0.0;
+            for (int i = 0; i < N; i++) acc += at[i] * S[i * N + j];
+            sa[j] = acc;
+        }
+        for (int i = 0; i < N; i++) {
+            double d = exp(wt[i]);
+            for (int j = 0; j < N; j++)
+                S[i * N + j] = d * S[i * N + j] + bt[i] * sa[j] + kt[i] * vt[j];
+        }
+        for (int j = 0; j < N; j++) {
+            double acc = 0.0;
+            for (int i = 0; i < N; i++) acc += rt[i] * S[i * N + j];
+            yt[j] = acc;
+        }
+    }
+    if (S_out) memcpy(S_out, S, sizeof(double) * NN);
+    free(S);
+    free(sa);
 }

@@ -25,6 +25,13 @@ Distributions follow the workloads the WKV operator is run on:
 * varlen serving (the web-rwkv batched-inference section: slots, a per-call
   ``token_chunk_size`` budget): prompt lengths ``~ U{1..2048}`` per slot,
   initial states ``~ N(0, 0.1)`` fp32, per-token inputs as v6.
+* v7 (the rwkv_ops ``generalized_delta_rule`` call: r, w, k, v, a, b of shape
+  [B, T, H, K], w the decay "in log space"): ``w = -exp(x)`` with
+  ``x ~ U(-6, 0)`` (decays exp(w) between 0.37 and 0.9975, as v6), r, k,
+  v ~ N(0, 0.5), and the delta-rule pair of the RWKV-7 time mix: a unit
+  direction ``kappa`` per (token, head) (an N(0, 1) vector scaled to length
+  1) with ``a = -kappa`` and ``b = kappa * beta``, ``beta ~ U(0, 1)`` per
+  channel; all rounded to bf16 when the dtype is bf16.
 
 ``N(m, s)`` means standard deviation ``s``.  Every generator uses numpy's
 PCG64 (``default_rng(seed)``) with a fixed draw order: lengths, decay
@@ -36,7 +43,7 @@ import numpy as np
 
 __all__ = [
     "bf16_round", "bf16_to_f32", "stored_f32",
-    "wkv4_inputs", "wkv5_inputs", "wkv6_inputs", "varlen_inputs", "wkv6_upstream",
+    "wkv4_inputs", "wkv5_inputs", "wkv6_inputs", "varlen_inputs", "wkv6_upstream", "wkv7_inputs",
 ]
 
 
@@ -189,3 +196,27 @@ def wkv6_upstream(B, T, H, N, seed=0, with_state=True):
     dy = _normal(rng, (B, T, H * N), 1.0)
     ds = _normal(rng, (B, H, N, N), 0.1) if with_state else None
     return dict(dy=dy, d_state=ds)
+
+
+def wkv7_inputs(B, T, H, N, seed=0, dtype="bf16", x_range=(-6.0, 0.0), init_state=None, state_std=0.1):
+    """Inputs of the v7 generalized delta rule.
+
+    ``r, w, k, v, a, b``: [B, T, H*N] in ``dtype`` (``w`` the log decay);
+    with ``init_state = n`` an [n, H, N, N] fp32 initial state ``~ N(0,
+    state_std)``.  Draw order: decay parameter, r, k, v, kappa, beta, state.
+    """
+    C = H * N
+    rng = np.random.default_rng(seed)
+    w = _store(-np.exp(_uniform(rng, (B, T, C), *x_range)), dtype)
+    r = _store(_normal(rng, (B, T, C), 0.5), dtype)
+    k = _store(_normal(rng, (B, T, C), 0.5), dtype)
+    v = _store(_normal(rng, (B, T, C), 0.5), dtype)
+    kappa = _normal(rng, (B, T, H, N), 1.0)
+    kappa /= np.sqrt(np.sum(kappa * kappa, axis=-1, keepdims=True, dtype=np.float32))
+    beta = _uniform(rng, (B, T, H, N), 0.0, 1.0)
+    a = _store((-kappa).reshape(B, T, C), dtype)
+    b = _store((kappa * beta).reshape(B, T, C), dtype)
+    state = None
+    if init_state:
+        state = _normal(rng, (init_state, H, N, N), state_std)
+    return dict(B=B, T=T, H=H, N=N, w=w, r=r, k=k, v=v, a=a, b=b, state=state, dtype=dtype)
