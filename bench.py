@@ -18,6 +18,10 @@ Other workloads (same JSON layout, not the headline):
            call (round robin), then 256 T=1 decode steps
   wkv6_bwd v6 backward of the headline shape: dr, dk, dv, dw, du and the
            initial-state gradient for upstream gradients of y and the final state
+  wkv7     v7 generalized delta rule forward, B=8 T=4096 H=32 N=64, bf16 inputs
+
+The wkv5 / wkv6 forward also takes --head-first ([B,H,T,N] token arrays) and
+--out-dtype bf16 (y rounded to bf16).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload wkv6] [--algo auto|scan|chunked]
 """
@@ -40,6 +44,7 @@ KERNEL_SOURCES = {
     "wkv4_scan_kernel": ["wkv4_scan.hip"],
     "wkv6_varlen_short_kernel": ["wkv6_decode.hip"],
     "wkv6_bwd_sweep_kernel": ["wkv6_backward.hip"],
+    "wkv7_scan_kernel": ["wkv7_scan.hip"],
 }
 SHORT_MAX = 8  # varlen calls with max_len up to this run the few-token kernel
 TC = "tokens·channels/s"
@@ -51,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20; 200 for the short decode step, 5 for the serving pass)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving", "wkv6_bwd"])
+    ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving", "wkv6_bwd", "wkv7"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
     ap.add_argument("--head-first", action="store_true",
                     help="wkv5/wkv6: head-first [B,H,T,N] token arrays instead of [B,T,H,N]")
@@ -248,6 +253,59 @@ def workload_wkv56(args, version):
                                f"{'bf16' if ybf else 'fp32'} output",
                    "B": B, "T": T, "H": H, "N": N, "algo": algo, "layout": "BHTN" if hf else "BTHN",
                    "y_dtype": args.out_dtype, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "cpu": cpu,
+    }
+
+
+def workload_wkv7(args):
+    """v7 generalized delta rule forward (B=8 T=4096 H=32 N=64 by default, bf16 inputs, fp32 y and state).
+    Bound by the vector ALUs: per state element and token one FMA for a^T h, three ops for the
+    update (decay, b sa, k v) and one FMA for r^T h."""
+    import numpy as np
+    import torch
+    import rwkv_linear_attention_wkv_amd as wkv
+    from wkv_inputs import wkv7_inputs
+
+    B, T, H, N = args.B or 8, args.T or 4096, args.H, 64
+    C = H * N
+    names = ("r", "w", "k", "v", "a", "b")
+    inp = wkv7_inputs(B, T, H, N, seed=args.seed)
+    toks = [_bf16_dev(inp[n]) for n in names]
+    y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
+    S = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
+    tc = B * T * C
+    alg_bytes = 6 * 2 * tc + 4 * tc + 4 * B * H * N * N
+    flops = 2 * 5 * N * tc
+
+    def run():
+        wkv.wkv7_forward(*toks, H, y=y, state_out=S)
+
+    def cpu(target_s):
+        import oracle
+        oracle.load()
+        units_all = [(b, h) for b in range(B) for h in range(H)]
+
+        def run_units(units, threads):
+            return oracle.wkv7(*(inp[n] for n in names), H, N, units=units, threads=threads)
+        res, units, (yo, So) = _oracle_units_baseline(inp, target_s, units_all, run_units, T * N,
+                                                      f"(batch row, head) units x T={T} x N={N}")
+        yg, Sg = y.cpu().numpy(), S.cpu().numpy()
+        ymax, ymean = _err(np.stack([yg[b, :, h * N:(h + 1) * N] for b, h in units]),
+                           np.stack([yo[b, :, h * N:(h + 1) * N] for b, h in units]))
+        smax, smean = _err(np.stack([Sg[b, h] for b, h in units]), np.stack([So[b, h] for b, h in units]))
+        return res, {"units": len(units), "y_max_abs": ymax, "y_mean_abs": ymean,
+                     "state_max_abs": smax, "state_mean_abs": smean}
+
+    return {
+        "metric": f"WKV7 fwd tokens·channels/s, B={B} T={T} H={H} N={N}",
+        "workload_key": f"wkv7_B{B}_T{T}_H{H}_N{N}_bf16",
+        "launches": [("forward", "wkv7_scan_kernel", run, alg_bytes, flops)],
+        "tc": tc,
+        "dtype": "fp32",
+        "compute": "fp32 vector ALU (token-sequential generalized delta rule)",
+        "data": "synthetic (seeded numpy PCG64; bf16 r,w,k,v,a,b with a = -kappa, b = kappa*beta; zero initial state)",
+        "config": {"workload": f"WKV7 forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
+                   "B": B, "T": T, "H": H, "N": N, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "cpu": cpu,
     }
 
@@ -562,6 +620,8 @@ def main():
         W = workload_wkv4(args)
     elif args.workload == "wkv6_bwd":
         W = workload_wkv6_bwd(args)
+    elif args.workload == "wkv7":
+        W = workload_wkv7(args)
     else:
         W = workload_serving(args, decode_only=args.workload == "decode")
     gen_s = time.perf_counter() - t0
@@ -644,7 +704,7 @@ def main():
         # run's kernel time (the busy fraction is clock-independent; the rate is not)
         roofline["mfma_busy"] = mfma["busy"]
         roofline["mfma_bf16_TFLOPs"] = round(mfma["gflop_per_launch"] / avg_s / 1e3, 1)
-    if D["kernel"] in ("wkv56_scan_kernel", "wkv6_bwd_sweep_kernel") and D["flops"] > 0:
+    if D["kernel"] in ("wkv56_scan_kernel", "wkv6_bwd_sweep_kernel", "wkv7_scan_kernel") and D["flops"] > 0:
         # The token-sequential scan (and each sweep of the backward) is bound by the vector ALUs: 3 fp32
         # FMA-class ops per state element and token by the recurrence's definition, packed FP32 off, against
         # the unpacked fp32 peak.  The HBM figures stay alongside.

@@ -261,6 +261,29 @@ WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
                          int32_t *dev_status, void *stream);
 
 /*
+ * v7 forward: the generalized delta rule of the rwkv_ops page's
+ * generalized_delta_rule operator (r, w, k, v, a, b of shape [B, T, H, K], w
+ * the decay "in log space", initial_state [N, H, K, V]; its single-step
+ * rwkv7_op_rnn call is this with T = 1).  The page gives no formula; this is
+ * the standard RWKV-7 recurrence.  Per (batch row, head), state h[key i][value j]:
+ *   sa[j] = sum_i a_t[i] h[i][j]
+ *   h[i][j] <- exp(w_t[i]) h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j]
+ *   y_t[j] = sum_i r_t[i] h[i][j]              (the updated state)
+ *   r, w, k, v, a, b [B,T,H*N] in_dtype
+ *   y          [B,T,H*N] out_dtype (WKV_F32, or WKV_BF16: the fp32 result
+ *              rounded to nearest even)
+ *   state_in, state_map, n_state, state_out, dev_status: as wkv6_forward
+ *              (states [.., H, N, N] indexed [key][value])
+ * N must be 64.  One token-sequential kernel (prefill and T = 1 decode).
+ */
+WKV_API wkv_status wkv7_forward(int B, int T, int H, int N,
+                        const void *r, const void *w, const void *k, const void *v,
+                        const void *a, const void *b, wkv_dtype in_dtype,
+                        void *y, wkv_dtype out_dtype,
+                        const float *state_in, const int32_t *state_map, int n_state,
+                        float *state_out, int32_t *dev_status, void *stream);
+
+/*
  * Host-side token-budget split for the varlen serving loop (HOST arrays).
  * Hands one token at a time to every slot with tokens left, in slot order,
  * until `budget` tokens are given out or no slot has tokens left.

@@ -29,7 +29,7 @@ _lib = _native.load()
 _ALGOS = {"auto": WKV_ALGO_AUTO, "scan": WKV_ALGO_SCAN, "chunked": WKV_ALGO_CHUNKED}
 
 __all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_backward", "wkv6_forward_varlen", "varlen_plan", "VarlenPlan",
-           "schedule_round_robin", "resolve_algo", "WkvError", "library"]
+           "wkv7_forward", "schedule_round_robin", "resolve_algo", "WkvError", "library"]
 
 
 def library():
@@ -234,6 +234,41 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
                              _ptr(dr), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), _ptr(du_rows), _ptr(d_state_in),
                              _ptr(dev_status), _stream(r)))
     return dr, dk, dv, dw, du, d_state_in
+
+
+def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
+                 dev_status=None, out_dtype=torch.float32):
+    """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] (one dtype; w = log decay).
+
+    ``state``: [n_state, H, N, N] fp32 initial states h[key][value]; ``state_map``: [B] int32.
+    Returns ``(y [B, T, H*N] in out_dtype unless given, state_out [B, H, N, N] fp32 or None)``.
+    """
+    B, T, C = r.shape
+    if C % H:
+        raise ValueError(f"C={C} is not a multiple of H={H}")
+    N = C // H
+    toks = [("r", r), ("w", w), ("k", k), ("v", v), ("a", a), ("b", b)]
+    _same_dtype(toks)
+    for name, t in toks:
+        _dev(t, name, shape=(B, T, C))
+    n_state = 0
+    if state is not None:
+        _dev(state, "state", torch.float32)
+        if state.dim() != 4 or tuple(state.shape[1:]) != (H, N, N):
+            raise ValueError(f"state must be [n_state, {H}, {N}, {N}], got {tuple(state.shape)}")
+        n_state = state.shape[0]
+    _dev(state_map, "state_map", torch.int32, (B,))
+    oc, odt = _out_code(y, out_dtype)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=odt, device=r.device)
+    _dev(y, "y", odt, (B, T, C))
+    if return_state and state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    _dev(state_out, "state_out", torch.float32, (B, H, N, N))
+    _dev(dev_status, "dev_status", torch.int32, (1,))
+    check(_lib.wkv7_forward(B, T, H, N, *(_ptr(t) for _, t in toks), _dtype_code(r), _ptr(y), oc, _ptr(state),
+                            _ptr(state_map), n_state, _ptr(state_out), _ptr(dev_status), _stream(r)))
+    return y, state_out
 
 
 class VarlenPlan:

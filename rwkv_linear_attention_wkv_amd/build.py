@@ -21,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libwkv.so")
-SOURCES = ["wkv_api.cpp", "wkv4_scan.hip", "wkv56_scan.hip", "wkv6_decode.hip", "wkv6_backward.hip", "wkv56_chunked.hip"]
+SOURCES = ["wkv_api.cpp", "wkv4_scan.hip", "wkv56_scan.hip", "wkv6_decode.hip", "wkv6_backward.hip", "wkv56_chunked.hip",
+           "wkv7_scan.hip"]
 ARCH = "gfx950"
 
 

@@ -61,6 +61,21 @@ struct BwdParams {
 
 hipError_t launch_wkv6_backward(const BwdParams &p, bool bf16, hipStream_t s);
 
+// v7 generalized delta rule, token-sequential (dense rows, [B, T, H*64] token arrays).
+struct V7Params {
+  int B, T, H;
+  const void *r, *w, *k, *v, *a, *b;  // w: log decay
+  void *y;                            // fp32, or bf16 when y_bf16
+  bool y_bf16;
+  const float *state_in;              // [n_state, H, 64, 64] h[key][value], or NULL
+  const int32_t *state_map;
+  int n_state;
+  float *state_out;                   // [B, H, 64, 64] or NULL
+  int32_t *dev_status;
+};
+
+hipError_t launch_wkv7_scan(const V7Params &p, bool bf16, hipStream_t s);
+
 // v4 channel-wise scan.
 struct V4Params {
   int B, T, C;

@@ -215,6 +215,51 @@ wkv_status wkv6_forward(int B, int T, int H, int N, const void *r, const void *k
                  n_state, state_out, algo, dev_status, stream);
 }
 
+wkv_status wkv7_forward(int B, int T, int H, int N, const void *r, const void *w, const void *k, const void *v,
+                        const void *a, const void *b, wkv_dtype in_dtype, void *y, wkv_dtype out_dtype,
+                        const float *state_in, const int32_t *state_map, int n_state, float *state_out,
+                        int32_t *dev_status, void *stream) {
+  const char *fn = "wkv7_forward";
+  REQUIRE(B >= 1 && T >= 0 && H >= 1, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn, B, T, H);
+  if (N != wkv::kHeadSize) return fail(WKV_ERR_UNSUPPORTED, "%s: head size N=%d is not supported (only 64)", fn, N);
+  if (!dtype_ok(in_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown input dtype %d", fn, in_dtype);
+  if (!dtype_ok(out_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown output dtype %d", fn, out_dtype);
+  REQUIRE(B <= kMaxGridY, "%s: B=%d exceeds %d", fn, B, kMaxGridY);
+  REQUIRE((int64_t)H * N <= (int64_t)1 << 30, "%s: H*N too large", fn);
+  if (T > 0) {
+    REQUIRE(r && w && k && v && a && b && y, "%s: r, w, k, v, a, b and y must be non-NULL", fn);
+    REQUIRE(aligned(r, 16) && aligned(w, 16) && aligned(k, 16) && aligned(v, 16) && aligned(a, 16) &&
+                aligned(b, 16) && aligned(y, 16),
+            "%s: r, w, k, v, a, b and y must be 16-byte aligned", fn);
+  }
+  if (state_in) {
+    REQUIRE(aligned(state_in, 16), "%s: state_in must be 16-byte aligned", fn);
+    REQUIRE(n_state >= 1, "%s: n_state must be >= 1 when state_in is given (got %d)", fn, n_state);
+    if (!state_map)
+      REQUIRE(n_state == 1 || n_state == B, "%s: without state_map, n_state must be 1 or B (got %d, B=%d)", fn,
+              n_state, B);
+    else
+      REQUIRE(aligned(state_map, 4), "%s: state_map must be 4-byte aligned", fn);
+  } else {
+    REQUIRE(!state_map, "%s: state_map given without state_in", fn);
+  }
+  if (state_out) {
+    REQUIRE(aligned(state_out, 16), "%s: state_out must be 16-byte aligned", fn);
+    if (state_out == state_in)
+      REQUIRE(!state_map && n_state == B, "%s: in-place state needs state_map == NULL and n_state == B", fn);
+  }
+  REQUIRE(!dev_status || aligned(dev_status, 4), "%s: dev_status must be 4-byte aligned", fn);
+  if (T == 0 && !state_out) return ok();
+  wkv::V7Params p{};
+  p.B = B; p.T = T; p.H = H;
+  p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
+  p.y = y;
+  p.y_bf16 = out_dtype == WKV_BF16;
+  p.state_in = state_in; p.state_map = state_map; p.n_state = n_state; p.state_out = state_out;
+  p.dev_status = dev_status;
+  return launched(wkv::launch_wkv7_scan(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
+}
+
 wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *k, const void *v, const void *w,
                          wkv_dtype in_dtype, const float *u, const float *dy, const float *state_in,
                          const int32_t *state_map, int n_state, const float *state_final,

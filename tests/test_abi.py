@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(nat.SIGNATURES)
@@ -213,6 +213,26 @@ def test_ex_v4_and_varlen_validation(lib):
                                       None) == U
     assert lib.wkv6_forward_varlen_ex(0, 2, 64, None, 16, 32, P, P, P, P, 1, P, P, 1, None, None, None, 4, None,
                                       None) == nat.WKV_OK
+
+
+def test_v7_validation(lib):
+    E, U = nat.WKV_ERR_INVALID_ARG, nat.WKV_ERR_UNSUPPORTED
+
+    def call(B=2, T=8, H=2, N=64, r=P, w=P, k=P, v=P, a=P, b=P, dt=1, y=P, odt=0, si=None, sm=None, ns=0, so=None,
+             ds=None):
+        return lib.wkv7_forward(B, T, H, N, r, w, k, v, a, b, dt, y, odt, si, sm, ns, so, ds, None)
+
+    assert call(N=32) == U and b"head size" in lib.wkv_last_error()
+    assert call(dt=4) == U
+    assert call(odt=3) == U and b"output dtype" in lib.wkv_last_error()
+    assert call(B=0) == E
+    assert call(T=-1) == E
+    assert call(a=None) == E
+    assert call(b=MIS) == E and b"aligned" in lib.wkv_last_error()
+    assert call(si=P, ns=3) == E
+    assert call(sm=P) == E
+    assert call(si=P, sm=P, ns=2, so=P) == E
+    assert call(T=0, r=None, w=None, k=None, v=None, a=None, b=None, y=None) == nat.WKV_OK
 
 
 def test_resolve_algo_wide_rows(lib):

@@ -1,0 +1,122 @@
+"""GPU parity of the v7 generalized-delta-rule kernel against the fp64 oracle (through the C ABI).
+
+Inputs (wkv7_inputs, seeded): log decay -exp(U(-6, 0)), r, k, v ~ N(0, 0.5), a = -kappa and
+b = kappa * beta with a unit kappa per (token, head) and beta ~ U(0, 1); initial states ~ N(0, 0.1).
+Tolerances as the other forms: bf16 inputs max abs 2e-2 and mean abs 5e-3 on y and the final
+state; fp32 inputs max error relative to max(|o|, rms(o)) 2e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rwkv_linear_attention_wkv_amd as wkv
+from parity import assert_bf16, assert_fp32, dev, host
+from wkv_inputs import wkv7_inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("r", "w", "k", "v", "a", "b")
+
+
+def _run(inp, **kw):
+    return wkv.wkv7_forward(*(dev(inp[n]) for n in NAMES), inp["H"], **kw)
+
+
+def _oracle(inp, **kw):
+    return oracle.wkv7(*(inp[n] for n in NAMES), inp["H"], inp["N"], **kw)
+
+
+@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (17, "f32"), (130, "bf16"), (200, "f32")])
+def test_v7_small_cases(T, dtype):
+    inp = wkv7_inputs(2, T, 3, 64, seed=200 + T, dtype=dtype, init_state=3)
+    check = assert_fp32 if dtype == "f32" else assert_bf16
+    smap = np.array([2, 0], dtype=np.int32)
+    y, S = _run(inp, state=dev(inp["state"]), state_map=dev(smap))
+    y1, S1 = _run(inp, state=dev(inp["state"][:1]))                    # shared row
+    st = dev(inp["state"][:2])
+    y2, _ = _run(inp, state=st, state_out=st)                          # in place
+    y0, S0 = _run(inp)                                                 # zero state
+    torch.cuda.synchronize()
+    yo, So = _oracle(inp, state=inp["state"], state_map=smap)
+    check(host(y), yo, "v7 y")
+    check(host(S), So, "v7 state")
+    yo1, So1 = _oracle(inp, state=inp["state"][:1])
+    check(host(y1), yo1, "v7 shared y")
+    check(host(S1), So1, "v7 shared state")
+    yo2, So2 = _oracle(inp, state=inp["state"][:2])
+    check(host(y2), yo2, "v7 in-place y")
+    check(host(st), So2, "v7 in-place state")
+    yo0, So0 = _oracle(inp)
+    check(host(y0), yo0, "v7 zero-state y")
+    check(host(S0), So0, "v7 zero-state state")
+
+
+def test_v7_moderate_full_compare():
+    inp = wkv7_inputs(2, 1024, 4, 64, seed=210)
+    y, S = _run(inp)
+    torch.cuda.synchronize()
+    yo, So = _oracle(inp)
+    assert_bf16(host(y), yo, "v7 y T=1024")
+    assert_bf16(host(S), So, "v7 state T=1024")
+    assert np.max(np.abs(host(y) - yo)) < 1e-3
+
+
+def test_v7_full_shape_sampled():
+    """B=8 T=4096 H=32 N=64 bf16 (the bench shape), sampled (row, head) units."""
+    B, T, H = 8, 4096, 32
+    inp = wkv7_inputs(B, T, H, 64, seed=0)
+    y, S = _run(inp)
+    torch.cuda.synchronize()
+    units = [(0, 0), (3, 17), (7, 31)]
+    yo, So = _oracle(inp, units=units)
+    yh, Sh = host(y), host(S)
+    for b, h in units:
+        sl = slice(h * 64, (h + 1) * 64)
+        assert_bf16(yh[b, :, sl], yo[b, :, sl], f"y unit {(b, h)}")
+        assert_bf16(Sh[b, h], So[b, h], f"state unit {(b, h)}")
+
+
+def test_v7_decode_steps_carry_the_state():
+    """A prompt then T = 1 steps with the state carried equals one pass over all tokens."""
+    inp = wkv7_inputs(4, 70, 2, 64, seed=211, init_state=4)
+    cut = 66
+    pre = dict(inp, **{n: inp[n][:, :cut] for n in NAMES})
+    y_pre, S = _run(pre, state=dev(inp["state"]))
+    ys = [y_pre]
+    for t in range(cut, 70):
+        step = dict(inp, **{n: inp[n][:, t:t + 1] for n in NAMES})
+        yt, S = _run(step, state=S)
+        ys.append(yt)
+    torch.cuda.synchronize()
+    yo, So = _oracle(inp, state=inp["state"])
+    assert_bf16(host(torch.cat(ys, dim=1)), yo, "prompt + decode y")
+    assert_bf16(host(S), So, "prompt + decode state")
+
+
+def test_v7_bf16_out_deterministic_and_empty():
+    inp = wkv7_inputs(2, 100, 2, 64, seed=212, init_state=2)
+    ya, Sa = _run(inp, state=dev(inp["state"]))
+    yb, Sb = _run(inp, state=dev(inp["state"]))
+    yc, Sc = _run(inp, state=dev(inp["state"]), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb) and torch.equal(Sa, Sb)
+    assert yc.dtype == torch.bfloat16 and torch.equal(yc, ya.to(torch.bfloat16)) and torch.equal(Sc, Sa)
+    # T = 0: the state row is copied, nothing else is touched
+    e = wkv7_inputs(2, 0, 2, 64, seed=213, init_state=3)
+    smap = dev(np.array([2, 1], dtype=np.int32))
+    st = dev(e["state"])
+    empty = torch.empty((2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    _, S0 = wkv.wkv7_forward(empty, empty, empty, empty, empty, empty, 2, state=st, state_map=smap)
+    torch.cuda.synchronize()
+    assert torch.equal(S0, st[[2, 1]])
+
+
+def test_v7_bad_state_map_sets_status():
+    inp = wkv7_inputs(2, 20, 1, 64, seed=214, init_state=2)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.full((2, 20, 64), float("nan"), device="cuda")
+    _run(inp, state=dev(inp["state"]), state_map=dev(np.array([1, 9], dtype=np.int32)), y=y, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & wkv.WKV_DEV_BAD_STATE_MAP
+    assert torch.isnan(y[1]).all() and not torch.isnan(y[0]).any()
