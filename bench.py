@@ -258,7 +258,8 @@ def workload_wkv56(args, version):
 
 
 def workload_wkv7(args):
-    """v7 generalized delta rule forward (B=8 T=4096 H=32 N=64 by default, bf16 inputs, fp32 y and state).
+    """v7 generalized delta rule forward (B=8 T=4096 H=32 N=64 by default, bf16 inputs, fp32 y, initial
+    and final states; --T 1 --B 64 is a decode step for 64 slots).
     Bound by the vector ALUs: per state element and token one FMA for a^T h, three ops for the
     update (decay, b sa, k v) and one FMA for r^T h."""
     import numpy as np
@@ -269,16 +270,17 @@ def workload_wkv7(args):
     B, T, H, N = args.B or 8, args.T or 4096, args.H, 64
     C = H * N
     names = ("r", "w", "k", "v", "a", "b")
-    inp = wkv7_inputs(B, T, H, N, seed=args.seed)
+    inp = wkv7_inputs(B, T, H, N, seed=args.seed, init_state=B)
     toks = [_bf16_dev(inp[n]) for n in names]
+    S0 = torch.from_numpy(inp["state"]).cuda()
     y = torch.empty((B, T, C), dtype=torch.float32, device="cuda")
     S = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
     tc = B * T * C
-    alg_bytes = 6 * 2 * tc + 4 * tc + 4 * B * H * N * N
+    alg_bytes = 6 * 2 * tc + 4 * tc + 2 * 4 * B * H * N * N  # tokens in, y out, state in and out
     flops = 2 * 5 * N * tc
 
     def run():
-        wkv.wkv7_forward(*toks, H, y=y, state_out=S)
+        wkv.wkv7_forward(*toks, H, state=S0, y=y, state_out=S)
 
     def cpu(target_s):
         import oracle
@@ -286,7 +288,7 @@ def workload_wkv7(args):
         units_all = [(b, h) for b in range(B) for h in range(H)]
 
         def run_units(units, threads):
-            return oracle.wkv7(*(inp[n] for n in names), H, N, units=units, threads=threads)
+            return oracle.wkv7(*(inp[n] for n in names), H, N, state=inp["state"], units=units, threads=threads)
         res, units, (yo, So) = _oracle_units_baseline(inp, target_s, units_all, run_units, T * N,
                                                       f"(batch row, head) units x T={T} x N={N}")
         yg, Sg = y.cpu().numpy(), S.cpu().numpy()
@@ -303,7 +305,7 @@ def workload_wkv7(args):
         "tc": tc,
         "dtype": "fp32",
         "compute": "fp32 vector ALU (token-sequential generalized delta rule)",
-        "data": "synthetic (seeded numpy PCG64; bf16 r,w,k,v,a,b with a = -kappa, b = kappa*beta; zero initial state)",
+        "data": "synthetic (seeded numpy PCG64; bf16 r,w,k,v,a,b with a = -kappa, b = kappa*beta; initial states ~ N(0,0.1))",
         "config": {"workload": f"WKV7 forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
                    "B": B, "T": T, "H": H, "N": N, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "cpu": cpu,

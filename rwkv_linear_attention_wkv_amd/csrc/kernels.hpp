@@ -74,6 +74,8 @@ struct V7Params {
   int32_t *dev_status;
 };
 
+// Calls with T <= kShortMax run a one-wave-per-(row, head) kernel, longer ones the
+// 256-thread token-block kernel.
 hipError_t launch_wkv7_scan(const V7Params &p, bool bf16, hipStream_t s);
 
 // v4 channel-wise scan.

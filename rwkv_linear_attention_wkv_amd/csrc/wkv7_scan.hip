@@ -13,7 +13,8 @@
 // are sums over the 8 lanes of a column pair, formed on DPP (half-row mirror, then
 // two quad permutes), so the token loop needs no barrier.  Tokens are staged through
 // LDS in blocks of 16 (r, exp(w), k, a, b per key row; v per column), read back as
-// 16-byte broadcasts, and the next block's tokens are loaded while one is computed.
+// 16-byte broadcasts one token ahead of their use, and the next block's tokens are
+// loaded from HBM while one is computed.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "wkv.h"
@@ -26,10 +27,13 @@ constexpr int kTB = 16;                          // tokens staged per block
 constexpr int kTPT = kTB * kHead / kThreads;     // (token, channel) pairs each thread stages
 static_assert(kTPT == 4, "staging: four tokens per thread");
 
+constexpr int kSP = kHead + 2;  // padded row of the LDS state tile (8-byte aligned rows)
+
 struct __align__(16) V7Smem {
   float f[5][kTB][kHead];  // per key row: a, b, exp(w), k, r
   float v[kTB][kHead];     // per value column
   float y[kTB][kHead];     // outputs of the block
+  float st[kHead][kSP];    // the state on its way in from and out to HBM
 };
 
 template <int CTRL>
@@ -66,12 +70,23 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
       return;
     }
   }
+  // The state tile moves between HBM and the lanes through LDS: HBM sees whole 1 KiB runs
+  // (thread t handles the 16-byte pieces t, t + 256, ...), the lanes their 8 x 2 blocks.
   float hs[8][2];
   if (row_in >= 0) {
-    const float *sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead);
+    const float4 *sp = reinterpret_cast<const float4 *>(p.state_in + ((long)row_in * p.H + h) * (kHead * kHead));
+#pragma unroll
+    for (int q = 0; q < kHead * kHead / 4 / kThreads; ++q) {
+      const int e = tid + kThreads * q;  // 16-byte piece: row e / 16, columns 4 (e % 16) ..
+      const float4 x = sp[e];
+      float *d = &sm.st[e >> 4][4 * (e & 15)];
+      *reinterpret_cast<float2 *>(d) = make_float2(x.x, x.y);
+      *reinterpret_cast<float2 *>(d + 2) = make_float2(x.z, x.w);
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float2 s2 = *reinterpret_cast<const float2 *>(sp + (8 * g + i) * kHead + col);
+      const float2 s2 = *reinterpret_cast<const float2 *>(&sm.st[8 * g + i][col]);
       hs[i][0] = s2.x;
       hs[i][1] = s2.y;
     }
@@ -111,45 +126,70 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
     if (t0 + kTB < T) fetch(t0 + kTB);  // the next block, in flight during this one
     __syncthreads();
 
-    for (int tt = 0; tt < nb; ++tt) {
-      const float4 *f4p[5];
+    // One token step from its staged factors.  The factors of the next token are read
+    // into the other register set before this token's arithmetic, so the LDS latency
+    // overlaps it (one wave per SIMD leaves nothing else to hide it).
+    struct Fac {
+      float4 f[5][2];  // a, b, exp(w), k, r of the lane's 8 key rows
+      float2 v;        // v of the lane's 2 columns
+    };
+    auto read_fac = [&](Fac &F, int tt) {
 #pragma unroll
-      for (int m = 0; m < 5; ++m) f4p[m] = reinterpret_cast<const float4 *>(&sm.f[m][tt][8 * g]);
-      float fa[8], fb[8], fd[8], fk[8], fr[8];
-      auto unpack = [&](float (&dst)[8], const float4 *src) {
-        const float4 lo = src[0], hi = src[1];
-        dst[0] = lo.x; dst[1] = lo.y; dst[2] = lo.z; dst[3] = lo.w;
-        dst[4] = hi.x; dst[5] = hi.y; dst[6] = hi.z; dst[7] = hi.w;
-      };
-      unpack(fa, f4p[0]);
-      const float2 vv = *reinterpret_cast<const float2 *>(&sm.v[tt][col]);
-      // sa over this lane's 8 key rows, then over the column's 8 lanes
-      float s0 = fa[0] * hs[0][0], s1 = fa[0] * hs[0][1];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        s0 = fmaf(fa[i], hs[i][0], s0);
-        s1 = fmaf(fa[i], hs[i][1], s1);
+      for (int m = 0; m < 5; ++m) {
+        const float4 *src = reinterpret_cast<const float4 *>(&sm.f[m][tt][8 * g]);
+        F.f[m][0] = src[0];
+        F.f[m][1] = src[1];
       }
-      s0 = sum8(s0);
-      s1 = sum8(s1);
-      unpack(fb, f4p[1]);
-      unpack(fd, f4p[2]);
-      unpack(fk, f4p[3]);
-      unpack(fr, f4p[4]);
+      F.v = *reinterpret_cast<const float2 *>(&sm.v[tt][col]);
+    };
+    auto step = [&](const Fac &F, int tt) {
+      float fa[8], fb[8], fd[8], fk[8], fr[8];
+      auto unpack = [&](float (&dst)[8], const float4 (&src)[2]) {
+        dst[0] = src[0].x; dst[1] = src[0].y; dst[2] = src[0].z; dst[3] = src[0].w;
+        dst[4] = src[1].x; dst[5] = src[1].y; dst[6] = src[1].z; dst[7] = src[1].w;
+      };
+      unpack(fa, F.f[0]);
+      unpack(fb, F.f[1]);
+      unpack(fd, F.f[2]);
+      unpack(fk, F.f[3]);
+      unpack(fr, F.f[4]);
+      // a^T h over this lane's 8 key rows (two chains of four), then over the column's 8 lanes
+      float s0a = fa[0] * hs[0][0], s1a = fa[0] * hs[0][1];
+      float s0b = fa[4] * hs[4][0], s1b = fa[4] * hs[4][1];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        s0a = fmaf(fa[i], hs[i][0], s0a);
+        s1a = fmaf(fa[i], hs[i][1], s1a);
+        s0b = fmaf(fa[i + 4], hs[i + 4][0], s0b);
+        s1b = fmaf(fa[i + 4], hs[i + 4][1], s1b);
+      }
+      const float s0 = sum8(s0a + s0b), s1 = sum8(s1a + s1b);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        hs[i][0] = fmaf(fk[i], vv.x, fmaf(fb[i], s0, fd[i] * hs[i][0]));
-        hs[i][1] = fmaf(fk[i], vv.y, fmaf(fb[i], s1, fd[i] * hs[i][1]));
+        hs[i][0] = fmaf(fk[i], F.v.x, fmaf(fb[i], s0, fd[i] * hs[i][0]));
+        hs[i][1] = fmaf(fk[i], F.v.y, fmaf(fb[i], s1, fd[i] * hs[i][1]));
       }
-      float y0 = fr[0] * hs[0][0], y1 = fr[0] * hs[0][1];
+      float y0a = fr[0] * hs[0][0], y1a = fr[0] * hs[0][1];
+      float y0b = fr[4] * hs[4][0], y1b = fr[4] * hs[4][1];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        y0 = fmaf(fr[i], hs[i][0], y0);
-        y1 = fmaf(fr[i], hs[i][1], y1);
+      for (int i = 1; i < 4; ++i) {
+        y0a = fmaf(fr[i], hs[i][0], y0a);
+        y1a = fmaf(fr[i], hs[i][1], y1a);
+        y0b = fmaf(fr[i + 4], hs[i + 4][0], y0b);
+        y1b = fmaf(fr[i + 4], hs[i + 4][1], y1b);
       }
-      y0 = sum8(y0);
-      y1 = sum8(y1);
+      const float y0 = sum8(y0a + y0b), y1 = sum8(y1a + y1b);
       if (g == 0) *reinterpret_cast<float2 *>(&sm.y[tt][col]) = make_float2(y0, y1);
+    };
+    Fac FA, FB;
+    read_fac(FA, 0);
+    for (int tt = 0; tt < nb; tt += 2) {
+      read_fac(FB, min(tt + 1, kTB - 1));  // past the block's last token: read, never used
+      step(FA, tt);
+      if (tt + 1 < nb) {
+        read_fac(FA, min(tt + 2, kTB - 1));
+        step(FB, tt + 1);
+      }
     }
     __syncthreads();
     // store the block's outputs: thread -> (token 4 wave + q, channel lane), coalesced rows
@@ -168,10 +208,96 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
   }
 
   if (p.state_out) {
-    float *sp = p.state_out + ((long)unit * p.H + h) * (kHead * kHead);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<float2 *>(sp + (8 * g + i) * kHead + col) = make_float2(hs[i][0], hs[i][1]);
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<float2 *>(&sm.st[8 * g + i][col]) = make_float2(hs[i][0], hs[i][1]);
+    __syncthreads();
+    float4 *sp = reinterpret_cast<float4 *>(p.state_out + ((long)unit * p.H + h) * (kHead * kHead));
+#pragma unroll
+    for (int q = 0; q < kHead * kHead / 4 / kThreads; ++q) {
+      const int e = tid + kThreads * q;
+      const float *d = &sm.st[e >> 4][4 * (e & 15)];
+      const float2 lo = *reinterpret_cast<const float2 *>(d), hi = *reinterpret_cast<const float2 *>(d + 2);
+      sp[e] = make_float4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+}
+
+// Calls of at most kShortMax tokens per row (T = 1 decode steps): one wave per (row,
+// head), lane j holding column j of the state (h[0..63][j], 64 registers), so the two
+// sums over key rows are sums inside the lane and the state moves as 256-byte rows.  The
+// key-row factors of a token reach all lanes through LDS as 16-byte broadcasts.  No
+// workgroup barrier beyond the one wave's own.
+template <bool BF16>
+__global__ void __launch_bounds__(64) wkv7_short_kernel(V7Params p) {
+  __shared__ __align__(16) float sf[5][kHead];  // a, b, exp(w), k, r of the token
+  const int h = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int lane = threadIdx.x;  // value column j; key row i for the factors
+  const long C = (long)p.H * kHead;
+  const long base = (long)unit * p.T * C + h * kHead + lane;
+
+  int row_in = -1;
+  if (p.state_in) {
+    row_in = p.state_map ? p.state_map[unit] : (p.n_state == 1 ? 0 : unit);
+    if (row_in < 0 || row_in >= p.n_state) {
+      if (lane == 0 && p.dev_status) atomicOr(p.dev_status, WKV_DEV_BAD_STATE_MAP);
+      return;
+    }
+  }
+  float hc[kHead];
+  if (row_in >= 0) {
+    const float *sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead) + lane;
+#pragma unroll
+    for (int i = 0; i < kHead; ++i) hc[i] = sp[i * kHead];
+  } else {
+#pragma unroll
+    for (int i = 0; i < kHead; ++i) hc[i] = 0.f;
+  }
+  for (int t = 0; t < p.T; ++t) {
+    const long e = base + (long)t * C;
+    sf[0][lane] = load1<BF16>(p.a, e);
+    sf[1][lane] = load1<BF16>(p.b, e);
+    sf[2][lane] = fast_exp(load1<BF16>(p.w, e));
+    sf[3][lane] = load1<BF16>(p.k, e);
+    sf[4][lane] = load1<BF16>(p.r, e);
+    const float vj = load1<BF16>(p.v, e);
+    __syncthreads();  // one wave: orders the factors' stores before the broadcast reads
+    // four independent chains per sum (a 64-long dependent chain would expose the FMA latency)
+    float sp4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i4 = 0; i4 < kHead / 4; ++i4) {
+      const float4 a4 = *reinterpret_cast<const float4 *>(&sf[0][4 * i4]);
+      sp4[0] = fmaf(a4.x, hc[4 * i4], sp4[0]);
+      sp4[1] = fmaf(a4.y, hc[4 * i4 + 1], sp4[1]);
+      sp4[2] = fmaf(a4.z, hc[4 * i4 + 2], sp4[2]);
+      sp4[3] = fmaf(a4.w, hc[4 * i4 + 3], sp4[3]);
+    }
+    const float sa = (sp4[0] + sp4[1]) + (sp4[2] + sp4[3]);
+    float yp4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i4 = 0; i4 < kHead / 4; ++i4) {
+      const float4 b4 = *reinterpret_cast<const float4 *>(&sf[1][4 * i4]);
+      const float4 d4 = *reinterpret_cast<const float4 *>(&sf[2][4 * i4]);
+      const float4 k4 = *reinterpret_cast<const float4 *>(&sf[3][4 * i4]);
+      const float4 r4 = *reinterpret_cast<const float4 *>(&sf[4][4 * i4]);
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
+      const float kk[4] = {k4.x, k4.y, k4.z, k4.w}, rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float &x = hc[4 * i4 + q];
+        x = fmaf(kk[q], vj, fmaf(bb[q], sa, dd[q] * x));
+        yp4[q] = fmaf(rr[q], x, yp4[q]);
+      }
+    }
+    const float y = (yp4[0] + yp4[1]) + (yp4[2] + yp4[3]);
+    if (p.y_bf16) static_cast<uint16_t *>(p.y)[e] = bf16_bits(y);
+    else static_cast<float *>(p.y)[e] = y;
+    __syncthreads();  // the broadcast reads finish before the next token's factors are stored
+  }
+  if (p.state_out) {
+    float *sp = p.state_out + ((long)unit * p.H + h) * (kHead * kHead) + lane;
+#pragma unroll
+    for (int i = 0; i < kHead; ++i) sp[i * kHead] = hc[i];
   }
 }
 
@@ -179,8 +305,13 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
 
 hipError_t launch_wkv7_scan(const V7Params &p, bool bf16, hipStream_t s) {
   dim3 grid(p.H, p.B);
-  if (bf16) hipLaunchKernelGGL((wkv7_scan_kernel<true>), grid, dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((wkv7_scan_kernel<false>), grid, dim3(kThreads), 0, s, p);
+  if (p.T <= kShortMax) {
+    if (bf16) hipLaunchKernelGGL((wkv7_short_kernel<true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((wkv7_short_kernel<false>), grid, dim3(64), 0, s, p);
+  } else {
+    if (bf16) hipLaunchKernelGGL((wkv7_scan_kernel<true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((wkv7_scan_kernel<false>), grid, dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
