@@ -262,12 +262,14 @@ WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
 
 /*
  * v7 forward: the generalized delta rule of the rwkv_ops page's
- * generalized_delta_rule operator (r, w, k, v, a, b of shape [B, T, H, K], w
- * the decay "in log space", initial_state [N, H, K, V]; its single-step
- * rwkv7_op_rnn call is this with T = 1).  The page gives no formula; this is
- * the standard RWKV-7 recurrence.  Per (batch row, head), state h[key i][value j]:
+ * generalized_delta_rule operator (r, w, k, v, a, b of shape [B, T, H, K],
+ * initial_state [N, H, K, V]; its single-step rwkv7_op_rnn call is this with
+ * T = 1).  The page gives no formula; this is the standard RWKV-7
+ * recurrence, with the decay exp(-exp(w)) of rwkv6op (the page's padding
+ * note, w += (1 - mask) * -1e9 for padded tokens, needs their decay to be
+ * exactly 1).  Per (batch row, head), state h[key i][value j]:
  *   sa[j] = sum_i a_t[i] h[i][j]
- *   h[i][j] <- exp(w_t[i]) h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j]
+ *   h[i][j] <- d_t[i] h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j],  d_t = exp(-exp(w_t))
  *   y_t[j] = sum_i r_t[i] h[i][j]              (the updated state)
  *   r, w, k, v, a, b [B,T,H*N] in_dtype
  *   y          [B,T,H*N] out_dtype (WKV_F32, or WKV_BF16: the fp32 result

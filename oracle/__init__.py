@@ -22,8 +22,9 @@ from):
 * :func:`wkv6_backward` — gradients of the v6 recurrence with respect to r,
   k, v, x, u and the initial state, by reverse-mode differentiation of the
   definition, one token at a time.
-* :func:`wkv7` — the RWKV-7 generalized delta rule, ``h <- diag(exp(w_t)) h
-  + b_t (a_t^T h) + k_t v_t^T`` then ``y_t = r_t^T h``, state [key][value].
+* :func:`wkv7` — the RWKV-7 generalized delta rule, ``h <- diag(d_t) h
+  + b_t (a_t^T h) + k_t v_t^T`` then ``y_t = r_t^T h``, state [key][value],
+  ``d_t = exp(-exp(w_t))``.
 """
 from __future__ import annotations
 
@@ -261,7 +262,8 @@ def _fan_out(fn, units, threads):
 def wkv7(r, w, k, v, a, b, H, N, state=None, state_map=None, units=None, threads=None, lib=None):
     """v7 generalized delta rule in fp64.
 
-    ``r, w, k, v, a, b``: [B, T, H*N] (``w`` = log decay); ``state``: [n_state,
+    ``r, w, k, v, a, b``: [B, T, H*N] (``w`` = raw decay parameter, decay
+    ``exp(-exp(w))``); ``state``: [n_state,
     H, N, N] initial states h[key][value] (None: zero), row ``b`` starting from
     ``state[state_map[b]]`` (``state_map`` None: ``b`` if n_state == B, else 0).
     ``units``: optional list of (b, h) pairs to evaluate.  Returns

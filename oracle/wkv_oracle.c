@@ -27,13 +27,17 @@
  *     [key i][value j].
  *
   *   - rwkv_ops page, generalized_delta_rule interface (rwkv7 "generalized
- *     delta rule"): r, w, k, v, a, b of shape [B, T, H, K], w the decay term
- *     "in log space", initial_state [N, H, K, V].  The page prints no formula;
- *     the recurrence used here is the standard RWKV-7 one, with the state h
- *     indexed [key i][value j] as the page's [.., K, V] layout:
+ *     delta rule"): r, w, k, v, a, b of shape [B, T, H, K], initial_state
+ *     [N, H, K, V].  The page prints no formula; the recurrence used here is
+ *     the standard RWKV-7 one, with the state h indexed [key i][value j] as
+ *     the page's [.., K, V] layout:
  *         sa[j]    = sum_i a_t[i] h[i][j]
- *         h[i][j] <- exp(w_t[i]) h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j]
+ *         h[i][j] <- d_t[i] h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j]
  *         y_t[j]   = sum_i r_t[i] h[i][j]          (after the update)
+ *     with d_t = exp(-exp(w_t)), the rwkv6op parameterisation: the page's
+ *     padding note for this operator (w += (1 - mask) * -1e9, handled for
+ *     left and right padding by the recurrent operator) needs a padded
+ *     token's decay to be exactly 1, which exp(-exp(-1e9)) is.
  *
  * Pins (tests/test_oracle_pins.py): closed-form weighted sums, O(T^2 N^2)
  * brute force, exact rational arithmetic on tiny cases, the no-decay case
@@ -221,11 +225,11 @@ void oracle_wkv6_head_bwd(int T, int N, long ts,
  * v7 (generalized delta rule), one (batch row, head) unit.
  *
  * r, w, k, v, a, b, y point at element [b, 0, h*N] of [B, T, H*N] arrays with
- * token stride ts.  w is the log decay: the decay of key row i at token t is
- * exp(w_t[i]).  S0 is the [N][N] initial state h[i][j] (NULL: zero), S_out
- * receives the state after the last token (NULL: not returned).  Per token,
- * in this order: sa = a_t^T h (over the key rows), the update
- *   h[i][j] <- exp(w_t[i]) h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j],
+ * token stride ts.  w is the raw decay parameter: the decay of key row i at
+ * token t is exp(-exp(w_t[i])).  S0 is the [N][N] initial state h[i][j] (NULL:
+ * zero), S_out receives the state after the last token (NULL: not returned).
+ * Per token, in this order: sa = a_t^T h (over the key rows), the update
+ *   h[i][j] <- d_t[i] h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j],
  * then y_t = r_t^T h with the updated state.
  */
 void oracle_wkv7_head(int T, int N, long ts,
@@ -249,7 +253,7 @@ void oracle_wkv7_head(int T, int N, long ts,
             sa[j] = acc;
         }
         for (int i = 0; i < N; i++) {
-            double d = exp(wt[i]);
+            double d = exp(-exp(wt[i]));
             for (int j = 0; j < N; j++)
                 S[i * N + j] = d * S[i * N + j] + bt[i] * sa[j] + kt[i] * vt[j];
         }

@@ -238,7 +238,7 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
 
 def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
                  dev_status=None, out_dtype=torch.float32):
-    """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] (one dtype; w = log decay).
+    """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] (one dtype; decay exp(-exp(w))).
 
     ``state``: [n_state, H, N, N] fp32 initial states h[key][value]; ``state_map``: [B] int32.
     Returns ``(y [B, T, H*N] in out_dtype unless given, state_out [B, H, N, N] fp32 or None)``.

@@ -64,7 +64,7 @@ hipError_t launch_wkv6_backward(const BwdParams &p, bool bf16, hipStream_t s);
 // v7 generalized delta rule, token-sequential (dense rows, [B, T, H*64] token arrays).
 struct V7Params {
   int B, T, H;
-  const void *r, *w, *k, *v, *a, *b;  // w: log decay
+  const void *r, *w, *k, *v, *a, *b;  // w: decay parameter, decay exp(-exp(w))
   void *y;                            // fp32, or bf16 when y_bf16
   bool y_bf16;
   const float *state_in;              // [n_state, H, 64, 64] h[key][value], or NULL

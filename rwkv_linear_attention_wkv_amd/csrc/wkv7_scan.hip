@@ -1,10 +1,11 @@
 // WKV v7 (the generalized delta rule of the rwkv_ops page's generalized_delta_rule
-// operator: r, w, k, v, a, b of shape [B, T, H, K], w the decay in log space, state
-// [.., K, V]).  Per (batch row, head), with the state h[key i][value j]:
+// operator: r, w, k, v, a, b of shape [B, T, H, K], state [.., K, V]).  Per (batch
+// row, head), with the state h[key i][value j] and d_t = exp(-exp(w_t)):
 //   sa[j]    = sum_i a_t[i] h[i][j]
-//   h[i][j] <- exp(w_t[i]) h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j]
+//   h[i][j] <- d_t[i] h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j]
 //   y_t[j]   = sum_i r_t[i] h[i][j]        (with the updated state)
-// (the standard RWKV-7 recurrence; the page gives the interface only).
+// (the standard RWKV-7 recurrence; the page gives the interface only, and its padding
+// note, w += (1 - mask) * -1e9, needs the rwkv6op decay exp(-exp(w))).
 //
 // Value columns j evolve independently, so one 256-thread workgroup per (row, head)
 // gives each wave 16 columns, and each lane 8 key rows of 2 columns (16 state values
@@ -12,7 +13,7 @@
 // 16w + 2m + 1.  The two sums over key rows (a^T h before the update, r^T h after it)
 // are sums over the 8 lanes of a column pair, formed on DPP (half-row mirror, then
 // two quad permutes), so the token loop needs no barrier.  Tokens are staged through
-// LDS in blocks of 16 (r, exp(w), k, a, b per key row; v per column), read back as
+// LDS in blocks of 16 (r, d, k, a, b per key row; v per column), read back as
 // 16-byte broadcasts one token ahead of their use, and the next block's tokens are
 // loaded from HBM while one is computed.
 #include "common.hpp"
@@ -30,7 +31,7 @@ static_assert(kTPT == 4, "staging: four tokens per thread");
 constexpr int kSP = kHead + 2;  // padded row of the LDS state tile (8-byte aligned rows)
 
 struct __align__(16) V7Smem {
-  float f[5][kTB][kHead];  // per key row: a, b, exp(w), k, r
+  float f[5][kTB][kHead];  // per key row: a, b, d = exp(-exp(w)), k, r
   float v[kTB][kHead];     // per value column
   float y[kTB][kHead];     // outputs of the block
   float st[kHead][kSP];    // the state on its way in from and out to HBM
@@ -118,7 +119,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
       const int tt = kTPT * wave + q;
       sm.f[0][tt][lane] = pa[q];
       sm.f[1][tt][lane] = pb[q];
-      sm.f[2][tt][lane] = fast_exp(pw[q]);
+      sm.f[2][tt][lane] = decay_of(pw[q]);
       sm.f[3][tt][lane] = pk[q];
       sm.f[4][tt][lane] = pr[q];
       sm.v[tt][lane] = pv[q];
@@ -130,7 +131,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
     // into the other register set before this token's arithmetic, so the LDS latency
     // overlaps it (one wave per SIMD leaves nothing else to hide it).
     struct Fac {
-      float4 f[5][2];  // a, b, exp(w), k, r of the lane's 8 key rows
+      float4 f[5][2];  // a, b, d, k, r of the lane's 8 key rows
       float2 v;        // v of the lane's 2 columns
     };
     auto read_fac = [&](Fac &F, int tt) {
@@ -229,7 +230,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
 // workgroup barrier beyond the one wave's own.
 template <bool BF16>
 __global__ void __launch_bounds__(64) wkv7_short_kernel(V7Params p) {
-  __shared__ __align__(16) float sf[5][kHead];  // a, b, exp(w), k, r of the token
+  __shared__ __align__(16) float sf[5][kHead];  // a, b, d = exp(-exp(w)), k, r of the token
   const int h = blockIdx.x;
   const int unit = blockIdx.y;
   const int lane = threadIdx.x;  // value column j; key row i for the factors
@@ -257,7 +258,7 @@ __global__ void __launch_bounds__(64) wkv7_short_kernel(V7Params p) {
     const long e = base + (long)t * C;
     sf[0][lane] = load1<BF16>(p.a, e);
     sf[1][lane] = load1<BF16>(p.b, e);
-    sf[2][lane] = fast_exp(load1<BF16>(p.w, e));
+    sf[2][lane] = decay_of(load1<BF16>(p.w, e));
     sf[3][lane] = load1<BF16>(p.k, e);
     sf[4][lane] = load1<BF16>(p.r, e);
     const float vj = load1<BF16>(p.v, e);

@@ -1,6 +1,6 @@
 """GPU parity of the v7 generalized-delta-rule kernel against the fp64 oracle (through the C ABI).
 
-Inputs (wkv7_inputs, seeded): log decay -exp(U(-6, 0)), r, k, v ~ N(0, 0.5), a = -kappa and
+Inputs (wkv7_inputs, seeded): decay parameter w ~ U(-6, 0) (decay exp(-exp(w))), r, k, v ~ N(0, 0.5), a = -kappa and
 b = kappa * beta with a unit kappa per (token, head) and beta ~ U(0, 1); initial states ~ N(0, 0.1).
 Tolerances as the other forms: bf16 inputs max abs 2e-2 and mean abs 5e-3 on y and the final
 state; fp32 inputs max error relative to max(|o|, rms(o)) 2e-5.
@@ -12,7 +12,7 @@ import torch
 import oracle
 import rwkv_linear_attention_wkv_amd as wkv
 from parity import assert_bf16, assert_fp32, dev, host
-from wkv_inputs import wkv7_inputs
+from wkv_inputs import bf16_round, wkv7_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -120,3 +120,25 @@ def test_v7_bad_state_map_sets_status():
     torch.cuda.synchronize()
     assert int(status.item()) & wkv.WKV_DEV_BAD_STATE_MAP
     assert torch.isnan(y[1]).all() and not torch.isnan(y[0]).any()
+
+
+@pytest.mark.parametrize("side", ["left", "right"])
+def test_v7_padding_by_decay_parameter(side):
+    """The page's padding convention for this operator: padded tokens carry w = -1e9 (decay exactly
+    1) and zero r, k, v, a, b.  They leave the state bitwise as it was, so the real tokens' outputs
+    and the final state equal the unpadded call's, bitwise; the padded outputs are zero."""
+    T, P = 40, 9
+    inp = wkv7_inputs(2, T, 2, 64, seed=215, init_state=2)
+    y, S = _run(inp, state=dev(inp["state"]))
+    pad = {n: np.zeros((2, P, 128), dtype=np.uint16) for n in NAMES}
+    pad["w"] = bf16_round(np.full((2, P, 128), -1e9, dtype=np.float32))
+    if side == "left":
+        padded = dict(inp, **{n: np.concatenate([pad[n], inp[n]], axis=1) for n in NAMES})
+        real, fill = slice(P, P + T), slice(0, P)
+    else:
+        padded = dict(inp, **{n: np.concatenate([inp[n], pad[n]], axis=1) for n in NAMES})
+        real, fill = slice(0, T), slice(T, T + P)
+    yp, Sp = _run(padded, state=dev(inp["state"]))
+    torch.cuda.synchronize()
+    assert torch.equal(yp[:, real], y) and torch.equal(Sp, S)
+    assert torch.count_nonzero(yp[:, fill]) == 0

@@ -26,8 +26,8 @@ Distributions follow the workloads the WKV operator is run on:
   ``token_chunk_size`` budget): prompt lengths ``~ U{1..2048}`` per slot,
   initial states ``~ N(0, 0.1)`` fp32, per-token inputs as v6.
 * v7 (the rwkv_ops ``generalized_delta_rule`` call: r, w, k, v, a, b of shape
-  [B, T, H, K], w the decay "in log space"): ``w = -exp(x)`` with
-  ``x ~ U(-6, 0)`` (decays exp(w) between 0.37 and 0.9975, as v6), r, k,
+  [B, T, H, K]): the decay parameter ``w ~ U(-6, 0)`` (decay
+  ``exp(-exp(w))`` between 0.37 and 0.9975, as v6), r, k,
   v ~ N(0, 0.5), and the delta-rule pair of the RWKV-7 time mix: a unit
   direction ``kappa`` per (token, head) (an N(0, 1) vector scaled to length
   1) with ``a = -kappa`` and ``b = kappa * beta``, ``beta ~ U(0, 1)`` per
@@ -201,13 +201,13 @@ def wkv6_upstream(B, T, H, N, seed=0, with_state=True):
 def wkv7_inputs(B, T, H, N, seed=0, dtype="bf16", x_range=(-6.0, 0.0), init_state=None, state_std=0.1):
     """Inputs of the v7 generalized delta rule.
 
-    ``r, w, k, v, a, b``: [B, T, H*N] in ``dtype`` (``w`` the log decay);
+    ``r, w, k, v, a, b``: [B, T, H*N] in ``dtype`` (``w`` the decay parameter);
     with ``init_state = n`` an [n, H, N, N] fp32 initial state ``~ N(0,
     state_std)``.  Draw order: decay parameter, r, k, v, kappa, beta, state.
     """
     C = H * N
     rng = np.random.default_rng(seed)
-    w = _store(-np.exp(_uniform(rng, (B, T, C), *x_range)), dtype)
+    w = _store(_uniform(rng, (B, T, C), *x_range), dtype)
     r = _store(_normal(rng, (B, T, C), 0.5), dtype)
     k = _store(_normal(rng, (B, T, C), 0.5), dtype)
     v = _store(_normal(rng, (B, T, C), 0.5), dtype)
