@@ -1,4 +1,4 @@
-"""MI355X (gfx950) RWKV WKV time-mixing kernels — thin PyTorch binding.
+"""MI355X (gfx950) RWKV WKV time-mixing kernels (v4, v5, v6 and the v6 backward, v7) — thin PyTorch binding.
 
 Every function here only checks and marshals arguments (shapes, dtypes,
 device pointers, the current HIP stream) and calls the C ABI of libwkv.so
