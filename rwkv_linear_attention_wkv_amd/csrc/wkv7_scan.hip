@@ -7,12 +7,12 @@
 // (the standard RWKV-7 recurrence; the page gives the interface only, and its padding
 // note, w += (1 - mask) * -1e9, needs the rwkv6op decay exp(-exp(w))).
 //
-// Value columns j evolve independently, so one 256-thread workgroup per (row, head)
-// gives each wave 16 columns, and each lane 8 key rows of 2 columns (16 state values
-// in registers): lane 8m + g of wave w holds rows 8g .. 8g+7 of columns 16w + 2m and
-// 16w + 2m + 1.  The two sums over key rows (a^T h before the update, r^T h after it)
-// are sums over the 8 lanes of a column pair, formed on DPP (half-row mirror, then
-// two quad permutes), so the token loop needs no barrier.  Tokens are staged through
+// Value columns j evolve independently, so one 512-thread workgroup per (row, head)
+// gives each wave 8 columns, and each lane 8 key rows of one column (8 state values in
+// registers): lane 8m + g of wave w holds rows 8g .. 8g+7 of column 8w + m.  The two
+// sums over key rows (a^T h before the update, r^T h after it) are sums over the 8
+// lanes of a column, formed on DPP (half-row mirror, then two quad permutes), so the
+// token loop needs no barrier; two waves per SIMD hide each other's dependency chains.  Tokens are staged through
 // LDS in blocks of 16 (r, d, k, a, b per key row; v per column), read back as
 // 16-byte broadcasts one token ahead of their use, and the next block's tokens are
 // loaded from HBM while one is computed.
@@ -23,10 +23,10 @@
 namespace wkv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kTB = 16;                          // tokens staged per block
 constexpr int kTPT = kTB * kHead / kThreads;     // (token, channel) pairs each thread stages
-static_assert(kTPT == 4, "staging: four tokens per thread");
+static_assert(kTPT * kThreads == kTB * kHead, "staging shape");
 
 constexpr int kSP = kHead + 2;  // padded row of the LDS state tile (8-byte aligned rows)
 
@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane & 7;                        // key rows 8g .. 8g+7
-  const int col = 16 * wave + 2 * (lane >> 3);   // value columns col, col + 1
+  const int col = 8 * wave + (lane >> 3);        // value column
   const long C = (long)p.H * kHead;
   const long base = (long)unit * p.T * C + h * kHead;  // token 0, channel 0 of this (row, head)
   const int T = p.T;
@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
   }
   // The state tile moves between HBM and the lanes through LDS: HBM sees whole 1 KiB runs
   // (thread t handles the 16-byte pieces t, t + 256, ...), the lanes their 8 x 2 blocks.
-  float hs[8][2];
+  float hs[8];
   if (row_in >= 0) {
     const float4 *sp = reinterpret_cast<const float4 *>(p.state_in + ((long)row_in * p.H + h) * (kHead * kHead));
 #pragma unroll
@@ -86,18 +86,14 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float2 s2 = *reinterpret_cast<const float2 *>(&sm.st[8 * g + i][col]);
-      hs[i][0] = s2.x;
-      hs[i][1] = s2.y;
-    }
+    for (int i = 0; i < 8; ++i) hs[i] = sm.st[8 * g + i][col];
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hs[i][0] = hs[i][1] = 0.f;
+    for (int i = 0; i < 8; ++i) hs[i] = 0.f;
   }
 
-  // staging role: channel `lane`, tokens 4 wave .. 4 wave + 3 of a block (rows past the end
-  // reread the last token: staged but never used)
+  // staging role: channel `lane`, tokens kTPT wave .. kTPT wave + kTPT - 1 of a block (rows
+  // past the end reread the last token: staged but never used)
   float pa[kTPT], pb[kTPT], pw[kTPT], pk[kTPT], pr[kTPT], pv[kTPT];
   auto fetch = [&](int t0) {
 #pragma unroll
@@ -132,7 +128,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
     // overlaps it (one wave per SIMD leaves nothing else to hide it).
     struct Fac {
       float4 f[5][2];  // a, b, d, k, r of the lane's 8 key rows
-      float2 v;        // v of the lane's 2 columns
+      float v;         // v of the lane's column
     };
     auto read_fac = [&](Fac &F, int tt) {
 #pragma unroll
@@ -141,7 +137,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
         F.f[m][0] = src[0];
         F.f[m][1] = src[1];
       }
-      F.v = *reinterpret_cast<const float2 *>(&sm.v[tt][col]);
+      F.v = sm.v[tt][col];
     };
     auto step = [&](const Fac &F, int tt) {
       float fa[8], fb[8], fd[8], fk[8], fr[8];
@@ -155,32 +151,23 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
       unpack(fk, F.f[3]);
       unpack(fr, F.f[4]);
       // a^T h over this lane's 8 key rows (two chains of four), then over the column's 8 lanes
-      float s0a = fa[0] * hs[0][0], s1a = fa[0] * hs[0][1];
-      float s0b = fa[4] * hs[4][0], s1b = fa[4] * hs[4][1];
+      float sa0 = fa[0] * hs[0], sa1 = fa[4] * hs[4];
 #pragma unroll
       for (int i = 1; i < 4; ++i) {
-        s0a = fmaf(fa[i], hs[i][0], s0a);
-        s1a = fmaf(fa[i], hs[i][1], s1a);
-        s0b = fmaf(fa[i + 4], hs[i + 4][0], s0b);
-        s1b = fmaf(fa[i + 4], hs[i + 4][1], s1b);
+        sa0 = fmaf(fa[i], hs[i], sa0);
+        sa1 = fmaf(fa[i + 4], hs[i + 4], sa1);
       }
-      const float s0 = sum8(s0a + s0b), s1 = sum8(s1a + s1b);
+      const float sa = sum8(sa0 + sa1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hs[i][0] = fmaf(fk[i], F.v.x, fmaf(fb[i], s0, fd[i] * hs[i][0]));
-        hs[i][1] = fmaf(fk[i], F.v.y, fmaf(fb[i], s1, fd[i] * hs[i][1]));
-      }
-      float y0a = fr[0] * hs[0][0], y1a = fr[0] * hs[0][1];
-      float y0b = fr[4] * hs[4][0], y1b = fr[4] * hs[4][1];
+      for (int i = 0; i < 8; ++i) hs[i] = fmaf(fk[i], F.v, fmaf(fb[i], sa, fd[i] * hs[i]));
+      float y0 = fr[0] * hs[0], y1 = fr[4] * hs[4];
 #pragma unroll
       for (int i = 1; i < 4; ++i) {
-        y0a = fmaf(fr[i], hs[i][0], y0a);
-        y1a = fmaf(fr[i], hs[i][1], y1a);
-        y0b = fmaf(fr[i + 4], hs[i + 4][0], y0b);
-        y1b = fmaf(fr[i + 4], hs[i + 4][1], y1b);
+        y0 = fmaf(fr[i], hs[i], y0);
+        y1 = fmaf(fr[i + 4], hs[i + 4], y1);
       }
-      const float y0 = sum8(y0a + y0b), y1 = sum8(y1a + y1b);
-      if (g == 0) *reinterpret_cast<float2 *>(&sm.y[tt][col]) = make_float2(y0, y1);
+      const float y = sum8(y0 + y1);
+      if (g == 0) sm.y[tt][col] = y;
     };
     Fac FA, FB;
     read_fac(FA, 0);
@@ -193,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
       }
     }
     __syncthreads();
-    // store the block's outputs: thread -> (token 4 wave + q, channel lane), coalesced rows
+    // store the block's outputs: thread -> (token kTPT wave + q, channel lane), coalesced rows
 #pragma unroll
     for (int q = 0; q < kTPT; ++q) {
       const int tt = kTPT * wave + q;
@@ -210,7 +197,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
 
   if (p.state_out) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<float2 *>(&sm.st[8 * g + i][col]) = make_float2(hs[i][0], hs[i][1]);
+    for (int i = 0; i < 8; ++i) sm.st[8 * g + i][col] = hs[i];
     __syncthreads();
     float4 *sp = reinterpret_cast<float4 *>(p.state_out + ((long)unit * p.H + h) * (kHead * kHead));
 #pragma unroll
