@@ -271,16 +271,17 @@ WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
  *   sa[j] = sum_i a_t[i] h[i][j]
  *   h[i][j] <- d_t[i] h[i][j] + b_t[i] sa[j] + k_t[i] v_t[j],  d_t = exp(-exp(w_t))
  *   y_t[j] = sum_i r_t[i] h[i][j]              (the updated state)
- *   r, w, k, v, a, b [B,T,H*N] in_dtype
- *   y          [B,T,H*N] out_dtype (WKV_F32, or WKV_BF16: the fp32 result
- *              rounded to nearest even)
+ *   r, w, k, v, a, b [B,T,H*N] in_dtype, or [B,H,T,N] with layout
+ *              WKV_LAYOUT_BHTN (the operators' head_first flag)
+ *   y          the same layout, out_dtype (WKV_F32, or WKV_BF16: the fp32
+ *              result rounded to nearest even)
  *   state_in, state_map, n_state, state_out, dev_status: as wkv6_forward
  *              (states [.., H, N, N] indexed [key][value])
  * N must be 64.  One token-sequential kernel (prefill and T = 1 decode).
  */
 WKV_API wkv_status wkv7_forward(int B, int T, int H, int N,
                         const void *r, const void *w, const void *k, const void *v,
-                        const void *a, const void *b, wkv_dtype in_dtype,
+                        const void *a, const void *b, wkv_dtype in_dtype, wkv_layout layout,
                         void *y, wkv_dtype out_dtype,
                         const float *state_in, const int32_t *state_map, int n_state,
                         float *state_out, int32_t *dev_status, void *stream);

@@ -237,20 +237,30 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
 
 
 def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
-                 dev_status=None, out_dtype=torch.float32):
-    """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] (one dtype; decay exp(-exp(w))).
+                 dev_status=None, out_dtype=torch.float32, head_first=False):
+    """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] ([B, H, T, N] with ``head_first``),
+    one dtype; decay exp(-exp(w)).
 
     ``state``: [n_state, H, N, N] fp32 initial states h[key][value]; ``state_map``: [B] int32.
-    Returns ``(y [B, T, H*N] in out_dtype unless given, state_out [B, H, N, N] fp32 or None)``.
+    Returns ``(y, state_out [B, H, N, N] fp32 or None)``; y has the token layout of r and dtype
+    ``out_dtype`` unless given.
     """
-    B, T, C = r.shape
-    if C % H:
-        raise ValueError(f"C={C} is not a multiple of H={H}")
-    N = C // H
+    if head_first:
+        if r.dim() != 4 or r.shape[1] != H:
+            raise ValueError(f"head-first r must be [B, {H}, T, N], got {tuple(r.shape)}")
+        B, _, T, N = r.shape
+        C = H * N
+        tok_shape = (B, H, T, N)
+    else:
+        B, T, C = r.shape
+        if C % H:
+            raise ValueError(f"C={C} is not a multiple of H={H}")
+        N = C // H
+        tok_shape = (B, T, C)
     toks = [("r", r), ("w", w), ("k", k), ("v", v), ("a", a), ("b", b)]
     _same_dtype(toks)
     for name, t in toks:
-        _dev(t, name, shape=(B, T, C))
+        _dev(t, name, shape=tok_shape)
     n_state = 0
     if state is not None:
         _dev(state, "state", torch.float32)
@@ -260,14 +270,15 @@ def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, sta
     _dev(state_map, "state_map", torch.int32, (B,))
     oc, odt = _out_code(y, out_dtype)
     if y is None:
-        y = torch.empty((B, T, C), dtype=odt, device=r.device)
-    _dev(y, "y", odt, (B, T, C))
+        y = torch.empty(tok_shape, dtype=odt, device=r.device)
+    _dev(y, "y", odt, tok_shape)
     if return_state and state_out is None:
         state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
     _dev(state_out, "state_out", torch.float32, (B, H, N, N))
     _dev(dev_status, "dev_status", torch.int32, (1,))
-    check(_lib.wkv7_forward(B, T, H, N, *(_ptr(t) for _, t in toks), _dtype_code(r), _ptr(y), oc, _ptr(state),
-                            _ptr(state_map), n_state, _ptr(state_out), _ptr(dev_status), _stream(r)))
+    layout = _native.WKV_LAYOUT_BHTN if head_first else _native.WKV_LAYOUT_BTHN
+    check(_lib.wkv7_forward(B, T, H, N, *(_ptr(t) for _, t in toks), _dtype_code(r), layout, _ptr(y), oc,
+                            _ptr(state), _ptr(state_map), n_state, _ptr(state_out), _ptr(dev_status), _stream(r)))
     return y, state_out
 
 

@@ -67,6 +67,7 @@ struct V7Params {
   const void *r, *w, *k, *v, *a, *b;  // w: decay parameter, decay exp(-exp(w))
   void *y;                            // fp32, or bf16 when y_bf16
   bool y_bf16;
+  long row_stride, tok_stride, head_stride;  // token-array layout, as in ScanParams
   const float *state_in;              // [n_state, H, 64, 64] h[key][value], or NULL
   const int32_t *state_map;
   int n_state;

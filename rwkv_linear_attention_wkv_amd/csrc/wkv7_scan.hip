@@ -59,8 +59,8 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane & 7;                        // key rows 8g .. 8g+7
   const int col = 8 * wave + (lane >> 3);        // value column
-  const long C = (long)p.H * kHead;
-  const long base = (long)unit * p.T * C + h * kHead;  // token 0, channel 0 of this (row, head)
+  const long C = p.tok_stride;                                     // elements between tokens
+  const long base = unit * p.row_stride + h * p.head_stride;       // token 0, channel 0 of (row, head)
   const int T = p.T;
 
   int row_in = -1;
@@ -221,8 +221,8 @@ __global__ void __launch_bounds__(64) wkv7_short_kernel(V7Params p) {
   const int h = blockIdx.x;
   const int unit = blockIdx.y;
   const int lane = threadIdx.x;  // value column j; key row i for the factors
-  const long C = (long)p.H * kHead;
-  const long base = (long)unit * p.T * C + h * kHead + lane;
+  const long C = p.tok_stride;
+  const long base = unit * p.row_stride + h * p.head_stride + lane;
 
   int row_in = -1;
   if (p.state_in) {

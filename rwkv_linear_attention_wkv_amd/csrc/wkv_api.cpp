@@ -216,14 +216,16 @@ wkv_status wkv6_forward(int B, int T, int H, int N, const void *r, const void *k
 }
 
 wkv_status wkv7_forward(int B, int T, int H, int N, const void *r, const void *w, const void *k, const void *v,
-                        const void *a, const void *b, wkv_dtype in_dtype, void *y, wkv_dtype out_dtype,
-                        const float *state_in, const int32_t *state_map, int n_state, float *state_out,
-                        int32_t *dev_status, void *stream) {
+                        const void *a, const void *b, wkv_dtype in_dtype, wkv_layout layout, void *y,
+                        wkv_dtype out_dtype, const float *state_in, const int32_t *state_map, int n_state,
+                        float *state_out, int32_t *dev_status, void *stream) {
   const char *fn = "wkv7_forward";
   REQUIRE(B >= 1 && T >= 0 && H >= 1, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn, B, T, H);
   if (N != wkv::kHeadSize) return fail(WKV_ERR_UNSUPPORTED, "%s: head size N=%d is not supported (only 64)", fn, N);
   if (!dtype_ok(in_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown input dtype %d", fn, in_dtype);
   if (!dtype_ok(out_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown output dtype %d", fn, out_dtype);
+  if (layout != WKV_LAYOUT_BTHN && layout != WKV_LAYOUT_BHTN)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: unknown layout %d", fn, layout);
   REQUIRE(B <= kMaxGridY, "%s: B=%d exceeds %d", fn, B, kMaxGridY);
   REQUIRE((int64_t)H * N <= (int64_t)1 << 30, "%s: H*N too large", fn);
   if (T > 0) {
@@ -255,6 +257,11 @@ wkv_status wkv7_forward(int B, int T, int H, int N, const void *r, const void *w
   p.r = r; p.w = w; p.k = k; p.v = v; p.a = a; p.b = b;
   p.y = y;
   p.y_bf16 = out_dtype == WKV_BF16;
+  if (layout == WKV_LAYOUT_BTHN) {
+    p.row_stride = (long)T * H * N; p.tok_stride = (long)H * N; p.head_stride = N;
+  } else {
+    p.row_stride = (long)H * T * N; p.tok_stride = N; p.head_stride = (long)T * N;
+  }
   p.state_in = state_in; p.state_map = state_map; p.n_state = n_state; p.state_out = state_out;
   p.dev_status = dev_status;
   return launched(wkv::launch_wkv7_scan(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);

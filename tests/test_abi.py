@@ -218,13 +218,14 @@ def test_ex_v4_and_varlen_validation(lib):
 def test_v7_validation(lib):
     E, U = nat.WKV_ERR_INVALID_ARG, nat.WKV_ERR_UNSUPPORTED
 
-    def call(B=2, T=8, H=2, N=64, r=P, w=P, k=P, v=P, a=P, b=P, dt=1, y=P, odt=0, si=None, sm=None, ns=0, so=None,
-             ds=None):
-        return lib.wkv7_forward(B, T, H, N, r, w, k, v, a, b, dt, y, odt, si, sm, ns, so, ds, None)
+    def call(B=2, T=8, H=2, N=64, r=P, w=P, k=P, v=P, a=P, b=P, dt=1, lay=0, y=P, odt=0, si=None, sm=None, ns=0,
+             so=None, ds=None):
+        return lib.wkv7_forward(B, T, H, N, r, w, k, v, a, b, dt, lay, y, odt, si, sm, ns, so, ds, None)
 
     assert call(N=32) == U and b"head size" in lib.wkv_last_error()
     assert call(dt=4) == U
     assert call(odt=3) == U and b"output dtype" in lib.wkv_last_error()
+    assert call(lay=5) == U and b"layout" in lib.wkv_last_error()
     assert call(B=0) == E
     assert call(T=-1) == E
     assert call(a=None) == E

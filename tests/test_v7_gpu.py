@@ -142,3 +142,17 @@ def test_v7_padding_by_decay_parameter(side):
     torch.cuda.synchronize()
     assert torch.equal(yp[:, real], y) and torch.equal(Sp, S)
     assert torch.count_nonzero(yp[:, fill]) == 0
+
+
+@pytest.mark.parametrize("T", [1, 130])
+def test_v7_head_first_is_exact(T):
+    """Head-first [B, H, T, N] arrays (the operators' head_first flag) give bitwise the token-major
+    results, on the prefill kernel (T = 130) and the few-token kernel (T = 1)."""
+    B, H = 3, 2
+    inp = wkv7_inputs(B, T, H, 64, seed=216 + T, init_state=B)
+    y, S = _run(inp, state=dev(inp["state"]))
+    hf = [dev(np.ascontiguousarray(inp[n].reshape(B, T, H, 64).transpose(0, 2, 1, 3))) for n in NAMES]
+    yh, Sh = wkv.wkv7_forward(*hf, H, state=dev(inp["state"]), head_first=True)
+    torch.cuda.synchronize()
+    assert yh.shape == (B, H, T, 64)
+    assert torch.equal(yh.permute(0, 2, 1, 3).reshape(B, T, H * 64), y) and torch.equal(Sh, S)
