@@ -10,12 +10,29 @@
 // Value columns j evolve independently, so one 512-thread workgroup per (row, head)
 // gives each wave 8 columns, and each lane 8 key rows of one column (8 state values in
 // registers): lane 8m + g of wave w holds rows 8g .. 8g+7 of column 8w + m.  The two
-// sums over key rows (a^T h before the update, r^T h after it) are sums over the 8
-// lanes of a column, formed on DPP (half-row mirror, then two quad permutes), so the
-// token loop needs no barrier; two waves per SIMD hide each other's dependency chains.  Tokens are staged through
-// LDS in blocks of 16 (r, d, k, a, b per key row; v per column), read back as
-// 16-byte broadcasts one token ahead of their use, and the next block's tokens are
-// loaded from HBM while one is computed.
+// sums over key rows are sums over the 8 lanes of a column, formed on DPP (half-row
+// mirror, then two quad permutes), so the token loop needs no barrier; two waves per
+// SIMD hide each other's dependency chains.  After a token's update the lane forms
+// r^T h (that token's output) and the next token's a^T h from the same state values, as
+// two interleaved sums.  Tokens are staged through LDS in blocks of 64 (8 consecutive
+// tokens per wave), read back as 16-byte broadcasts one token ahead of their use, and
+// the next block's tokens are loaded from HBM while one is computed.
+//
+// Rescaled frame.  Inside a block let G_t[i] = d_0[i] ... d_t[i] (from the block start,
+// G_{-1} = 1) and carry g[i][j] = h[i][j] / G_t[i] instead of h.  The recurrence becomes
+//   sa[j]    = sum_i (a_t[i] G_{t-1}[i]) g[i][j]
+//   g[i][j] <- g[i][j] + (b_t[i] / G_t[i]) sa[j] + (k_t[i] / G_t[i]) v_t[j]
+//   y_t[j]   = sum_i (r_t[i] G_t[i]) g[i][j]
+// (two FMAs per state value for the update instead of a multiply and two FMAs), and
+// h = G_last g at the block end.  The staging pass forms the scaled factors (1 / G from
+// the hardware reciprocal, within an ulp: a rounding-level change of the increments):
+// each wave posts the running product of its 8 decays per key row through LDS one
+// barrier ahead, and every wave chains the 8 posted products in the same order.  A
+// block where some G falls below 2^-64 (so that 1/G would leave the safe range) is
+// staged and run in the direct form instead; the test is on values every wave holds
+// bitwise alike, so all waves take the same branch.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "wkv.h"
@@ -24,28 +41,34 @@ namespace wkv {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kTB = 16;                          // tokens staged per block
+constexpr int kTB = 64;                          // tokens staged per block
 constexpr int kTPT = kTB * kHead / kThreads;     // (token, channel) pairs each thread stages
-static_assert(kTPT * kThreads == kTB * kHead, "staging shape");
+constexpr int kWaves = kThreads / 64;
+static_assert(kWaves * kTPT == kTB, "staging shape: consecutive tokens per wave");
+constexpr float kMinFrame = 0x1p-64f;            // smallest block decay product of the frame form
 
 constexpr int kSP = kHead + 2;  // padded row of the LDS state tile (8-byte aligned rows)
 
 struct __align__(16) V7Smem {
-  float f[5][kTB][kHead];  // per key row: a, b, d = exp(-exp(w)), k, r
-  float v[kTB][kHead];     // per value column
-  float y[kTB][kHead];     // outputs of the block
-  float st[kHead][kSP];    // the state on its way in from and out to HBM
+  // per key row, per token of the block: a, b, d, k, r (direct form) or
+  // a G_{t-1}, b / G_t, G_t, k / G_t, r G_t (frame form)
+  float f[5][kTB][kHead];
+  float v[kTB][kHead];      // per value column
+  float y[kTB][kHead];      // outputs of the block
+  float dp[kWaves][kHead];  // per key row: the product of each wave's decays
+  float st[kHead][kSP];     // the state on its way in from and out to HBM
 };
 
 template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ float dpp_add(float x) {
+  // x + x[lane permuted by CTRL]; full row and bank masks, so every source lane is valid
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 // Sum over the 8 lanes of an aligned group of 8 (every lane receives the same sum).
 __device__ __forceinline__ float sum8(float x) {
-  x += dpp<0x141>(x);  // row_half_mirror: lane i <-> 7 - i
-  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_add<0x141>(x);  // row_half_mirror: lane i <-> 7 - i
+  x = dpp_add<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_add<0x4E>(x);   // quad_perm [2, 3, 0, 1]
   return x;
 }
 
@@ -94,7 +117,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
 
   // staging role: channel `lane`, tokens kTPT wave .. kTPT wave + kTPT - 1 of a block (rows
   // past the end reread the last token: staged but never used)
-  float pa[kTPT], pb[kTPT], pw[kTPT], pk[kTPT], pr[kTPT], pv[kTPT];
+  float pa[kTPT], pb[kTPT], pw[kTPT], pk[kTPT], pr[kTPT], pv[kTPT], pd[kTPT];
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int q = 0; q < kTPT; ++q) {
@@ -107,77 +130,144 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
       pv[q] = load1<BF16>(p.v, e);
     }
   };
-  if (T > 0) fetch(0);
-  for (int t0 = 0; t0 < T; t0 += kTB) {
-    const int nb = min(kTB, T - t0);
+  // The fetched block's decays (1 for rows past the end, so that they neither shrink the
+  // block's product nor change the verdict below) and this wave's running product of them.
+  auto decays = [&](int t0) {
+    float c = 1.f;
 #pragma unroll
     for (int q = 0; q < kTPT; ++q) {
-      const int tt = kTPT * wave + q;
-      sm.f[0][tt][lane] = pa[q];
-      sm.f[1][tt][lane] = pb[q];
-      sm.f[2][tt][lane] = decay_of(pw[q]);
-      sm.f[3][tt][lane] = pk[q];
-      sm.f[4][tt][lane] = pr[q];
-      sm.v[tt][lane] = pv[q];
+      pd[q] = t0 + kTPT * wave + q < T ? decay_of(pw[q]) : 1.f;
+      c = q ? c * pd[q] : pd[q];
+    }
+    sm.dp[wave][lane] = c;
+  };
+  if (T > 0) {
+    fetch(0);
+    decays(0);
+  }
+  __syncthreads();  // the first block's decay products
+  for (int t0 = 0; t0 < T; t0 += kTB) {
+    const int nb = min(kTB, T - t0);
+    // Decay products in one fixed order in every wave: `ex` is G before this wave's first
+    // token, `all` the block's product (its smallest G).  A wave's own G continue ex by the
+    // running product of its decays, the value it posted, so a run of decays equal to 1
+    // leaves G bitwise as it was.
+    float ex = 1.f, all = 1.f;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) {
+      if (u == wave) ex = all;
+      all *= sm.dp[u][lane];
+    }
+    const bool frame = __ballot(all < kMinFrame) == 0;  // same verdict in every wave
+    const int t2 = kTPT * wave;
+    if (frame) {
+      float c = 1.f, gprev = ex;
+#pragma unroll
+      for (int q = 0; q < kTPT; ++q) {
+        c = q ? c * pd[q] : pd[q];
+        const float gq = ex * c;
+        const float iq = __builtin_amdgcn_rcpf(gq);
+        sm.f[0][t2 + q][lane] = pa[q] * gprev;
+        sm.f[1][t2 + q][lane] = pb[q] * iq;
+        sm.f[2][t2 + q][lane] = gq;
+        sm.f[3][t2 + q][lane] = pk[q] * iq;
+        sm.f[4][t2 + q][lane] = pr[q] * gq;
+        sm.v[t2 + q][lane] = pv[q];
+        gprev = gq;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kTPT; ++q) {
+        sm.f[0][t2 + q][lane] = pa[q];
+        sm.f[1][t2 + q][lane] = pb[q];
+        sm.f[2][t2 + q][lane] = pd[q];
+        sm.f[3][t2 + q][lane] = pk[q];
+        sm.f[4][t2 + q][lane] = pr[q];
+        sm.v[t2 + q][lane] = pv[q];
+      }
     }
     if (t0 + kTB < T) fetch(t0 + kTB);  // the next block, in flight during this one
     __syncthreads();
 
     // One token step from its staged factors.  The factors of the next token are read
     // into the other register set before this token's arithmetic, so the LDS latency
-    // overlaps it (one wave per SIMD leaves nothing else to hide it).
+    // overlaps it.
     struct Fac {
-      float4 f[5][2];  // a, b, d, k, r of the lane's 8 key rows
+      float4 f[5][2];  // the lane's 8 key rows of the five planes (the frame form skips the decay)
       float v;         // v of the lane's column
     };
-    auto read_fac = [&](Fac &F, int tt) {
+    auto read_fac = [&](Fac &F, int tt, auto is_frame) {
 #pragma unroll
       for (int m = 0; m < 5; ++m) {
+        if (decltype(is_frame)::value && m == 2) continue;
         const float4 *src = reinterpret_cast<const float4 *>(&sm.f[m][tt][8 * g]);
         F.f[m][0] = src[0];
         F.f[m][1] = src[1];
       }
       F.v = sm.v[tt][col];
     };
-    auto step = [&](const Fac &F, int tt) {
-      float fa[8], fb[8], fd[8], fk[8], fr[8];
-      auto unpack = [&](float (&dst)[8], const float4 (&src)[2]) {
-        dst[0] = src[0].x; dst[1] = src[0].y; dst[2] = src[0].z; dst[3] = src[0].w;
-        dst[4] = src[1].x; dst[5] = src[1].y; dst[6] = src[1].z; dst[7] = src[1].w;
-      };
-      unpack(fa, F.f[0]);
+    auto unpack = [](float (&dst)[8], const float4 (&src)[2]) {
+      dst[0] = src[0].x; dst[1] = src[0].y; dst[2] = src[0].z; dst[3] = src[0].w;
+      dst[4] = src[1].x; dst[5] = src[1].y; dst[6] = src[1].z; dst[7] = src[1].w;
+    };
+    // sum over the column's 64 key rows of x[i] * hs[i] (two chains of four per lane)
+    auto dot8 = [&](const float (&x)[8]) {
+      float s0 = x[0] * hs[0], s1 = x[4] * hs[4];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        s0 = fmaf(x[i], hs[i], s0);
+        s1 = fmaf(x[i + 4], hs[i + 4], s1);
+      }
+      return sum8(s0 + s1);
+    };
+    // One token: the update from sa (a^T h before it), then r^T h for this token's output
+    // and the next token's a^T h from the updated state, as two interleaved sums.
+    auto step = [&](const Fac &F, const Fac &Fn, int tt, float sa, auto is_frame) {
+      float fb[8], fk[8], fr[8], fan[8];
       unpack(fb, F.f[1]);
-      unpack(fd, F.f[2]);
       unpack(fk, F.f[3]);
       unpack(fr, F.f[4]);
-      // a^T h over this lane's 8 key rows (two chains of four), then over the column's 8 lanes
-      float sa0 = fa[0] * hs[0], sa1 = fa[4] * hs[4];
+      if constexpr (decltype(is_frame)::value) {
 #pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        sa0 = fmaf(fa[i], hs[i], sa0);
-        sa1 = fmaf(fa[i + 4], hs[i + 4], sa1);
+        for (int i = 0; i < 8; ++i) hs[i] = fmaf(fk[i], F.v, fmaf(fb[i], sa, hs[i]));
+      } else {
+        float fd[8];
+        unpack(fd, F.f[2]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hs[i] = fmaf(fk[i], F.v, fmaf(fb[i], sa, fd[i] * hs[i]));
       }
-      const float sa = sum8(sa0 + sa1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) hs[i] = fmaf(fk[i], F.v, fmaf(fb[i], sa, fd[i] * hs[i]));
-      float y0 = fr[0] * hs[0], y1 = fr[4] * hs[4];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        y0 = fmaf(fr[i], hs[i], y0);
-        y1 = fmaf(fr[i + 4], hs[i + 4], y1);
-      }
-      const float y = sum8(y0 + y1);
+      unpack(fan, Fn.f[0]);
+      const float y = dot8(fr);
+      const float san = dot8(fan);
       if (g == 0) sm.y[tt][col] = y;
+      return san;
     };
-    Fac FA, FB;
-    read_fac(FA, 0);
-    for (int tt = 0; tt < nb; tt += 2) {
-      read_fac(FB, min(tt + 1, kTB - 1));  // past the block's last token: read, never used
-      step(FA, tt);
-      if (tt + 1 < nb) {
-        read_fac(FA, min(tt + 2, kTB - 1));
-        step(FB, tt + 1);
+    auto run_block = [&](auto is_frame) {
+      Fac FA, FB;
+      read_fac(FA, 0, is_frame);
+      float fa0[8];
+      unpack(fa0, FA.f[0]);
+      float sa = dot8(fa0);
+      for (int tt = 0; tt < nb; tt += 2) {
+        read_fac(FB, min(tt + 1, kTB - 1), is_frame);  // past the block's last token: read, never used
+        sa = step(FA, FB, tt, sa, is_frame);
+        if (tt + 1 < nb) {
+          read_fac(FA, min(tt + 2, kTB - 1), is_frame);
+          sa = step(FB, FA, tt + 1, sa, is_frame);
+        }
       }
+    };
+    if (frame) {
+      run_block(std::true_type{});
+      // back from the frame: h = G_last g
+      const float4 *gl = reinterpret_cast<const float4 *>(&sm.f[2][nb - 1][8 * g]);
+      float gv[8];
+      const float4 gsrc[2] = {gl[0], gl[1]};
+      unpack(gv, gsrc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hs[i] *= gv[i];
+    } else {
+      run_block(std::false_type{});
     }
     __syncthreads();
     // store the block's outputs: thread -> (token kTPT wave + q, channel lane), coalesced rows
@@ -191,6 +281,9 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
         else static_cast<float *>(p.y)[e] = yv;
       }
     }
+    // every wave has read this block's decay products (before the barrier above): the next
+    // block's may be written
+    if (t0 + kTB < T) decays(t0 + kTB);
     // the next staging rewrites the token arrays and outputs after this block's reads
     __syncthreads();
   }

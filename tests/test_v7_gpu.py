@@ -125,9 +125,11 @@ def test_v7_bad_state_map_sets_status():
 @pytest.mark.parametrize("side", ["left", "right"])
 def test_v7_padding_by_decay_parameter(side):
     """The page's padding convention for this operator: padded tokens carry w = -1e9 (decay exactly
-    1) and zero r, k, v, a, b.  They leave the state bitwise as it was, so the real tokens' outputs
-    and the final state equal the unpadded call's, bitwise; the padded outputs are zero."""
-    T, P = 40, 9
+    1) and zero r, k, v, a, b, so they leave the state as it was and read zero.  Right padding keeps
+    the real tokens' blocks, so their outputs and the final state equal the unpadded call's bitwise;
+    left padding shifts the 64-token blocks of the prefill kernel's rescaled frame, so the two agree
+    to fp32 rounding.  The padded outputs are zero."""
+    T, P = 150, 9
     inp = wkv7_inputs(2, T, 2, 64, seed=215, init_state=2)
     y, S = _run(inp, state=dev(inp["state"]))
     pad = {n: np.zeros((2, P, 128), dtype=np.uint16) for n in NAMES}
@@ -140,8 +142,27 @@ def test_v7_padding_by_decay_parameter(side):
         real, fill = slice(0, T), slice(T, T + P)
     yp, Sp = _run(padded, state=dev(inp["state"]))
     torch.cuda.synchronize()
-    assert torch.equal(yp[:, real], y) and torch.equal(Sp, S)
+    if side == "right":
+        assert torch.equal(yp[:, real], y) and torch.equal(Sp, S)
+    else:
+        assert_fp32(host(yp[:, real]), host(y), "left padding y")
+        assert_fp32(host(Sp), host(S), "left padding state")
     assert torch.count_nonzero(yp[:, fill]) == 0
+
+
+def test_v7_direct_form_blocks():
+    """Decays strong enough that a 64-token block's decay product falls below 2^-64 (w ~ U(1, 2.5):
+    per-step decays exp(-e^1) .. exp(-e^2.5), in the first 70 tokens) send those blocks through the
+    direct form; the later blocks take the rescaled frame.  The result matches the oracle."""
+    T, S = 200, 70
+    inp = wkv7_inputs(2, T, 2, 64, seed=217, dtype="f32", init_state=2)
+    rng = np.random.default_rng(9)
+    inp["w"][:, :S] = rng.uniform(1.0, 2.5, size=inp["w"][:, :S].shape).astype(np.float32)
+    y, St = _run(inp, state=dev(inp["state"]))
+    torch.cuda.synchronize()
+    yo, So = _oracle(inp, state=inp["state"])
+    assert_fp32(host(y), yo, "direct-form blocks y")
+    assert_fp32(host(St), So, "direct-form blocks state")
 
 
 @pytest.mark.parametrize("T", [1, 130])
