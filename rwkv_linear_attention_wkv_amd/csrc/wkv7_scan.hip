@@ -303,82 +303,99 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
   }
 }
 
-// Calls of at most kShortMax tokens per row (T = 1 decode steps): one wave per (row,
-// head), lane j holding column j of the state (h[0..63][j], 64 registers), so the two
-// sums over key rows are sums inside the lane and the state moves as 256-byte rows.  The
-// key-row factors of a token reach all lanes through LDS as 16-byte broadcasts.  No
-// workgroup barrier beyond the one wave's own.
+// Calls of at most kShortMax tokens per row (T = 1 decode steps): two waves per (row,
+// head), wave c holding value columns 32c .. 32c+31.  Lane l of a wave holds key rows
+// 32 (l / 32) .. +31 of column 32c + l % 32 (32 registers), so each sum over key rows is
+// a sum inside the lane plus one exchange with the lane 32 away, and the state moves
+// as 128-byte row pieces.  Against one wave per (row, head) with whole columns in the
+// lanes, this halves each wave's dependent work and doubles the waves in flight, which
+// shortens the tail after the state stream.  The key-row factors of a token reach the
+// lanes through LDS (the two halves read rows 32 apart: different banks); v is read
+// per lane.
+constexpr int kCW = 32;               // value columns per wave
+constexpr int kLG = 64 / kCW;         // lanes per column (key-row groups)
+constexpr int kRL = kHead / kLG;      // key rows per lane
 template <bool BF16>
-__global__ void __launch_bounds__(64) wkv7_short_kernel(V7Params p) {
+__global__ void __launch_bounds__(64 * kLG) wkv7_short_kernel(V7Params p) {
   __shared__ __align__(16) float sf[5][kHead];  // a, b, d = exp(-exp(w)), k, r of the token
   const int h = blockIdx.x;
   const int unit = blockIdx.y;
-  const int lane = threadIdx.x;  // value column j; key row i for the factors
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int col = kCW * (tid >> 6) + lane % kCW;  // value column j
+  const int r0 = kRL * (lane / kCW);              // first key row of the lane
   const long C = p.tok_stride;
-  const long base = unit * p.row_stride + h * p.head_stride + lane;
+  const long base = unit * p.row_stride + h * p.head_stride;
 
   int row_in = -1;
   if (p.state_in) {
     row_in = p.state_map ? p.state_map[unit] : (p.n_state == 1 ? 0 : unit);
     if (row_in < 0 || row_in >= p.n_state) {
-      if (lane == 0 && p.dev_status) atomicOr(p.dev_status, WKV_DEV_BAD_STATE_MAP);
+      if (tid == 0 && p.dev_status) atomicOr(p.dev_status, WKV_DEV_BAD_STATE_MAP);
       return;
     }
   }
-  float hc[kHead];
+  float hc[kRL];
   if (row_in >= 0) {
-    const float *sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead) + lane;
+    const float *sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead) + r0 * kHead + col;
 #pragma unroll
-    for (int i = 0; i < kHead; ++i) hc[i] = sp[i * kHead];
+    for (int i = 0; i < kRL; ++i) hc[i] = sp[i * kHead];
   } else {
 #pragma unroll
-    for (int i = 0; i < kHead; ++i) hc[i] = 0.f;
+    for (int i = 0; i < kRL; ++i) hc[i] = 0.f;
   }
+  // sum over the column's 64 key rows of x[i] h[i] (four chains in the lane, then the other half)
+  auto colsum = [&](int m) {
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i4 = 0; i4 < kRL / 4; ++i4) {
+      const float4 x = *reinterpret_cast<const float4 *>(&sf[m][r0 + 4 * i4]);
+      s4[0] = fmaf(x.x, hc[4 * i4], s4[0]);
+      s4[1] = fmaf(x.y, hc[4 * i4 + 1], s4[1]);
+      s4[2] = fmaf(x.z, hc[4 * i4 + 2], s4[2]);
+      s4[3] = fmaf(x.w, hc[4 * i4 + 3], s4[3]);
+    }
+    float part = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+#pragma unroll
+    for (int m = kCW; m < 64; m <<= 1) part += __shfl_xor(part, m);  // same sum in every group
+    return part;
+  };
   for (int t = 0; t < p.T; ++t) {
     const long e = base + (long)t * C;
-    sf[0][lane] = load1<BF16>(p.a, e);
-    sf[1][lane] = load1<BF16>(p.b, e);
-    sf[2][lane] = decay_of(load1<BF16>(p.w, e));
-    sf[3][lane] = load1<BF16>(p.k, e);
-    sf[4][lane] = load1<BF16>(p.r, e);
-    const float vj = load1<BF16>(p.v, e);
-    __syncthreads();  // one wave: orders the factors' stores before the broadcast reads
-    // four independent chains per sum (a 64-long dependent chain would expose the FMA latency)
-    float sp4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i4 = 0; i4 < kHead / 4; ++i4) {
-      const float4 a4 = *reinterpret_cast<const float4 *>(&sf[0][4 * i4]);
-      sp4[0] = fmaf(a4.x, hc[4 * i4], sp4[0]);
-      sp4[1] = fmaf(a4.y, hc[4 * i4 + 1], sp4[1]);
-      sp4[2] = fmaf(a4.z, hc[4 * i4 + 2], sp4[2]);
-      sp4[3] = fmaf(a4.w, hc[4 * i4 + 3], sp4[3]);
+    if (tid < kHead) {
+      sf[0][tid] = load1<BF16>(p.a, e + tid);
+      sf[1][tid] = load1<BF16>(p.b, e + tid);
+      sf[2][tid] = decay_of(load1<BF16>(p.w, e + tid));
+      sf[3][tid] = load1<BF16>(p.k, e + tid);
+      sf[4][tid] = load1<BF16>(p.r, e + tid);
     }
-    const float sa = (sp4[0] + sp4[1]) + (sp4[2] + sp4[3]);
-    float yp4[4] = {0.f, 0.f, 0.f, 0.f};
+    const float vj = load1<BF16>(p.v, e + col);
+    __syncthreads();  // the factors' stores before the reads
+    const float sa = colsum(0);
 #pragma unroll
-    for (int i4 = 0; i4 < kHead / 4; ++i4) {
-      const float4 b4 = *reinterpret_cast<const float4 *>(&sf[1][4 * i4]);
-      const float4 d4 = *reinterpret_cast<const float4 *>(&sf[2][4 * i4]);
-      const float4 k4 = *reinterpret_cast<const float4 *>(&sf[3][4 * i4]);
-      const float4 r4 = *reinterpret_cast<const float4 *>(&sf[4][4 * i4]);
+    for (int i4 = 0; i4 < kRL / 4; ++i4) {
+      const float4 b4 = *reinterpret_cast<const float4 *>(&sf[1][r0 + 4 * i4]);
+      const float4 d4 = *reinterpret_cast<const float4 *>(&sf[2][r0 + 4 * i4]);
+      const float4 k4 = *reinterpret_cast<const float4 *>(&sf[3][r0 + 4 * i4]);
       const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
-      const float kk[4] = {k4.x, k4.y, k4.z, k4.w}, rr[4] = {r4.x, r4.y, r4.z, r4.w};
+      const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float &x = hc[4 * i4 + q];
         x = fmaf(kk[q], vj, fmaf(bb[q], sa, dd[q] * x));
-        yp4[q] = fmaf(rr[q], x, yp4[q]);
       }
     }
-    const float y = (yp4[0] + yp4[1]) + (yp4[2] + yp4[3]);
-    if (p.y_bf16) static_cast<uint16_t *>(p.y)[e] = bf16_bits(y);
-    else static_cast<float *>(p.y)[e] = y;
-    __syncthreads();  // the broadcast reads finish before the next token's factors are stored
+    const float y = colsum(4);
+    if (lane < kCW) {
+      if (p.y_bf16) static_cast<uint16_t *>(p.y)[e + col] = bf16_bits(y);
+      else static_cast<float *>(p.y)[e + col] = y;
+    }
+    __syncthreads();  // the reads finish before the next token's factors are stored
   }
   if (p.state_out) {
-    float *sp = p.state_out + ((long)unit * p.H + h) * (kHead * kHead) + lane;
+    float *sp = p.state_out + ((long)unit * p.H + h) * (kHead * kHead) + r0 * kHead + col;
 #pragma unroll
-    for (int i = 0; i < kHead; ++i) sp[i * kHead] = hc[i];
+    for (int i = 0; i < kRL; ++i) sp[i * kHead] = hc[i];
   }
 }
 
@@ -387,8 +404,8 @@ __global__ void __launch_bounds__(64) wkv7_short_kernel(V7Params p) {
 hipError_t launch_wkv7_scan(const V7Params &p, bool bf16, hipStream_t s) {
   dim3 grid(p.H, p.B);
   if (p.T <= kShortMax) {
-    if (bf16) hipLaunchKernelGGL((wkv7_short_kernel<true>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((wkv7_short_kernel<false>), grid, dim3(64), 0, s, p);
+    if (bf16) hipLaunchKernelGGL((wkv7_short_kernel<true>), grid, dim3(64 * kLG), 0, s, p);
+    else hipLaunchKernelGGL((wkv7_short_kernel<false>), grid, dim3(64 * kLG), 0, s, p);
   } else {
     if (bf16) hipLaunchKernelGGL((wkv7_scan_kernel<true>), grid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((wkv7_scan_kernel<false>), grid, dim3(kThreads), 0, s, p);
