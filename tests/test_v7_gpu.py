@@ -52,6 +52,20 @@ def test_v7_small_cases(T, dtype):
     check(host(S0), So0, "v7 zero-state state")
 
 
+@pytest.mark.parametrize("T", [8, 9, 63, 64, 65, 128, 129])
+def test_v7_block_edges(T):
+    """Lengths on either side of the few-token kernel's limit (8 / 9) and of the prefill kernel's
+    64-token blocks (one short block, exact multiples, one token past them), fp32 inputs with a
+    mapped initial state, against the oracle."""
+    inp = wkv7_inputs(3, T, 2, 64, seed=230 + T, dtype="f32", init_state=2)
+    smap = np.array([1, 0, 1], dtype=np.int32)
+    y, S = _run(inp, state=dev(inp["state"]), state_map=dev(smap))
+    torch.cuda.synchronize()
+    yo, So = _oracle(inp, state=inp["state"], state_map=smap)
+    assert_fp32(host(y), yo, f"v7 y T={T}")
+    assert_fp32(host(S), So, f"v7 state T={T}")
+
+
 def test_v7_moderate_full_compare():
     inp = wkv7_inputs(2, 1024, 4, 64, seed=210)
     y, S = _run(inp)
@@ -110,6 +124,24 @@ def test_v7_bf16_out_deterministic_and_empty():
     _, S0 = wkv.wkv7_forward(empty, empty, empty, empty, empty, empty, 2, state=st, state_map=smap)
     torch.cuda.synchronize()
     assert torch.equal(S0, st[[2, 1]])
+
+
+def test_v7_plan_repeats_the_eager_call():
+    """A pre-marshalled plan, called twice on a carried state (two decode steps in place), gives
+    bitwise the outputs and states of two eager calls."""
+    inp = wkv7_inputs(4, 1, 3, 64, seed=218, init_state=4)
+    toks = [dev(inp[n]) for n in NAMES]
+    st_a, st_b = dev(inp["state"]), dev(inp["state"])
+    ys_a = []
+    for _ in range(2):
+        y, _ = wkv.wkv7_forward(*toks, 3, state=st_a, state_out=st_a)
+        ys_a.append(y)
+    plan = wkv.wkv7_plan(*toks, 3, state=st_b, state_out=st_b)
+    ys_b = [plan()[0].clone() for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b)
+    for a, b in zip(ys_a, ys_b):
+        assert torch.equal(a, b)
 
 
 def test_v7_bad_state_map_sets_status():
