@@ -15,8 +15,10 @@
 // SIMD hide each other's dependency chains.  After a token's update the lane forms
 // r^T h (that token's output) and the next token's a^T h from the same state values, as
 // two interleaved sums.  Tokens are staged through LDS in blocks of 64 (8 consecutive
-// tokens per wave), read back as 16-byte broadcasts one token ahead of their use, and
-// the next block's tokens are loaded from HBM while one is computed.
+// tokens per wave) as one record per token, so that a token's reads are one running base
+// address plus immediate offsets; they are read back as 16-byte broadcasts one token
+// ahead of their use, and the next block's tokens are loaded from HBM while one is
+// computed.
 //
 // Rescaled frame.  Inside a block let G_t[i] = d_0[i] ... d_t[i] (from the block start,
 // G_{-1} = 1) and carry g[i][j] = h[i][j] / G_t[i] instead of h.  The recurrence becomes
@@ -50,11 +52,11 @@ constexpr float kMinFrame = 0x1p-64f;            // smallest block decay product
 constexpr int kSP = kHead + 2;  // padded row of the LDS state tile (8-byte aligned rows)
 
 struct __align__(16) V7Smem {
-  // per key row, per token of the block: a, b, d, k, r (direct form) or
-  // a G_{t-1}, b / G_t, G_t, k / G_t, r G_t (frame form)
-  float f[5][kTB][kHead];
-  float v[kTB][kHead];      // per value column
   float y[kTB][kHead];      // outputs of the block
+  // Per token of the block, one 1.5 KiB record: per key row a, b, d, k, r (direct form) or
+  // a G_{t-1}, b / G_t, G_t, k / G_t, r G_t (frame form), then v per value column.  One
+  // record past the block is read ahead at the last token and never used.
+  float tok[kTB + 1][6][kHead];
   float dp[kWaves][kHead];  // per key row: the product of each wave's decays
   float st[kHead][kSP];     // the state on its way in from and out to HBM
 };
@@ -167,23 +169,23 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
         c = q ? c * pd[q] : pd[q];
         const float gq = ex * c;
         const float iq = __builtin_amdgcn_rcpf(gq);
-        sm.f[0][t2 + q][lane] = pa[q] * gprev;
-        sm.f[1][t2 + q][lane] = pb[q] * iq;
-        sm.f[2][t2 + q][lane] = gq;
-        sm.f[3][t2 + q][lane] = pk[q] * iq;
-        sm.f[4][t2 + q][lane] = pr[q] * gq;
-        sm.v[t2 + q][lane] = pv[q];
+        sm.tok[t2 + q][0][lane] = pa[q] * gprev;
+        sm.tok[t2 + q][1][lane] = pb[q] * iq;
+        sm.tok[t2 + q][2][lane] = gq;
+        sm.tok[t2 + q][3][lane] = pk[q] * iq;
+        sm.tok[t2 + q][4][lane] = pr[q] * gq;
+        sm.tok[t2 + q][5][lane] = pv[q];
         gprev = gq;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < kTPT; ++q) {
-        sm.f[0][t2 + q][lane] = pa[q];
-        sm.f[1][t2 + q][lane] = pb[q];
-        sm.f[2][t2 + q][lane] = pd[q];
-        sm.f[3][t2 + q][lane] = pk[q];
-        sm.f[4][t2 + q][lane] = pr[q];
-        sm.v[t2 + q][lane] = pv[q];
+        sm.tok[t2 + q][0][lane] = pa[q];
+        sm.tok[t2 + q][1][lane] = pb[q];
+        sm.tok[t2 + q][2][lane] = pd[q];
+        sm.tok[t2 + q][3][lane] = pk[q];
+        sm.tok[t2 + q][4][lane] = pr[q];
+        sm.tok[t2 + q][5][lane] = pv[q];
       }
     }
     if (t0 + kTB < T) fetch(t0 + kTB);  // the next block, in flight during this one
@@ -200,11 +202,11 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
 #pragma unroll
       for (int m = 0; m < 5; ++m) {
         if (decltype(is_frame)::value && m == 2) continue;
-        const float4 *src = reinterpret_cast<const float4 *>(&sm.f[m][tt][8 * g]);
+        const float4 *src = reinterpret_cast<const float4 *>(&sm.tok[tt][m][8 * g]);
         F.f[m][0] = src[0];
         F.f[m][1] = src[1];
       }
-      F.v = sm.v[tt][col];
+      F.v = sm.tok[tt][5][col];
     };
     auto unpack = [](float (&dst)[8], const float4 (&src)[2]) {
       dst[0] = src[0].x; dst[1] = src[0].y; dst[2] = src[0].z; dst[3] = src[0].w;
@@ -249,10 +251,10 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
       unpack(fa0, FA.f[0]);
       float sa = dot8(fa0);
       for (int tt = 0; tt < nb; tt += 2) {
-        read_fac(FB, min(tt + 1, kTB - 1), is_frame);  // past the block's last token: read, never used
+        read_fac(FB, tt + 1, is_frame);  // past the block's last token: read, never used
         sa = step(FA, FB, tt, sa, is_frame);
         if (tt + 1 < nb) {
-          read_fac(FA, min(tt + 2, kTB - 1), is_frame);
+          read_fac(FA, tt + 2, is_frame);
           sa = step(FB, FA, tt + 1, sa, is_frame);
         }
       }
@@ -260,7 +262,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
     if (frame) {
       run_block(std::true_type{});
       // back from the frame: h = G_last g
-      const float4 *gl = reinterpret_cast<const float4 *>(&sm.f[2][nb - 1][8 * g]);
+      const float4 *gl = reinterpret_cast<const float4 *>(&sm.tok[nb - 1][2][8 * g]);
       float gv[8];
       const float4 gsrc[2] = {gl[0], gl[1]};
       unpack(gv, gsrc);
