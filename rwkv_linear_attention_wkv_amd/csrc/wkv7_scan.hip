@@ -16,9 +16,9 @@
 // r^T h (that token's output) and the next token's a^T h from the same state values, as
 // two interleaved sums.  Tokens are staged through LDS in blocks of 64 (8 consecutive
 // tokens per wave) as one record per token, so that a token's reads are one running base
-// address plus immediate offsets; they are read back as 16-byte broadcasts one token
-// ahead of their use, and the next block's tokens are loaded from HBM while one is
-// computed.
+// address plus immediate offsets; they are read back as 16-byte broadcasts two tokens
+// ahead of their use (three register sets), and the next block's tokens are loaded from
+// HBM while one is computed.
 //
 // Rescaled frame.  Inside a block let G_t[i] = d_0[i] ... d_t[i] (from the block start,
 // G_{-1} = 1) and carry g[i][j] = h[i][j] / G_t[i] instead of h.  The recurrence becomes
@@ -54,9 +54,9 @@ constexpr int kSP = kHead + 2;  // padded row of the LDS state tile (8-byte alig
 struct __align__(16) V7Smem {
   float y[kTB][kHead];      // outputs of the block
   // Per token of the block, one 1.5 KiB record: per key row a, b, d, k, r (direct form) or
-  // a G_{t-1}, b / G_t, G_t, k / G_t, r G_t (frame form), then v per value column.  One
-  // record past the block is read ahead at the last token and never used.
-  float tok[kTB + 1][6][kHead];
+  // a G_{t-1}, b / G_t, G_t, k / G_t, r G_t (frame form), then v per value column.  The two
+  // records past the block are read ahead at the last tokens and never used.
+  float tok[kTB + 2][6][kHead];
   float dp[kWaves][kHead];  // per key row: the product of each wave's decays
   float st[kHead][kSP];     // the state on its way in from and out to HBM
 };
@@ -191,9 +191,9 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
     if (t0 + kTB < T) fetch(t0 + kTB);  // the next block, in flight during this one
     __syncthreads();
 
-    // One token step from its staged factors.  The factors of the next token are read
-    // into the other register set before this token's arithmetic, so the LDS latency
-    // overlaps it.
+    // One token step from its staged factors.  The factors of the token after next are
+    // read into a third register set before this token's arithmetic, so the LDS latency
+    // overlaps two tokens' work.
     struct Fac {
       float4 f[5][2];  // the lane's 8 key rows of the five planes (the frame form skips the decay)
       float v;         // v of the lane's column
@@ -245,17 +245,22 @@ __global__ void __launch_bounds__(kThreads) wkv7_scan_kernel(V7Params p) {
       return san;
     };
     auto run_block = [&](auto is_frame) {
-      Fac FA, FB;
-      read_fac(FA, 0, is_frame);
+      Fac F0, F1, F2;
+      read_fac(F0, 0, is_frame);
+      read_fac(F1, 1, is_frame);
       float fa0[8];
-      unpack(fa0, FA.f[0]);
+      unpack(fa0, F0.f[0]);
       float sa = dot8(fa0);
-      for (int tt = 0; tt < nb; tt += 2) {
-        read_fac(FB, tt + 1, is_frame);  // past the block's last token: read, never used
-        sa = step(FA, FB, tt, sa, is_frame);
+      for (int tt = 0; tt < nb; tt += 3) {
+        read_fac(F2, tt + 2, is_frame);  // past the block's last token: read, never used
+        sa = step(F0, F1, tt, sa, is_frame);
         if (tt + 1 < nb) {
-          read_fac(FA, tt + 2, is_frame);
-          sa = step(FB, FA, tt + 1, sa, is_frame);
+          read_fac(F0, tt + 3, is_frame);
+          sa = step(F1, F2, tt + 1, sa, is_frame);
+          if (tt + 2 < nb) {
+            read_fac(F1, tt + 4, is_frame);
+            sa = step(F2, F0, tt + 2, sa, is_frame);
+          }
         }
       }
     };
