@@ -66,6 +66,18 @@ def test_v7_block_edges(T):
     assert_fp32(host(S), So, f"v7 state T={T}")
 
 
+@pytest.mark.parametrize("B,T,H", [(1, 300, 1), (2, 70, 40)])
+def test_v7_grid_shapes(B, T, H):
+    """A single (row, head) workgroup, and 40 heads (C = 2560), bf16 inputs with zero initial
+    state, against the oracle."""
+    inp = wkv7_inputs(B, T, H, 64, seed=240 + H)
+    y, S = _run(inp)
+    torch.cuda.synchronize()
+    yo, So = _oracle(inp)
+    assert_bf16(host(y), yo, f"v7 y B={B} T={T} H={H}")
+    assert_bf16(host(S), So, f"v7 state B={B} T={T} H={H}")
+
+
 def test_v7_moderate_full_compare():
     inp = wkv7_inputs(2, 1024, 4, 64, seed=210)
     y, S = _run(inp)
