@@ -92,10 +92,9 @@ typedef int32_t wkv_algo;
 #define WKV_DEV_BAD_LENGTH     2  /* varlen length < 0 or > max_len               */
 #define WKV_DEV_TOKEN_OVERFLOW 4  /* varlen: sum of lengths exceeds total_tokens  */
 #define WKV_DEV_DUPLICATE_ROW  8  /* varlen: two slots map to the same state row  */
-#define WKV_DEV_DECAY_RANGE   16  /* chunked: a chunk's accumulated log-decay
-                                     exceeds the kernel's exponent range; that
-                                     head's outputs are not valid — rerun with
-                                     WKV_ALGO_SCAN                                */
+/* Bit 16 is reserved.  Both algorithms take any decay parameter: the chunked
+ * form runs a chunk whose accumulated decay would leave its exponent range
+ * with the direct token recurrence instead, so no decay is a data error. */
 
 /*
  * v4 forward (prefill over T tokens, or T = 1 decode).

@@ -21,7 +21,7 @@ import torch
 
 from . import _native
 from ._native import (WKV_ALGO_AUTO, WKV_ALGO_CHUNKED, WKV_ALGO_SCAN, WKV_DEV_BAD_LENGTH,  # noqa: F401
-                      WKV_DEV_BAD_STATE_MAP, WKV_DEV_DECAY_RANGE, WKV_DEV_DUPLICATE_ROW,
+                      WKV_DEV_BAD_STATE_MAP, WKV_DEV_DUPLICATE_ROW,
                       WKV_DEV_TOKEN_OVERFLOW, WkvError, check)
 
 _lib = _native.load()

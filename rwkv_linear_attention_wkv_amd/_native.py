@@ -15,7 +15,6 @@ WKV_DEV_BAD_STATE_MAP = 1
 WKV_DEV_BAD_LENGTH = 2
 WKV_DEV_TOKEN_OVERFLOW = 4
 WKV_DEV_DUPLICATE_ROW = 8
-WKV_DEV_DECAY_RANGE = 16
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int

@@ -23,9 +23,13 @@
 // mask is bounded by |r k|, since exp(Lam_{t-1} - Lam_s) <= 1 for s < t.
 //
 // Range.  ktil carries exp(-Lam_s) >= 1.  A chunk whose accumulated log2
-// decay in some channel is below -kMaxLog2 sets WKV_DEV_DECAY_RANGE (its
-// outputs are then not trustworthy; the token-sequential scan has no such
-// limit).  Per-step decays exp(-exp(x)) with x <= 0 stay far inside it.
+// decay in some channel is below -kMaxLog2 (or -inf: a decay of exactly 0)
+// would overflow that factor, so it is not run in this form: the consumer
+// waves walk its 64 tokens one at a time with the direct recurrence
+//   y_t[j] = sum_i r_t[i] S[i][j] + bonus_t v_t[j],  S[i][j] <- d_t[i] S[i][j] + k_t[i] v_t[j]
+// in fp32, where every factor is at most 1, and the next chunk continues on
+// the matrix cores from the state this leaves.  Per-step decays exp(-exp(x))
+// with x <= 0 never need it (at most 92 log2 units per chunk).
 //
 // Work decomposition: one 1024-thread workgroup (16 waves) per (batch row,
 // head) walks the chunks in order as a pipeline with one workgroup barrier
@@ -68,20 +72,29 @@ constexpr int kThreads = 1024;  // 16 waves: 8 producers, 8 consumers
 constexpr int RS = 72;          // LDS row stride in bf16 elements (144 bytes)
 constexpr float kMaxLog2 = 100.f;
 
-struct Ops {                      // one chunk's operands, written by the producers
+// A chunk that runs directly keeps the same arrays with other contents:
+// rb_hi = r and rb_lo = k as loaded (bf16), kt_hi / kt_lo = upper / lower 16
+// bits of the fp32 decay d_t[i], all [token][key row].
+struct alignas(16) Ops {          // one chunk's operands, written by the producers
   uint16_t rb_hi[L][RS], rb_lo[L][RS];  // rbar [token][key row]
   uint16_t kt_hi[L][RS], kt_lo[L][RS];  // ktil [token][key row]
   uint16_t vt[kHead][RS];               // V^T  [value col][token]
   float bonus[L];
   float pl[kHead];                      // exp(Lam_{L-1}) per key row
+  int direct;                           // 1: this chunk takes the direct recurrence
 };
+
+constexpr int SFS = 68;  // row stride (floats) of the fp32 state while a chunk runs directly
 
 struct Smem {
   Ops ops[2];
-  uint16_t st_hi[2][kHead][RS], st_lo[2][kHead][RS];  // S^T [value col][key row], ping-pong
+  // S^T [value col][key row] as bf16 hi / lo, ping-pong by chunk parity.  While a
+  // chunk runs directly, the buffer of its own parity holds the fp32 state
+  // [key row][SFS] instead (the output waves then do not read it).
+  uint16_t st[2][2][kHead][RS];
   float2 wtot[2][8][32];                              // log2-decay total of each producer wave, per channel pair
-  int range_bad;
 };
+static_assert(sizeof(float) * kHead * SFS <= sizeof(uint16_t) * 2 * kHead * RS, "fp32 state fits one S^T buffer");
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -129,6 +142,9 @@ __device__ __forceinline__ float xor1(float x) {
 }
 __device__ __forceinline__ float xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float mirror8(float x) {  // lane i of each 8-lane group reads lane 7 - i
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
 }
 template <int M>
 __device__ __forceinline__ float xor_swz(float x) {  // M in {4, 8, 16}
@@ -198,8 +214,8 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       split2(S[4 * q], S[4 * q + 1], h0, l0);
       split2(S[4 * q + 2], S[4 * q + 3], h1, l1);
       const int i0 = 32 * tile_r + 8 * q + 4 * hh;
-      *reinterpret_cast<uint2 *>(&sm.st_hi[buf][jcol][i0]) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2 *>(&sm.st_lo[buf][jcol][i0]) = make_uint2(l0, l1);
+      *reinterpret_cast<uint2 *>(&sm.st[buf][0][jcol][i0]) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(&sm.st[buf][1][jcol][i0]) = make_uint2(l0, l1);
     }
   };
 
@@ -210,8 +226,6 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       for (int e = 0; e < 16; ++e) S[e] = sp[(32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3)) * kHead + jcol];
     }
     if (!y_wave) publish_state(0);
-  } else if (tid == 0) {
-    sm.range_bad = 0;
   }
 
   // ---------------- producer state carried between its two phases
@@ -253,8 +267,9 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       for (int t = 0; t < 4; ++t) ldx[t] = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)roff[t], 0, 0);
     }
   };
-  // carried from phase 1 to phase 2 of a chunk (one pipeline step apart)
-  float cum0[4], cum1[4], lower0 = 0.f, lower1 = 0.f;
+  // carried from phase 1 to phase 2 of a chunk (one pipeline step apart): the
+  // per-token log2 decays of the thread's two channels and the lower half-wave's total
+  float lam0[4], lam1[4], lower0 = 0.f, lower1 = 0.f;
 
   // producer phase 1 of chunk c: decay, in-thread prefix, wave totals; loads chunk c + 1.
   // The tail masks are applied to every chunk: with a single code path the words loaded
@@ -278,7 +293,6 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) nx[t] = 4 * tg + t < nvalid ? nx[t] : 0xff80ff80u;
     }
-    float run0 = 0.f, run1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float x0 = xs.x, x1 = xs.y;
@@ -287,21 +301,19 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
         x1 = __uint_as_float(nx[t] & 0xffff0000u);
       }
       // log2 of the decay exp(-exp(x)) is -exp(x) * log2(e)
-      run0 -= fast_exp(x0) * 1.4426950408889634f;
-      run1 -= fast_exp(x1) * 1.4426950408889634f;
-      cum0[t] = run0;
-      cum1[t] = run1;
+      lam0[t] = -(fast_exp(x0) * 1.4426950408889634f);
+      lam1[t] = -(fast_exp(x1) * 1.4426950408889634f);
     }
-    if (!V6) {  // static decay: tokens past the end must not decay the prefix
+    if (!V6) {  // static decay: tokens past the end do not decay
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const bool past = 4 * tg + t >= nvalid;
-        cum0[t] = past ? (t ? cum0[t - 1] : 0.f) : cum0[t];
-        cum1[t] = past ? (t ? cum1[t - 1] : 0.f) : cum1[t];
+        lam0[t] = past ? 0.f : lam0[t];
+        lam1[t] = past ? 0.f : lam1[t];
       }
-      run0 = cum0[3];
-      run1 = cum1[3];
     }
+    const float run0 = ((lam0[0] + lam0[1]) + lam0[2]) + lam0[3];
+    const float run1 = ((lam1[0] + lam1[1]) + lam1[2]) + lam1[3];
     // next chunk (rows past the end read as zero or belong to the next batch row; masked on use)
     prefetch(c + 1, std::integral_constant<int, S ^ 1>{});
     // wave totals: the upper half-wave (odd token group) adds the lower one's total
@@ -332,25 +344,46 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
         tot1 += wt[q].y;
       }
     }
-    if (pwave == 0) {  // exp(Lam_{L-1}) per key row and the range check
-      if (!hh) *reinterpret_cast<float2 *>(&o.pl[2 * cp]) =
-          make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
-      if (tot0 < -kMaxLog2 || tot1 < -kMaxLog2) sm.range_bad = 1;
-    }
+    // The chunk leaves the exponent range when some channel's total is below
+    // -kMaxLog2 (or is -inf).  Every producer wave sees all 64 channels and the
+    // same totals, so the ballot gives every wave the same answer.
+    const bool direct = __builtin_amdgcn_ballot_w64(!(tot0 >= -kMaxLog2 && tot1 >= -kMaxLog2)) != 0;
+    if (pwave == 0 && lane == 0) o.direct = direct ? 1 : 0;
+    if (!direct) {
+      if (pwave == 0 && !hh)  // exp(Lam_{L-1}) per key row
+        *reinterpret_cast<float2 *>(&o.pl[2 * cp]) =
+            make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
+      float c0 = 0.f, c1 = 0.f;  // in-thread inclusive prefix of the log2 decays
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tau = 4 * tg + t;
-      const float lp0 = t ? pre0 + cum0[t - 1] : pre0, lp1 = t ? pre1 + cum1[t - 1] : pre1;
-      const float la0 = pre0 + cum0[t], la1 = pre1 + cum1[t];
-      const float r0 = bf16_bits_to_f32(rw[t] & 0xffffu), r1 = __uint_as_float(rw[t] & 0xffff0000u);
-      const float k0 = bf16_bits_to_f32(kw[t] & 0xffffu), k1 = __uint_as_float(kw[t] & 0xffff0000u);
-      uint32_t hi, lo;
-      split2(r0 * __builtin_amdgcn_exp2f(lp0), r1 * __builtin_amdgcn_exp2f(lp1), hi, lo);
-      *reinterpret_cast<uint32_t *>(&o.rb_hi[tau][2 * cp]) = hi;
-      *reinterpret_cast<uint32_t *>(&o.rb_lo[tau][2 * cp]) = lo;
-      split2(k0 * __builtin_amdgcn_exp2f(-la0), k1 * __builtin_amdgcn_exp2f(-la1), hi, lo);
-      *reinterpret_cast<uint32_t *>(&o.kt_hi[tau][2 * cp]) = hi;
-      *reinterpret_cast<uint32_t *>(&o.kt_lo[tau][2 * cp]) = lo;
+      for (int t = 0; t < 4; ++t) {
+        const int tau = 4 * tg + t;
+        const float lp0 = t ? pre0 + c0 : pre0, lp1 = t ? pre1 + c1 : pre1;
+        c0 = t ? c0 + lam0[t] : lam0[t];
+        c1 = t ? c1 + lam1[t] : lam1[t];
+        const float la0 = pre0 + c0, la1 = pre1 + c1;
+        const float r0 = bf16_bits_to_f32(rw[t] & 0xffffu), r1 = __uint_as_float(rw[t] & 0xffff0000u);
+        const float k0 = bf16_bits_to_f32(kw[t] & 0xffffu), k1 = __uint_as_float(kw[t] & 0xffff0000u);
+        uint32_t hi, lo;
+        split2(r0 * __builtin_amdgcn_exp2f(lp0), r1 * __builtin_amdgcn_exp2f(lp1), hi, lo);
+        *reinterpret_cast<uint32_t *>(&o.rb_hi[tau][2 * cp]) = hi;
+        *reinterpret_cast<uint32_t *>(&o.rb_lo[tau][2 * cp]) = lo;
+        split2(k0 * __builtin_amdgcn_exp2f(-la0), k1 * __builtin_amdgcn_exp2f(-la1), hi, lo);
+        *reinterpret_cast<uint32_t *>(&o.kt_hi[tau][2 * cp]) = hi;
+        *reinterpret_cast<uint32_t *>(&o.kt_lo[tau][2 * cp]) = lo;
+      }
+    } else {
+      // direct recurrence: r and k as loaded, the per-token decays d = 2^lam split
+      // into their upper and lower 16 bits (the same addresses as the MFMA form)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int tau = 4 * tg + t;
+        const uint32_t d0 = __float_as_uint(__builtin_amdgcn_exp2f(lam0[t]));
+        const uint32_t d1 = __float_as_uint(__builtin_amdgcn_exp2f(lam1[t]));
+        *reinterpret_cast<uint32_t *>(&o.rb_hi[tau][2 * cp]) = rw[t];
+        *reinterpret_cast<uint32_t *>(&o.rb_lo[tau][2 * cp]) = kw[t];
+        *reinterpret_cast<uint32_t *>(&o.kt_hi[tau][2 * cp]) = __builtin_amdgcn_perm(d1, d0, 0x07060302u);
+        *reinterpret_cast<uint32_t *>(&o.kt_lo[tau][2 * cp]) = __builtin_amdgcn_perm(d1, d0, 0x05040100u);
+      }
     }
     // bonus diagonal: the sum over the 32 channel pairs of a token group (one half-wave)
     float bon[4];
@@ -414,8 +447,8 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
           if (DY) {
 #pragma unroll
             for (int tc = 0; tc < 2; ++tc) {
-              sh[tc] = ld8(&sm.st_hi[buf][32 * tc + l32][col_of(0)]);
-              sl[tc] = ld8(&sm.st_lo[buf][32 * tc + l32][col_of(0)]);
+              sh[tc] = ld8(&sm.st[buf][0][32 * tc + l32][col_of(0)]);
+              sl[tc] = ld8(&sm.st[buf][1][32 * tc + l32][col_of(0)]);
             }
           }
           if (DA) {
@@ -436,8 +469,8 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
                 Y[tc] = mfma32(sh[tc], rl, Y[tc]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (q < 3) {
-                  sh[tc] = ld8(&sm.st_hi[buf][32 * tc + l32][nc]);
-                  sl[tc] = ld8(&sm.st_lo[buf][32 * tc + l32][nc]);
+                  sh[tc] = ld8(&sm.st[buf][0][32 * tc + l32][nc]);
+                  sl[tc] = ld8(&sm.st[buf][1][32 * tc + l32][nc]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
               }
@@ -552,10 +585,103 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     }
   };
 
+  // Direct recurrence over chunk c, for chunks outside the exponent range.  The
+  // eight consumer waves share it by value columns: wave cw owns columns
+  // 8cw .. 8cw + 7, and lane 8m + q holds rows 8q .. 8q + 7 of column 8cw + m, so
+  // a token's output is a sum inside the lane and over the column's eight lanes
+  // (three DPP adds), and the state update needs no exchange at all.  The state
+  // moves from the state waves' tile layout to this one and back through the fp32
+  // buffer in st[c & 1], with one extra workgroup barrier each way (every wave of
+  // the workgroup takes them).  Lane q keeps the output of the q-th token of each
+  // group of eight, so a store covers eight tokens.
+  auto direct_chunk = [&](int c) {
+    const Ops &o = sm.ops[c & 1];
+    float *sf = reinterpret_cast<float *>(&sm.st[c & 1][0][0][0]);  // [key row][SFS]
+    const int nvalid = min(L, T - c * L);
+    // Addresses of this rare path are built from an opaque copy of the lane
+    // index, so the compiler does not hoist them out of the chunk loop (where
+    // they would hold registers across the matrix-core path).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int tile_off = (32 * tile_r + 4 * (ln >> 5)) * SFS + 32 * tile_c + (ln & 31);
+    if (!y_wave) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sf[tile_off + (8 * (e >> 2) + (e & 3)) * SFS] = S[e];
+    }
+    __syncthreads();
+    const int q = ln & 7, col = 8 * cw + (ln >> 3);
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = sf[(8 * q + e) * SFS + col];
+    constexpr int ESZ = OUTB ? 2 : 4;
+    char *yb = reinterpret_cast<char *>(p.y) + (base + (long)c * L * ts + col) * ESZ;
+    for (int t0 = 0; t0 < L; t0 += 8) {
+      const uint4 v8 = *reinterpret_cast<const uint4 *>(&o.vt[col][t0]);
+      const float4 b0 = *reinterpret_cast<const float4 *>(&o.bonus[t0]);
+      const float4 b1 = *reinterpret_cast<const float4 *>(&o.bonus[t0 + 4]);
+      const float vv[8] = {bf16_lo(v8.x), bf16_hi(v8.x), bf16_lo(v8.y), bf16_hi(v8.y),
+                           bf16_lo(v8.z), bf16_hi(v8.z), bf16_lo(v8.w), bf16_hi(v8.w)};
+      const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float ykeep = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int t = t0 + tt;
+        const uint4 rr = *reinterpret_cast<const uint4 *>(&o.rb_hi[t][8 * q]);
+        const uint4 kk = *reinterpret_cast<const uint4 *>(&o.rb_lo[t][8 * q]);
+        const uint4 dh = *reinterpret_cast<const uint4 *>(&o.kt_hi[t][8 * q]);
+        const uint4 dl = *reinterpret_cast<const uint4 *>(&o.kt_lo[t][8 * q]);
+        const float r[8] = {bf16_lo(rr.x), bf16_hi(rr.x), bf16_lo(rr.y), bf16_hi(rr.y),
+                            bf16_lo(rr.z), bf16_hi(rr.z), bf16_lo(rr.w), bf16_hi(rr.w)};
+        const float k[8] = {bf16_lo(kk.x), bf16_hi(kk.x), bf16_lo(kk.y), bf16_hi(kk.y),
+                            bf16_lo(kk.z), bf16_hi(kk.z), bf16_lo(kk.w), bf16_hi(kk.w)};
+        float d[8];
+        {
+          const uint32_t hw[4] = {dh.x, dh.y, dh.z, dh.w}, lw[4] = {dl.x, dl.y, dl.z, dl.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            d[2 * m] = __uint_as_float(__builtin_amdgcn_perm(hw[m], lw[m], 0x05040100u));
+            d[2 * m + 1] = __uint_as_float(__builtin_amdgcn_perm(hw[m], lw[m], 0x07060302u));
+          }
+        }
+        float p0 = r[0] * s[0], p1 = r[1] * s[1];
+#pragma unroll
+        for (int e = 2; e < 8; e += 2) {
+          p0 = fmaf(r[e], s[e], p0);
+          p1 = fmaf(r[e + 1], s[e + 1], p1);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = fmaf(d[e], s[e], k[e] * vv[tt]);
+        float part = p0 + p1;
+        part += xor1(part);
+        part += xor2(part);
+        part += mirror8(part);
+        const float yv = fmaf(bb[tt], vv[tt], part);
+        ykeep = q == tt ? yv : ykeep;
+      }
+      if (t0 + q < nvalid) {
+        char *yp = yb + (long)(t0 + q) * ts * ESZ;
+        if constexpr (OUTB)
+          *reinterpret_cast<uint16_t *>(yp) = bf16_bits(ykeep);
+        else
+          *reinterpret_cast<float *>(yp) = ykeep;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sf[(8 * q + e) * SFS + col] = s[e];
+    __syncthreads();
+    if (!y_wave) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[e] = sf[tile_off + (8 * (e >> 2) + (e & 3)) * SFS];
+      publish_state((c & 1) ^ 1);
+    }
+  };
+  // wave-uniform: does chunk c take the direct recurrence?
+  auto is_direct = [&](int c) { return __builtin_amdgcn_readfirstlane(sm.ops[c & 1].direct) != 0; };
+
   // Step i: producers finish chunk i + 1 and start chunk i + 2 while the
   // consumers process chunk i.  Producers, output waves and state waves run
   // separate loops (so each keeps only its own registers live) with one
-  // workgroup barrier per step.
+  // workgroup barrier per step, plus two when chunk i runs directly.
   if (producer) {
     // step i works on chunks i + 1 (register set (i + 1) & 1) and i + 2 (set i & 1);
     // the loop is unrolled by two so that the sets are fixed in each copy
@@ -567,27 +693,40 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
     prefetch(0, std::integral_constant<int, 0>{});
     // the producers' vector-ALU chain is the longest per step: let them issue first
     __builtin_amdgcn_s_setprio(2);
+    auto direct_barriers = [&](int i) {
+      if (i >= 0 && is_direct(i)) {
+        __syncthreads();
+        __syncthreads();
+      }
+    };
     for (int i = -2; i < nchunks; i += 2) {
       step(i, std::integral_constant<int, 0>{});
+      direct_barriers(i);
       __syncthreads();
       if (i + 1 < nchunks) {
         step(i + 1, std::integral_constant<int, 1>{});
+        direct_barriers(i + 1);
         __syncthreads();
       }
     }
   } else if (y_wave) {
     for (int i = -2; i < nchunks; ++i) {
-      if (i >= 0) consume(i);
+      if (i >= 0) {
+        if (is_direct(i)) direct_chunk(i);
+        else consume(i);
+      }
       __syncthreads();
     }
   } else {
     for (int i = -2; i < nchunks; ++i) {
-      if (i >= 0) consume(i);
+      if (i >= 0) {
+        if (is_direct(i)) direct_chunk(i);
+        else consume(i);
+      }
       __syncthreads();
     }
   }
 
-  if (tid == 0 && sm.range_bad && p.dev_status) atomicOr(p.dev_status, WKV_DEV_DECAY_RANGE);
   if (!producer && !y_wave && p.state_out) {
     float *sp = p.state_out + ((long)b * p.H + h) * (kHead * kHead);
 #pragma unroll

@@ -79,23 +79,16 @@ def test_backward_zero_state_and_decay_extremes():
         _check(got, (dr, dk, dv, dx, du, dS), f"x in {x_range}")
 
 
-def test_backward_full_shape_sampled():
-    """B=8 T=4096 H=32 N=64 (the headline forward shape), checked on sampled (row, head) units."""
+def test_backward_full_shape():
+    """B=8 T=4096 H=32 N=64 (the headline forward shape): every (row, head) unit of every
+    gradient, du included, against the oracle."""
     inp = wkv6_inputs(8, 4096, 32, 64, seed=0)
     up = wkv6_upstream(8, 4096, 32, 64, seed=1)
     got = _gpu(inp, up)
     torch.cuda.synchronize()
-    units = [(0, 0), (3, 17), (7, 31)]
-    dr, dk, dv, dx, du, du_rows, dS = oracle.wkv6_backward(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], 32,
-                                                           64, up["dy"], d_state_out=up["d_state"], units=units)
-    g = [host(t) for t in got[:4]]
-    for b, h in units:
-        sl = (b, slice(None), slice(h * 64, (h + 1) * 64))
-        for name, a, o in zip(("dr", "dk", "dv", "dw"), g, (dr, dk, dv, dx)):
-            e = fp32_relerr(a[sl], o[sl])
-            assert e <= (DW_REL if name == "dw" else GRAD_REL), f"unit {(b, h)} {name}: {e:.3e}"
-        e = fp32_relerr(host(got[5])[b, h], dS[b, h])
-        assert e <= GRAD_REL, f"unit {(b, h)} d_state: {e:.3e}"
+    ref = oracle.wkv6_backward(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], 32, 64, up["dy"],
+                               d_state_out=up["d_state"])
+    _check(got, (*ref[:5], ref[6]), "B=8 T=4096 H=32")
 
 
 def test_backward_deterministic_and_empty():

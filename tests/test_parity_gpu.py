@@ -3,8 +3,8 @@
 Workloads (seeded, synthetic):
   v4  B=1 T=64 C=32 fp32, zero state (small) and B=8 T=1024 C=2048 fp32 with
       the sigmoid(r) gate plus one T=1 decode step carrying (a, b, p);
-  v5  B=8 T=4096 H=32 N=64 bf16 (sampled heads) plus small ragged cases;
-  v6  B=4 T=4096 H=40 N=64 and B=8 T=4096 H=32 N=64 bf16 (sampled heads),
+  v5  B=8 T=4096 H=32 N=64 bf16 (every unit) plus small ragged cases;
+  v6  B=4 T=4096 H=40 N=64 and B=8 T=4096 H=32 N=64 bf16 (every unit),
       plus small cases covering ragged tails, T=1, shared / mapped / in-place
       states and fp32 inputs.
 Tolerances: fp32 inputs max error relative to max(|o|, rms(o)) <= 2e-5;
@@ -106,35 +106,17 @@ def _oracle56(inp, state=None, state_map=None, units=None):
                         state=state, state_map=state_map, units=units)
 
 
-def _sampled_units(B, H, n, seed):
-    rng = np.random.default_rng(seed)
-    picks = {(0, 0), (B - 1, H - 1)}
-    while len(picks) < n:
-        picks.add((int(rng.integers(B)), int(rng.integers(H))))
-    return sorted(picks)
-
-
-def _compare_units(y, S, yo, So, units, N, what):
-    yh = host(y)
-    Sh = host(S)
-    ys = np.stack([yh[b, :, h * N:(h + 1) * N] for b, h in units])
-    yos = np.stack([yo[b, :, h * N:(h + 1) * N] for b, h in units])
-    Ss = np.stack([Sh[b, h] for b, h in units])
-    Sos = np.stack([So[b, h] for b, h in units])
-    assert_bf16(ys, yos, what + " y")
-    assert_bf16(Ss, Sos, what + " state")
-
-
 # ------------------------------------------------------------------ v5
 
 @pytest.mark.parametrize("algo", ALGOS)
-def test_v5_full_config_sampled(algo):
+def test_v5_full_config(algo):
+    """B=8 T=4096 H=32: every (row, head) unit against the oracle."""
     inp = wkv5_inputs(8, 4096, 32, 64, seed=0)
     y, S = _run56(5, inp, algo)
     torch.cuda.synchronize()
-    units = _sampled_units(8, 32, 6, seed=1)
-    yo, So = _oracle56(inp, units=units)
-    _compare_units(y, S, yo, So, units, 64, f"v5 C2 {algo}")
+    yo, So = _oracle56(inp)
+    assert_bf16(host(y), yo, f"v5 B=8 T=4096 H=32 {algo} y")
+    assert_bf16(host(S), So, f"v5 B=8 T=4096 H=32 {algo} state")
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -153,13 +135,14 @@ def test_v5_small_mapped_state(algo, T):
 
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("B,H", [(4, 40), (8, 32)])
-def test_v6_full_config_sampled(algo, B, H):
+def test_v6_full_config(algo, B, H):
+    """B=4 H=40 and B=8 H=32 at T=4096: every (row, head) unit against the oracle."""
     inp = wkv6_inputs(B, 4096, H, 64, seed=0)
     y, S = _run56(6, inp, algo)
     torch.cuda.synchronize()
-    units = _sampled_units(B, H, 6, seed=2)
-    yo, So = _oracle56(inp, units=units)
-    _compare_units(y, S, yo, So, units, 64, f"v6 B={B} H={H} {algo}")
+    yo, So = _oracle56(inp)
+    assert_bf16(host(y), yo, f"v6 B={B} H={H} {algo} y")
+    assert_bf16(host(S), So, f"v6 B={B} H={H} {algo} state")
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -227,10 +210,12 @@ def test_v6_bad_state_map_sets_status_and_skips():
     assert torch.isnan(y[1]).all() and not torch.isnan(y[0]).any()
 
 
-def test_v6_deterministic():
-    inp = wkv6_inputs(2, 500, 4, 64, seed=9)
-    ya, Sa = _run56(6, inp, "scan")
-    yb, Sb = _run56(6, inp, "scan")
+@pytest.mark.parametrize("algo", ALGOS)
+def test_v6_deterministic(algo):
+    """Two runs on the same inputs are bitwise equal (fixed-order sums, no atomics)."""
+    inp = wkv6_inputs(2, 500, 4, 64, seed=9, init_state=2)
+    ya, Sa = _run56(6, inp, algo, state=dev(inp["state"]))
+    yb, Sb = _run56(6, inp, algo, state=dev(inp["state"]))
     torch.cuda.synchronize()
     assert torch.equal(ya, yb) and torch.equal(Sa, Sb)
 
