@@ -208,6 +208,11 @@ WKV_API wkv_status wkv6_forward_ex(int B, int T, int H, int N,
  *                may equal state_in (the usual in-place serving loop)
  *   state_map    [num_slots] int32 DEVICE or NULL (identity; then
  *                n_state >= num_slots).  Entries must be distinct.
+ * A length below 0 or above max_len in any slot sets WKV_DEV_BAD_LENGTH and
+ * rejects every slot of the call (the offsets of the slots after it are
+ * meaningless); offsets are summed in 64 bits, so lengths whose sum passes
+ * total_tokens set WKV_DEV_TOKEN_OVERFLOW for the slots they push past it.
+ * A rejected slot writes neither y nor its state row.
  * N must be 64.
  */
 WKV_API wkv_status wkv6_forward_varlen(int num_slots, int H, int N,
@@ -245,6 +250,9 @@ WKV_API wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N,
  *   d_state_in   [B,H,N,N] fp32 or NULL: gradient with respect to the initial
  *                state row b started from (rows that share a state_in row are
  *                not summed: the caller adds them)
+ * A batch row whose state_map entry is outside [0, n_state) sets
+ * WKV_DEV_BAD_STATE_MAP; its rows of dr, dk, dv, dw and d_state_in are not
+ * written, its du_rows row is zero, and du sums the other rows.
  * All pointers are device pointers owned by the caller; the library
  * allocates nothing.  Outputs are written, not accumulated.  Three
  * token-sequential sweeps plus a small reduction are enqueued on `stream`.

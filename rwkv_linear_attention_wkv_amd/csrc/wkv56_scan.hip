@@ -54,6 +54,7 @@ struct __align__(16) ScanSmem {
   float dend[kHead];             // decay product of the block per key row
   float tot[kWaves][kHead];      // log2 decay of each staging wave's tokens
   float bon[kTB];                // r . (u * k) per token
+  unsigned long long off_sum;  // varlen: 64-bit sum of the earlier slots' lengths
   int meta[3];
   int frame;                     // 1: the current block takes the direct form
 };
@@ -86,26 +87,31 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
 
   if constexpr (VARLEN) {
     // Offset of this slot = sum of earlier lengths; validate the slot.
-    if (tid == 0) { s_meta[0] = 0; s_meta[1] = 0; s_meta[2] = 0; }
+    // The sum is 64-bit (65535 slots of up to 2^31 - 1 tokens cannot wrap it), and
+    // one invalid length anywhere makes every slot's offset meaningless, so every
+    // slot is then rejected.
+    if (tid == 0) { sm.off_sum = 0ull; s_meta[1] = 0; s_meta[2] = 0; }
     __syncthreads();
     const int my_row = p.state_map ? p.state_map[unit] : unit;
-    int sum = 0, bad = 0, dup = 0;
+    long sum = 0;
+    int bad = 0, dup = 0;
     for (int i = tid; i < p.units; i += kThreads) {
       const int L = p.lengths[i];
-      if (i < unit) { sum += L; bad |= (L < 0); }
+      if (i < unit) sum += L;
+      bad |= (L < 0) | (L > p.max_len);
       if (p.state_map && i != unit && p.state_map[i] == my_row) dup = 1;
     }
-    if (sum) atomicAdd(&s_meta[0], sum);
+    if (sum) atomicAdd(&sm.off_sum, (unsigned long long)sum);
     if (bad) atomicOr(&s_meta[1], 1);
     if (dup) atomicOr(&s_meta[2], 1);
     __syncthreads();
-    const int off = s_meta[0];
+    const long off = (long)sm.off_sum;
     const int my_len = p.lengths[unit];
     int status = 0;
     if (my_len < 0 || my_len > p.max_len || s_meta[1]) status |= WKV_DEV_BAD_LENGTH;
     if (my_row < 0 || my_row >= p.n_state) status |= WKV_DEV_BAD_STATE_MAP;
     if (s_meta[2]) status |= WKV_DEV_DUPLICATE_ROW;
-    if (!(status & WKV_DEV_BAD_LENGTH) && (long)off + my_len > (long)p.total_tokens)
+    if (!(status & WKV_DEV_BAD_LENGTH) && off + my_len > (long)p.total_tokens)
       status |= WKV_DEV_TOKEN_OVERFLOW;
     if (status) {
       if (tid == 0 && p.dev_status) atomicOr(p.dev_status, status);

@@ -108,13 +108,22 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
 #pragma unroll
   for (int a = 0; a < 4; ++a) X[a][0] = X[a][1] = 0.f;
   const long head_off = (long)h * kHead * kHead;
+  // A batch row whose state_map entry is out of range is skipped by all three sweeps
+  // alike (its token and state gradients are not written), and its share of du is
+  // zero, so du still sums the other rows.
+  if (p.state_in) {
+    const int row_in = p.state_map ? p.state_map[b] : (p.n_state == 1 ? 0 : b);
+    if (row_in < 0 || row_in >= p.n_state) {
+      if (MODE == TFWD) {
+        if (tid == 0 && p.dev_status) atomicOr(p.dev_status, WKV_DEV_BAD_STATE_MAP);
+        if (wave == 0 && p.du_rows) p.du_rows[(long)b * C + h * kHead + lane] = 0.f;
+      }
+      return;
+    }
+  }
   if (MODE == TFWD) {
     if (p.state_in) {
       const int row_in = p.state_map ? p.state_map[b] : (p.n_state == 1 ? 0 : b);
-      if (row_in < 0 || row_in >= p.n_state) {
-        if (tid == 0 && p.dev_status) atomicOr(p.dev_status, WKV_DEV_BAD_STATE_MAP);
-        return;
-      }
       const float *s0 = p.state_in + (long)row_in * p.H * kHead * kHead + head_off;
 #pragma unroll
       for (int a = 0; a < 4; ++a)

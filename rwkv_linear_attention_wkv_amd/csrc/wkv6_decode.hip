@@ -21,7 +21,7 @@
 namespace wkv {
 namespace {
 
-__device__ __forceinline__ int wave_sum_i(int x) {
+__device__ __forceinline__ long wave_sum_l(long x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
   return x;
@@ -43,12 +43,16 @@ __global__ void __launch_bounds__(64) wkv6_varlen_short_kernel(ScanParams p) {
   const int my_row = p.state_map ? p.state_map[unit] : unit;
   // the other slots' lengths and rows (64 per pass) first, then the state column of the
   // (clamped) row, so that waiting for the former does not wait for the latter
-  int sum = 0, bad = 0, dup = 0;
+  // 64-bit offset sum (65535 slots of up to 2^31 - 1 tokens cannot wrap it); one
+  // invalid length anywhere rejects every slot, whose offsets it makes meaningless
+  long sum = 0;
+  int bad = 0, dup = 0;
   {
     const bool in = lane < p.units;
     const int L = in ? p.lengths[lane] : 0;
     const int m = (p.state_map && in) ? p.state_map[lane] : 0;
-    if (lane < unit) { sum = L; bad = L < 0; }
+    if (lane < unit) sum = L;
+    bad = (L < 0) | (L > p.max_len);
     dup = p.state_map && in && lane != unit && m == my_row;
   }
   const int row_c = min(max(my_row, 0), p.n_state - 1);
@@ -60,16 +64,17 @@ __global__ void __launch_bounds__(64) wkv6_varlen_short_kernel(ScanParams p) {
   }
   for (int i = lane + 64; i < p.units; i += 64) {
     const int L = p.lengths[i];
-    if (i < unit) { sum += L; bad |= (L < 0); }
+    if (i < unit) sum += L;
+    bad |= (L < 0) | (L > p.max_len);
     if (p.state_map && i != unit && p.state_map[i] == my_row) dup = 1;
   }
-  const int off = wave_sum_i(sum);
+  const long off = wave_sum_l(sum);
   const bool any_bad = __any(bad), any_dup = __any(dup);
   int status = 0;
   if (my_len < 0 || my_len > p.max_len || any_bad) status |= WKV_DEV_BAD_LENGTH;
   if (my_row < 0 || my_row >= p.n_state) status |= WKV_DEV_BAD_STATE_MAP;
   if (any_dup) status |= WKV_DEV_DUPLICATE_ROW;
-  if (!(status & WKV_DEV_BAD_LENGTH) && (long)off + my_len > (long)p.total_tokens)
+  if (!(status & WKV_DEV_BAD_LENGTH) && off + my_len > (long)p.total_tokens)
     status |= WKV_DEV_TOKEN_OVERFLOW;
   if (status) {
     if (lane == 0 && p.dev_status) atomicOr(p.dev_status, status);

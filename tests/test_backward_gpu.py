@@ -68,6 +68,26 @@ def test_backward_no_state_gradient_and_mapped_state():
     _check(got, (dr, dk, dv, dx, du, dS), "mapped")
 
 
+def test_backward_bad_state_map_row_is_skipped():
+    """A state_map entry out of range sets the status bit; that batch row's gradients are not
+    written, and du sums the other rows only (its share is zero), matching the oracle run on the
+    valid rows."""
+    inp = wkv6_inputs(3, 70, 2, 64, seed=15, init_state=2)
+    up = wkv6_upstream(3, 70, 2, 64, seed=16, with_state=False)
+    smap = np.array([1, 7, 0], dtype=np.int32)
+    args = [dev(inp[n]) for n in ("r", "k", "v", "x")] + [dev(inp["u"]), 2]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = wkv.wkv6_backward(*args, dev(up["dy"]), state=dev(inp["state"]), state_map=dev(smap),
+                            dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & wkv.WKV_DEV_BAD_STATE_MAP
+    good = [0, 2]
+    sub = {n: inp[n][good] for n in ("r", "k", "v", "x")}
+    dr, dk, dv, dx, du, _, dS = oracle.wkv6_backward(sub["r"], sub["k"], sub["v"], sub["x"], inp["u"], 2, 64,
+                                                     up["dy"][good], state=inp["state"], state_map=smap[good])
+    _check([t[good] for t in got[:4]] + [got[4], got[5][good]], (dr, dk, dv, dx, du, dS), "bad map row skipped")
+
+
 def test_backward_zero_state_and_decay_extremes():
     for x_range in [(-6.0, 2.0), (-20.0, -10.0)]:
         inp = wkv6_inputs(2, 50, 2, 64, seed=9, dtype="f32", x_range=x_range)

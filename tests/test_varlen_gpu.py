@@ -133,6 +133,27 @@ def test_varlen_device_status(case):
         assert not torch.equal(state[1], before[1])
 
 
+@pytest.mark.parametrize("max_len", [8, 2 ** 31 - 1])
+def test_varlen_lengths_past_32_bit_offsets(max_len):
+    """Lengths whose running sum passes 2^31 (the third slot's offset would wrap to -2 in 32-bit
+    arithmetic and point before the arrays): offsets are summed in 64 bits, so every slot is
+    rejected — BAD_LENGTH when a length exceeds max_len (the few-token kernel), TOKEN_OVERFLOW
+    otherwise (the scan kernel) — and neither y nor any state row is written."""
+    H, N = 1, 64
+    lengths = np.array([2 ** 31 - 1, 2 ** 31 - 1, 1], dtype=np.int32)
+    inp = varlen_inputs(3, H, N, seed=53, decode_steps=0, lengths=[2, 3, 1])
+    state = dev(inp["state"])
+    before = state.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.full((6, 64), float("nan"), device="cuda")
+    wkv.wkv6_forward_varlen(dev(lengths), dev(inp["r"]), dev(inp["k"]), dev(inp["v"]), dev(inp["x"]),
+                            dev(inp["u"]), H, state, max_len=max_len, y=y, dev_status=status)
+    torch.cuda.synchronize()
+    flag = wkv.WKV_DEV_BAD_LENGTH if max_len == 8 else wkv.WKV_DEV_TOKEN_OVERFLOW
+    assert int(status.item()) & flag
+    assert torch.isnan(y).all() and torch.equal(state, before)
+
+
 def test_serving_workload_prefill_and_decode():
     S, H, N = 64, 32, 64
     steps = 256
