@@ -268,6 +268,30 @@ WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
                          int32_t *dev_status, void *stream);
 
 /*
+ * v6 backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc): wkv6_backward without the du_rows workspace.  The per-row du
+ * staging lives in a static device array of the library, 1,048,576 floats
+ * (4 MiB) per GPU, held until the process ends, so B*H*N must be at most
+ * 1,048,576 (larger calls return WKV_ERR_INVALID_ARG before anything is
+ * enqueued).  The array's device address is looked up on the first call on
+ * each device (the calling thread's current device must be the stream's).
+ * Nothing is allocated or freed, by the library or any routine it calls.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and give wrong du.  Every other
+ * argument, result and error as wkv6_backward; the results are bitwise those
+ * of wkv6_backward.
+ */
+WKV_API wkv_status wkv6_backward_noalloc(int B, int T, int H, int N,
+                                 const void *r, const void *k, const void *v, const void *w,
+                                 wkv_dtype in_dtype, const float *u, const float *dy,
+                                 const float *state_in, const int32_t *state_map, int n_state,
+                                 const float *state_final, const float *d_state_out,
+                                 float *dr, float *dk, float *dv, float *dw,
+                                 float *du, float *d_state_in,
+                                 int32_t *dev_status, void *stream);
+
+/*
  * v7 forward: the generalized delta rule of the rwkv_ops page's
  * generalized_delta_rule operator (r, w, k, v, a, b of shape [B, T, H, K],
  * initial_state [N, H, K, V]; its single-step rwkv7_op_rnn call is this with

@@ -195,7 +195,7 @@ def wkv6_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y
 
 
 def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_final=None, d_state=None,
-                  return_d_state=True, dev_status=None):
+                  return_d_state=True, dev_status=None, library_scratch=False):
     """Gradients of :func:`wkv6_forward` (same r, k, v, w, u, H, state, state_map).
 
     ``dy`` [B, T, H*N] fp32 is the gradient of y; ``d_state`` [B, H, N, N] fp32
@@ -203,7 +203,10 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
     ``state_final``, the forward call's final state.  Returns ``(dr, dk, dv,
     dw [B, T, H*N], du [H*N], d_state_in [B, H, N, N] or None)`` in fp32;
     ``d_state_in[b]`` is the gradient with respect to the initial state row b
-    started from.
+    started from.  With ``library_scratch`` the call goes to
+    ``wkv6_backward_noalloc``, whose du staging is the library's own device
+    array (B*H*N <= 1,048,576; calls that overlap on one GPU race) instead of a
+    workspace allocated here.
     """
     B, T, C = r.shape
     if C % H:
@@ -227,12 +230,15 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
     f32 = dict(dtype=torch.float32, device=r.device)
     dr, dk, dv, dw = (torch.empty((B, T, C), **f32) for _ in range(4))
     du = torch.empty((C,), **f32)
-    du_rows = torch.empty((B, C), **f32)
     d_state_in = torch.empty((B, H, N, N), **f32) if return_d_state else None
-    check(_lib.wkv6_backward(B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r), _ptr(u), _ptr(dy),
-                             _ptr(state), _ptr(state_map), n_state, _ptr(state_final), _ptr(d_state),
-                             _ptr(dr), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), _ptr(du_rows), _ptr(d_state_in),
-                             _ptr(dev_status), _stream(r)))
+    head = (B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r), _ptr(u), _ptr(dy),
+            _ptr(state), _ptr(state_map), n_state, _ptr(state_final), _ptr(d_state),
+            _ptr(dr), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du))
+    if library_scratch:
+        check(_lib.wkv6_backward_noalloc(*head, _ptr(d_state_in), _ptr(dev_status), _stream(r)))
+    else:
+        du_rows = torch.empty((B, C), **f32)
+        check(_lib.wkv6_backward(*head, _ptr(du_rows), _ptr(d_state_in), _ptr(dev_status), _stream(r)))
     return dr, dk, dv, dw, du, d_state_in
 
 

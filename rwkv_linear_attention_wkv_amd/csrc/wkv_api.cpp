@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "wkv.h"
@@ -86,6 +87,82 @@ wkv_status check_dense56(const char *fn, int B, int T, int H, int N, const void 
       REQUIRE(!state_map && n_state == B, "%s: in-place state needs state_map == NULL and n_state == B", fn);
   }
   return WKV_OK;
+}
+
+// Scratch of wkv6_backward_noalloc: each batch row's share of du, [B, H*N] fp32.
+// Every GPU the library runs on holds its own copy until the process ends.
+constexpr long kNoAllocScratchFloats = 1l << 20;  // 4 MiB: B * H * N <= 1,048,576
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of `scratch` on the current device, looked up once per device.  The
+// array's name in host code is only a host-side stand-in, so kernels get this address.
+wkv_status scratch_address(const char *fn, float **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices the scratch table holds", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(WKV_ERR_DEVICE, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float *>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return WKV_OK;
+}
+
+// Validation and launch of the v6 backward, with du_rows from the caller or the scratch.
+wkv_status backward6(const char *fn, int B, int T, int H, int N, const void *r, const void *k, const void *v,
+                     const void *w, wkv_dtype in_dtype, const float *u, const float *dy, const float *state_in,
+                     const int32_t *state_map, int n_state, const float *state_final, const float *d_state_out,
+                     float *dr, float *dk, float *dv, float *dw, float *du, float *du_rows, bool use_scratch,
+                     float *d_state_in, int32_t *dev_status, void *stream) {
+  wkv_status st = check_dense56(fn, B, T, H, N, r, k, v, w, in_dtype, u, dr, state_in, state_map, n_state,
+                                nullptr, WKV_ALGO_AUTO);
+  if (st != WKV_OK) return st;
+  if (T > 0) {
+    REQUIRE(dy && dk && dv && dw, "%s: dy, dk, dv and dw must be non-NULL", fn);
+    REQUIRE(aligned(dy, 4) && aligned(dk, 16) && aligned(dv, 16) && aligned(dw, 4),
+            "%s: dk and dv must be 16-byte aligned, dy and dw 4-byte aligned", fn);
+  }
+  if (use_scratch) {
+    REQUIRE(u && du, "%s: u and du must be non-NULL", fn);
+    REQUIRE(aligned(du, 4), "%s: du must be 4-byte aligned", fn);
+    REQUIRE((int64_t)B * H * N <= kNoAllocScratchFloats,
+            "%s: B*H*N = %lld exceeds the library's scratch of %ld floats (use wkv6_backward with a du_rows "
+            "workspace)", fn, (long long)B * H * N, kNoAllocScratchFloats);
+  } else {
+    REQUIRE(u && du && du_rows, "%s: u, du and du_rows must be non-NULL", fn);
+    REQUIRE(aligned(du, 4) && aligned(du_rows, 4), "%s: du and du_rows must be 4-byte aligned", fn);
+  }
+  REQUIRE(!d_state_in || aligned(d_state_in, 4), "%s: d_state_in must be 4-byte aligned", fn);
+  if (d_state_out) {
+    REQUIRE(state_final, "%s: state_final (the forward call's final state) is needed with d_state_out", fn);
+    REQUIRE(aligned(d_state_out, 4) && aligned(state_final, 4), "%s: d_state_out and state_final misaligned", fn);
+  }
+  REQUIRE(!dev_status || aligned(dev_status, 4), "%s: dev_status must be 4-byte aligned", fn);
+  if (use_scratch) {
+    st = scratch_address(fn, &du_rows);
+    if (st != WKV_OK) return st;
+  }
+  wkv::BwdParams p{};
+  p.B = B; p.T = T; p.H = H;
+  p.r = r; p.k = k; p.v = v; p.w = w;
+  p.u = u; p.dy = dy;
+  p.state_in = state_in; p.state_map = state_map; p.n_state = n_state;
+  p.state_final = state_final; p.d_state_out = d_state_out;
+  p.dr = dr; p.dk = dk; p.dv = dv; p.dw = dw; p.du = du; p.du_rows = du_rows; p.d_state_in = d_state_in;
+  p.dev_status = dev_status;
+  return launched(wkv::launch_wkv6_backward(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // namespace
@@ -272,32 +349,19 @@ wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *
                          const int32_t *state_map, int n_state, const float *state_final,
                          const float *d_state_out, float *dr, float *dk, float *dv, float *dw, float *du,
                          float *du_rows, float *d_state_in, int32_t *dev_status, void *stream) {
-  const char *fn = "wkv6_backward";
-  wkv_status st = check_dense56(fn, B, T, H, N, r, k, v, w, in_dtype, u, dr, state_in, state_map, n_state,
-                                nullptr, WKV_ALGO_AUTO);
-  if (st != WKV_OK) return st;
-  if (T > 0) {
-    REQUIRE(dy && dk && dv && dw, "%s: dy, dk, dv and dw must be non-NULL", fn);
-    REQUIRE(aligned(dy, 4) && aligned(dk, 16) && aligned(dv, 16) && aligned(dw, 4),
-            "%s: dk and dv must be 16-byte aligned, dy and dw 4-byte aligned", fn);
-  }
-  REQUIRE(u && du && du_rows, "%s: u, du and du_rows must be non-NULL", fn);
-  REQUIRE(aligned(du, 4) && aligned(du_rows, 4), "%s: du and du_rows must be 4-byte aligned", fn);
-  REQUIRE(!d_state_in || aligned(d_state_in, 4), "%s: d_state_in must be 4-byte aligned", fn);
-  if (d_state_out) {
-    REQUIRE(state_final, "%s: state_final (the forward call's final state) is needed with d_state_out", fn);
-    REQUIRE(aligned(d_state_out, 4) && aligned(state_final, 4), "%s: d_state_out and state_final misaligned", fn);
-  }
-  REQUIRE(!dev_status || aligned(dev_status, 4), "%s: dev_status must be 4-byte aligned", fn);
-  wkv::BwdParams p{};
-  p.B = B; p.T = T; p.H = H;
-  p.r = r; p.k = k; p.v = v; p.w = w;
-  p.u = u; p.dy = dy;
-  p.state_in = state_in; p.state_map = state_map; p.n_state = n_state;
-  p.state_final = state_final; p.d_state_out = d_state_out;
-  p.dr = dr; p.dk = dk; p.dv = dv; p.dw = dw; p.du = du; p.du_rows = du_rows; p.d_state_in = d_state_in;
-  p.dev_status = dev_status;
-  return launched(wkv::launch_wkv6_backward(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
+  return backward6("wkv6_backward", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map, n_state,
+                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, dev_status, stream);
+}
+
+wkv_status wkv6_backward_noalloc(int B, int T, int H, int N, const void *r, const void *k, const void *v,
+                                 const void *w, wkv_dtype in_dtype, const float *u, const float *dy,
+                                 const float *state_in, const int32_t *state_map, int n_state,
+                                 const float *state_final, const float *d_state_out, float *dr, float *dk,
+                                 float *dv, float *dw, float *du, float *d_state_in, int32_t *dev_status,
+                                 void *stream) {
+  return backward6("wkv6_backward_noalloc", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map,
+                   n_state, state_final, d_state_out, dr, dk, dv, dw, du, nullptr, true, d_state_in, dev_status,
+                   stream);
 }
 
 wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N, const int32_t *lengths, int max_len,

@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(nat.SIGNATURES)
@@ -45,6 +45,18 @@ def test_status_strings(lib):
     assert lib.wkv_status_string(2) == b"unsupported"
     assert lib.wkv_status_string(3) == b"device error"
     assert lib.wkv_status_string(99) == b"unknown status"
+
+
+def test_noalloc_backward_size_limit(lib):
+    """The allocation-free backward rejects B*H*N beyond its 1,048,576-float scratch before any
+    HIP call; the workspace variant takes the same shape."""
+    E = nat.WKV_ERR_INVALID_ARG
+    args = (1025, 8, 16, 64, P, P, P, P, 1, P, P, None, None, 0, None, None, P, P, P, P, P)
+    assert lib.wkv6_backward_noalloc(*args, None, None, None) == E
+    assert b"scratch" in lib.wkv_last_error()
+    assert lib.wkv6_backward_noalloc(1, 8, 16, 64, P, P, P, P, 1, P, P, None, None, 0, None, None, P, P, P, P,
+                                     None, None, None, None) == E  # du NULL
+    assert lib.wkv6_backward(*args, None, None, None, None) == E  # du_rows NULL: the workspace is required
 
 
 def v6(lib, B=2, T=8, H=2, N=64, r=P, k=P, v=P, w=P, dt=1, u=P, y=P, si=None, sm=None, ns=0, so=None,
