@@ -40,12 +40,13 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TFLOPS = 78.6
 KERNEL_SOURCES = {
     "wkv56_scan_kernel": ["wkv56_scan.hip"],
-    "wkv56_chunked_kernel": ["wkv56_chunked.hip"],
+    "wkv56_chunked_kernel": ["wkv56_chunked.hip", "mfma_ops.hpp"],
     "wkv4_scan_kernel": ["wkv4_scan.hip"],
     "wkv6_varlen_short_kernel": ["wkv6_decode.hip"],
     "wkv6_bwd_sweep_kernel": ["wkv6_backward.hip"],
     "wkv7_scan_kernel": ["wkv7_scan.hip"],
     "wkv7_short_kernel": ["wkv7_scan.hip"],
+    "wkv7_chunked_kernel": ["wkv7_chunked.hip", "mfma_ops.hpp"],
 }
 SHORT_MAX = 8  # varlen calls with max_len up to this run the few-token kernel
 TC = "tokens·channels/s"
@@ -261,8 +262,10 @@ def workload_wkv56(args, version):
 def workload_wkv7(args):
     """v7 generalized delta rule forward (B=8 T=4096 H=32 N=64 by default, bf16 inputs, fp32 y, initial
     and final states; --T 1 --B 64 is a decode step for 64 slots).
-    Bound by the vector ALUs: per state element and token one FMA for a^T h, three ops for the
-    update (decay, b sa, k v) and one FMA for r^T h."""
+    The chunked form (the default for T >= 64) is bound by HBM: 16 B per token and channel (six
+    bf16 inputs, fp32 y) plus the states.  The token-sequential kernel (--algo scan) is bound by
+    the vector ALUs: per state element and token one FMA for a^T h, three ops for the update
+    (decay, b sa, k v) and one FMA for r^T h."""
     import numpy as np
     import torch
     import rwkv_linear_attention_wkv_amd as wkv
@@ -281,7 +284,9 @@ def workload_wkv7(args):
     flops = 2 * 5 * N * tc
 
     # validated and marshalled once, as a decode loop would; every call runs the kernel
-    run = wkv.wkv7_plan(*toks, H, state=S0, y=y, state_out=S)
+    algo = wkv.resolve_algo(7, B, T, H, N, args.algo)
+    run = wkv.wkv7_plan(*toks, H, state=S0, y=y, state_out=S, algo=algo)
+    kernel = ("wkv7_short_kernel" if T <= SHORT_MAX else "wkv7_scan_kernel") if algo == "scan" else "wkv7_chunked_kernel"
 
     def cpu(target_s):
         import oracle
@@ -301,15 +306,17 @@ def workload_wkv7(args):
 
     return {
         "metric": f"WKV7 fwd tokens·channels/s, B={B} T={T} H={H} N={N}",
-        "workload_key": f"wkv7_B{B}_T{T}_H{H}_N{N}_bf16",
+        "workload_key": f"wkv7_{'chunked_' if algo == 'chunked' else ''}B{B}_T{T}_H{H}_N{N}_bf16",
         # calls of at most SHORT_MAX tokens per row run the few-token kernel, bound by streaming the states
-        "launches": [("forward", "wkv7_short_kernel" if T <= SHORT_MAX else "wkv7_scan_kernel", run, alg_bytes, flops)],
+        "launches": [("forward", kernel, run, alg_bytes, flops)],
         "tc": tc,
-        "dtype": "fp32",
-        "compute": "fp32 vector ALU (token-sequential generalized delta rule)",
+        "dtype": "bf16" if algo == "chunked" else "fp32",
+        "compute": ("bf16 MFMA on hi/lo-split operands, fp32 accumulation and fp32 triangular solve"
+                    if algo == "chunked" else "fp32 vector ALU (token-sequential generalized delta rule)"),
         "data": "synthetic (seeded numpy PCG64; bf16 r,w,k,v,a,b with a = -kappa, b = kappa*beta; initial states ~ N(0,0.1))",
         "config": {"workload": f"WKV7 forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
-                   "B": B, "T": T, "H": H, "N": N, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
+                   "parallelism": "single GPU"},
         "cpu": cpu,
     }
 

@@ -308,7 +308,10 @@ WKV_API wkv_status wkv6_backward_noalloc(int B, int T, int H, int N,
  *              result rounded to nearest even)
  *   state_in, state_map, n_state, state_out, dev_status: as wkv6_forward
  *              (states [.., H, N, N] indexed [key][value])
- * N must be 64.  One token-sequential kernel (prefill and T = 1 decode).
+ * N must be 64.  The algorithm is WKV_ALGO_AUTO: the 64-token chunked form on
+ * MFMA for bf16 inputs with T >= 64 (the chunkwise operator the page names
+ * next to the recurrent one), else the token-sequential kernel (prefill and
+ * T = 1 decode).  Both are exact for any decay parameter.
  */
 WKV_API wkv_status wkv7_forward(int B, int T, int H, int N,
                         const void *r, const void *w, const void *k, const void *v,
@@ -316,6 +319,16 @@ WKV_API wkv_status wkv7_forward(int B, int T, int H, int N,
                         void *y, wkv_dtype out_dtype,
                         const float *state_in, const int32_t *state_map, int n_state,
                         float *state_out, int32_t *dev_status, void *stream);
+
+/* wkv7_forward with a choice of algorithm: WKV_ALGO_SCAN (token-sequential),
+ * WKV_ALGO_CHUNKED (64-token chunks on MFMA; bf16 inputs only, else
+ * WKV_ERR_UNSUPPORTED) or WKV_ALGO_AUTO. */
+WKV_API wkv_status wkv7_forward_ex(int B, int T, int H, int N,
+                           const void *r, const void *w, const void *k, const void *v,
+                           const void *a, const void *b, wkv_dtype in_dtype, wkv_layout layout,
+                           void *y, wkv_dtype out_dtype,
+                           const float *state_in, const int32_t *state_map, int n_state,
+                           float *state_out, wkv_algo algo, int32_t *dev_status, void *stream);
 
 /*
  * Host-side token-budget split for the varlen serving loop (HOST arrays).
@@ -328,7 +341,7 @@ WKV_API wkv_status wkv7_forward(int B, int T, int H, int N,
 WKV_API wkv_status wkv_schedule_round_robin(int num_slots, const int32_t *remaining,
                                     int budget, int32_t *take, int32_t *total);
 
-/* Algorithm a v5 (version 5) or v6 (version 6) call of this shape and input
+/* Algorithm a v5, v6 or v7 call (version 5, 6 or 7) of this shape and input
  * dtype runs when it requests `requested` (WKV_ALGO_AUTO: chunked for bf16
  * inputs with T >= 64, else the scan; the chunked form needs bf16 inputs).
  * Pure host function. */

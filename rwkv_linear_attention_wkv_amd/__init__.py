@@ -263,7 +263,7 @@ class Wkv7Plan:
 
 
 def wkv7_plan(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
-              dev_status=None, out_dtype=torch.float32, head_first=False):
+              dev_status=None, out_dtype=torch.float32, head_first=False, algo="auto"):
     """Validate and marshal a v7 call once; see :func:`wkv7_forward` for the arguments."""
     if head_first:
         if r.dim() != 4 or r.shape[1] != H:
@@ -298,22 +298,23 @@ def wkv7_plan(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_
     _dev(dev_status, "dev_status", torch.int32, (1,))
     layout = _native.WKV_LAYOUT_BHTN if head_first else _native.WKV_LAYOUT_BTHN
     args = (B, T, H, N, *(_ptr(t) for _, t in toks), _dtype_code(r), layout, _ptr(y), oc,
-            _ptr(state), _ptr(state_map), n_state, _ptr(state_out), _ptr(dev_status), _stream(r))
-    return Wkv7Plan(_lib.wkv7_forward, args, y, state_out,
+            _ptr(state), _ptr(state_map), n_state, _ptr(state_out), _ALGOS[algo], _ptr(dev_status), _stream(r))
+    return Wkv7Plan(_lib.wkv7_forward_ex, args, y, state_out,
                     tuple(t for _, t in toks) + (y, state, state_map, state_out, dev_status))
 
 
 def wkv7_forward(r, w, k, v, a, b, H, state=None, state_map=None, *, y=None, state_out=None, return_state=True,
-                 dev_status=None, out_dtype=torch.float32, head_first=False):
+                 dev_status=None, out_dtype=torch.float32, head_first=False, algo="auto"):
     """v7 generalized delta rule.  r, w, k, v, a, b: [B, T, H*N] ([B, H, T, N] with ``head_first``),
     one dtype; decay exp(-exp(w)).
 
     ``state``: [n_state, H, N, N] fp32 initial states h[key][value]; ``state_map``: [B] int32.
+    ``algo``: "auto" (chunked for bf16 inputs with T >= 64), "scan" or "chunked".
     Returns ``(y, state_out [B, H, N, N] fp32 or None)``; y has the token layout of r and dtype
     ``out_dtype`` unless given.
     """
     return wkv7_plan(r, w, k, v, a, b, H, state, state_map, y=y, state_out=state_out, return_state=return_state,
-                     dev_status=dev_status, out_dtype=out_dtype, head_first=head_first)()
+                     dev_status=dev_status, out_dtype=out_dtype, head_first=head_first, algo=algo)()
 
 
 class VarlenPlan:
@@ -395,7 +396,7 @@ def schedule_round_robin(remaining, budget):
 
 
 def resolve_algo(version, B, T, H, N, algo="auto", dtype=torch.bfloat16):
-    """Name of the algorithm the library runs for a v5/v6 call of this shape and input dtype."""
+    """Name of the algorithm the library runs for a v5, v6 or v7 call of this shape and input dtype."""
     a = _ALGOS[algo] if isinstance(algo, str) else int(algo)
     d = _native.WKV_BF16 if dtype == torch.bfloat16 else _native.WKV_F32
     code = _lib.wkv_resolve_algo(version, B, T, H, N, d, a)

@@ -79,6 +79,9 @@ struct V7Params {
 // 256-thread token-block kernel.
 hipError_t launch_wkv7_scan(const V7Params &p, bool bf16, hipStream_t s);
 
+// v7 64-token chunked form with the contractions on MFMA (bf16 inputs, dense rows).
+hipError_t launch_wkv7_chunked(const V7Params &p, bool bf16, hipStream_t s);
+
 // v4 channel-wise scan.
 struct V4Params {
   int B, T, C;

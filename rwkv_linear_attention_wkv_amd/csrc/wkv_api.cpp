@@ -186,7 +186,7 @@ const char *wkv_status_string(wkv_status s) {
 wkv_algo wkv_resolve_algo(int version, int B, int T, int H, int N, wkv_dtype in_dtype, wkv_algo requested) {
   (void)B; (void)H; (void)N;
   if (requested == WKV_ALGO_SCAN || requested == WKV_ALGO_CHUNKED) return requested;
-  if ((version != 5 && version != 6) || in_dtype != WKV_BF16) return WKV_ALGO_SCAN;
+  if ((version != 5 && version != 6 && version != 7) || in_dtype != WKV_BF16) return WKV_ALGO_SCAN;
   if ((int64_t)H * N > kChunkedMaxRow) return WKV_ALGO_SCAN;
   // Chunks only pay off once a row holds at least one full chunk.
   return T >= kChunk ? WKV_ALGO_CHUNKED : WKV_ALGO_SCAN;
@@ -292,11 +292,18 @@ wkv_status wkv6_forward(int B, int T, int H, int N, const void *r, const void *k
                  n_state, state_out, algo, dev_status, stream);
 }
 
-wkv_status wkv7_forward(int B, int T, int H, int N, const void *r, const void *w, const void *k, const void *v,
-                        const void *a, const void *b, wkv_dtype in_dtype, wkv_layout layout, void *y,
-                        wkv_dtype out_dtype, const float *state_in, const int32_t *state_map, int n_state,
-                        float *state_out, int32_t *dev_status, void *stream) {
+wkv_status wkv7_forward_ex(int B, int T, int H, int N, const void *r, const void *w, const void *k, const void *v,
+                           const void *a, const void *b, wkv_dtype in_dtype, wkv_layout layout, void *y,
+                           wkv_dtype out_dtype, const float *state_in, const int32_t *state_map, int n_state,
+                           float *state_out, wkv_algo algo, int32_t *dev_status, void *stream) {
   const char *fn = "wkv7_forward";
+  if (algo != WKV_ALGO_AUTO && algo != WKV_ALGO_SCAN && algo != WKV_ALGO_CHUNKED)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: unknown algorithm %d", fn, algo);
+  if (algo == WKV_ALGO_CHUNKED && in_dtype != WKV_BF16)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: the chunked algorithm needs bf16 inputs", fn);
+  if (algo == WKV_ALGO_CHUNKED && (int64_t)H * N > kChunkedMaxRow)
+    return fail(WKV_ERR_UNSUPPORTED, "%s: the chunked algorithm takes at most %d channels per token (H*N=%lld)",
+                fn, kChunkedMaxRow, (long long)H * N);
   REQUIRE(B >= 1 && T >= 0 && H >= 1, "%s: need B >= 1, T >= 0, H >= 1 (got B=%d T=%d H=%d)", fn, B, T, H);
   if (N != wkv::kHeadSize) return fail(WKV_ERR_UNSUPPORTED, "%s: head size N=%d is not supported (only 64)", fn, N);
   if (!dtype_ok(in_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown input dtype %d", fn, in_dtype);
@@ -341,7 +348,18 @@ wkv_status wkv7_forward(int B, int T, int H, int N, const void *r, const void *w
   }
   p.state_in = state_in; p.state_map = state_map; p.n_state = n_state; p.state_out = state_out;
   p.dev_status = dev_status;
-  return launched(wkv::launch_wkv7_scan(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T > 0 && wkv_resolve_algo(7, B, T, H, N, in_dtype, algo) == WKV_ALGO_CHUNKED)
+    return launched(wkv::launch_wkv7_chunked(p, in_dtype == WKV_BF16, s), fn);
+  return launched(wkv::launch_wkv7_scan(p, in_dtype == WKV_BF16, s), fn);
+}
+
+wkv_status wkv7_forward(int B, int T, int H, int N, const void *r, const void *w, const void *k, const void *v,
+                        const void *a, const void *b, wkv_dtype in_dtype, wkv_layout layout, void *y,
+                        wkv_dtype out_dtype, const float *state_in, const int32_t *state_map, int n_state,
+                        float *state_out, int32_t *dev_status, void *stream) {
+  return wkv7_forward_ex(B, T, H, N, r, w, k, v, a, b, in_dtype, layout, y, out_dtype, state_in, state_map,
+                         n_state, state_out, WKV_ALGO_AUTO, dev_status, stream);
 }
 
 wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *k, const void *v, const void *w,

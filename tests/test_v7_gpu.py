@@ -1,4 +1,6 @@
-"""GPU parity of the v7 generalized-delta-rule kernel against the fp64 oracle (through the C ABI).
+"""GPU parity of the v7 generalized-delta-rule kernels against the fp64 oracle (through the C ABI):
+the token-sequential kernel ("scan") and the 64-token chunked form on MFMA ("chunked", the
+default for bf16 inputs with T >= 64).
 
 Inputs (wkv7_inputs, seeded): decay parameter w ~ U(-6, 0) (decay exp(-exp(w))), r, k, v ~ N(0, 0.5), a = -kappa and
 b = kappa * beta with a unit kappa per (token, head) and beta ~ U(0, 1); initial states ~ N(0, 0.1).
@@ -12,7 +14,7 @@ import torch
 import oracle
 import rwkv_linear_attention_wkv_amd as wkv
 from parity import assert_bf16, assert_fp32, dev, host
-from wkv_inputs import bf16_round, wkv7_inputs
+from wkv_inputs import bf16_round, bf16_to_f32, wkv7_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -27,16 +29,18 @@ def _oracle(inp, **kw):
     return oracle.wkv7(*(inp[n] for n in NAMES), inp["H"], inp["N"], **kw)
 
 
-@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (17, "f32"), (130, "bf16"), (200, "f32")])
-def test_v7_small_cases(T, dtype):
+@pytest.mark.parametrize("T,dtype,algo", [(1, "bf16", "auto"), (17, "f32", "auto"), (130, "bf16", "scan"),
+                                          (130, "bf16", "chunked"), (200, "f32", "auto"), (1, "bf16", "chunked"),
+                                          (63, "bf16", "chunked")])
+def test_v7_small_cases(T, dtype, algo):
     inp = wkv7_inputs(2, T, 3, 64, seed=200 + T, dtype=dtype, init_state=3)
     check = assert_fp32 if dtype == "f32" else assert_bf16
     smap = np.array([2, 0], dtype=np.int32)
-    y, S = _run(inp, state=dev(inp["state"]), state_map=dev(smap))
-    y1, S1 = _run(inp, state=dev(inp["state"][:1]))                    # shared row
+    y, S = _run(inp, state=dev(inp["state"]), state_map=dev(smap), algo=algo)
+    y1, S1 = _run(inp, state=dev(inp["state"][:1]), algo=algo)         # shared row
     st = dev(inp["state"][:2])
-    y2, _ = _run(inp, state=st, state_out=st)                          # in place
-    y0, S0 = _run(inp)                                                 # zero state
+    y2, _ = _run(inp, state=st, state_out=st, algo=algo)               # in place
+    y0, S0 = _run(inp, algo=algo)                                      # zero state
     torch.cuda.synchronize()
     yo, So = _oracle(inp, state=inp["state"], state_map=smap)
     check(host(y), yo, "v7 y")
@@ -66,21 +70,23 @@ def test_v7_block_edges(T):
     assert_fp32(host(S), So, f"v7 state T={T}")
 
 
+@pytest.mark.parametrize("algo", ["scan", "chunked"])
 @pytest.mark.parametrize("B,T,H", [(1, 300, 1), (2, 70, 40)])
-def test_v7_grid_shapes(B, T, H):
+def test_v7_grid_shapes(B, T, H, algo):
     """A single (row, head) workgroup, and 40 heads (C = 2560), bf16 inputs with zero initial
     state, against the oracle."""
     inp = wkv7_inputs(B, T, H, 64, seed=240 + H)
-    y, S = _run(inp)
+    y, S = _run(inp, algo=algo)
     torch.cuda.synchronize()
     yo, So = _oracle(inp)
     assert_bf16(host(y), yo, f"v7 y B={B} T={T} H={H}")
     assert_bf16(host(S), So, f"v7 state B={B} T={T} H={H}")
 
 
-def test_v7_moderate_full_compare():
+@pytest.mark.parametrize("algo", ["scan", "chunked"])
+def test_v7_moderate_full_compare(algo):
     inp = wkv7_inputs(2, 1024, 4, 64, seed=210)
-    y, S = _run(inp)
+    y, S = _run(inp, algo=algo)
     torch.cuda.synchronize()
     yo, So = _oracle(inp)
     assert_bf16(host(y), yo, "v7 y T=1024")
@@ -88,15 +94,62 @@ def test_v7_moderate_full_compare():
     assert np.max(np.abs(host(y) - yo)) < 1e-3
 
 
-def test_v7_full_shape():
+@pytest.mark.parametrize("algo", ["scan", "chunked"])
+def test_v7_full_shape(algo):
     """B=8 T=4096 H=32 N=64 bf16 (the bench shape): every (row, head) unit."""
     B, T, H = 8, 4096, 32
     inp = wkv7_inputs(B, T, H, 64, seed=0)
-    y, S = _run(inp)
+    y, S = _run(inp, algo=algo)
     torch.cuda.synchronize()
     yo, So = _oracle(inp)
-    assert_bf16(host(y), yo, "v7 B=8 T=4096 H=32 y")
-    assert_bf16(host(S), So, "v7 B=8 T=4096 H=32 state")
+    assert_bf16(host(y), yo, f"v7 B=8 T=4096 H=32 {algo} y")
+    assert_bf16(host(S), So, f"v7 B=8 T=4096 H=32 {algo} state")
+    assert np.max(np.abs(host(y) - yo)) < 1e-3
+
+
+@pytest.mark.parametrize("T", [64, 65, 127, 128, 129, 191, 200])
+def test_v7_chunked_edges(T):
+    """The chunked form at its 64-token chunk edges (exact multiples, one past, a ragged last
+    chunk), bf16 inputs with a mapped initial state and a bf16 y, against the oracle; the bf16 y
+    is the fp32 y rounded, and the result agrees with the scan."""
+    inp = wkv7_inputs(3, T, 2, 64, seed=250 + T, init_state=2)
+    smap = np.array([1, 0, 1], dtype=np.int32)
+    y, S = _run(inp, state=dev(inp["state"]), state_map=dev(smap), algo="chunked")
+    yb, Sb = _run(inp, state=dev(inp["state"]), state_map=dev(smap), algo="chunked", out_dtype=torch.bfloat16)
+    ys, Ss = _run(inp, state=dev(inp["state"]), state_map=dev(smap), algo="scan")
+    torch.cuda.synchronize()
+    yo, So = _oracle(inp, state=inp["state"], state_map=smap)
+    assert_bf16(host(y), yo, f"chunked y T={T}")
+    assert_bf16(host(S), So, f"chunked state T={T}")
+    assert torch.equal(yb, y.to(torch.bfloat16)) and torch.equal(Sb, S)
+    assert_bf16(host(y), host(ys), f"chunked vs scan y T={T}")
+
+
+@pytest.mark.parametrize("case", ["strong", "mixed"])
+def test_v7_chunked_strong_decays(case):
+    """Decays far past the chunked form's exponent range (w ~ U(1, 4): a per-step decay below
+    exp(-e)) in every chunk, or in one chunk plus a few tokens whose decay is exactly 0 (w = 100):
+    those chunks run the direct recurrence inside the kernel and the result matches the oracle
+    with no status bit set."""
+    T = 200
+    inp = wkv7_inputs(2, T, 2, 64, seed=260, init_state=2)
+    rng = np.random.default_rng(10)
+    w = bf16_to_f32(inp["w"]).copy()
+    if case == "strong":
+        w[:] = rng.uniform(1.0, 4.0, size=w.shape)
+    else:
+        w[:, 64:128] = rng.uniform(1.0, 4.0, size=w[:, 64:128].shape)
+        w[1, 150:153] = 100.0
+    inp["w"] = bf16_round(w)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y, S = _run(inp, state=dev(inp["state"]), algo="chunked", dev_status=st)
+    y2, S2 = _run(inp, state=dev(inp["state"]), algo="chunked")
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(y, y2) and torch.equal(S, S2)
+    yo, So = _oracle(inp, state=inp["state"])
+    assert_bf16(host(y), yo, f"{case}: chunked y")
+    assert_bf16(host(S), So, f"{case}: chunked state")
 
 
 def test_v7_decode_steps_carry_the_state():
@@ -162,16 +215,18 @@ def test_v7_bad_state_map_sets_status():
     assert torch.isnan(y[1]).all() and not torch.isnan(y[0]).any()
 
 
+@pytest.mark.parametrize("algo", ["scan", "chunked"])
 @pytest.mark.parametrize("side", ["left", "right"])
-def test_v7_padding_by_decay_parameter(side):
+def test_v7_padding_by_decay_parameter(side, algo):
     """The page's padding convention for this operator: padded tokens carry w = -1e9 (decay exactly
     1) and zero r, k, v, a, b, so they leave the state as it was and read zero.  Right padding keeps
-    the real tokens' blocks, so their outputs and the final state equal the unpadded call's bitwise;
-    left padding shifts the 64-token blocks of the prefill kernel's rescaled frame, so the two agree
-    to fp32 rounding.  The padded outputs are zero."""
+    the real tokens' blocks (or chunks), so their outputs and the final state equal the unpadded
+    call's bitwise; left padding shifts the 64-token blocks of the scan's rescaled frame (or the
+    chunks of the chunked form), so the two agree to that algorithm's rounding: fp32 for the scan,
+    the bf16-input tolerance for the chunked form.  The padded outputs are zero."""
     T, P = 150, 9
     inp = wkv7_inputs(2, T, 2, 64, seed=215, init_state=2)
-    y, S = _run(inp, state=dev(inp["state"]))
+    y, S = _run(inp, state=dev(inp["state"]), algo=algo)
     pad = {n: np.zeros((2, P, 128), dtype=np.uint16) for n in NAMES}
     pad["w"] = bf16_round(np.full((2, P, 128), -1e9, dtype=np.float32))
     if side == "left":
@@ -180,13 +235,14 @@ def test_v7_padding_by_decay_parameter(side):
     else:
         padded = dict(inp, **{n: np.concatenate([inp[n], pad[n]], axis=1) for n in NAMES})
         real, fill = slice(0, T), slice(T, T + P)
-    yp, Sp = _run(padded, state=dev(inp["state"]))
+    yp, Sp = _run(padded, state=dev(inp["state"]), algo=algo)
     torch.cuda.synchronize()
     if side == "right":
         assert torch.equal(yp[:, real], y) and torch.equal(Sp, S)
     else:
-        assert_fp32(host(yp[:, real]), host(y), "left padding y")
-        assert_fp32(host(Sp), host(S), "left padding state")
+        check = assert_fp32 if algo == "scan" else assert_bf16
+        check(host(yp[:, real]), host(y), "left padding y")
+        check(host(Sp), host(S), "left padding state")
     assert torch.count_nonzero(yp[:, fill]) == 0
 
 
@@ -205,15 +261,15 @@ def test_v7_direct_form_blocks():
     assert_fp32(host(St), So, "direct-form blocks state")
 
 
-@pytest.mark.parametrize("T", [1, 130])
-def test_v7_head_first_is_exact(T):
+@pytest.mark.parametrize("T,algo", [(1, "auto"), (130, "scan"), (130, "chunked")])
+def test_v7_head_first_is_exact(T, algo):
     """Head-first [B, H, T, N] arrays (the operators' head_first flag) give bitwise the token-major
-    results, on the prefill kernel (T = 130) and the few-token kernel (T = 1)."""
+    results, on the prefill kernels (T = 130) and the few-token kernel (T = 1)."""
     B, H = 3, 2
     inp = wkv7_inputs(B, T, H, 64, seed=216 + T, init_state=B)
-    y, S = _run(inp, state=dev(inp["state"]))
+    y, S = _run(inp, state=dev(inp["state"]), algo=algo)
     hf = [dev(np.ascontiguousarray(inp[n].reshape(B, T, H, 64).transpose(0, 2, 1, 3))) for n in NAMES]
-    yh, Sh = wkv.wkv7_forward(*hf, H, state=dev(inp["state"]), head_first=True)
+    yh, Sh = wkv.wkv7_forward(*hf, H, state=dev(inp["state"]), head_first=True, algo=algo)
     torch.cuda.synchronize()
     assert yh.shape == (B, H, T, 64)
     assert torch.equal(yh.permute(0, 2, 1, 3).reshape(B, T, H * 64), y) and torch.equal(Sh, S)
