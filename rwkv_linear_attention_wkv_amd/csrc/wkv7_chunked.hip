@@ -34,18 +34,20 @@
 //   stage   all waves: thread (channel pair cp, token group tg) turns its 4 tokens of the
 //           (one chunk ahead) loaded words into log2 decays, posts its wave's totals,
 //           [barrier] adds the earlier waves' totals and writes Ab, Rb, Bt, Kt as bf16
-//           hi / lo [token][key], V^T [col][token] and the final decay; issues the loads
-//           of the next chunk.  [barrier]
-//   A       waves 0, 1 (token block 0 / 1): Y^T = H0^T Rb^T + V^T Grk^T with the causal
-//           32 x 32 blocks Grk^T = Kt Rb^T formed in registers and used from there (the
-//           accumulator layout is the operand layout, with the token order permuted
-//           alike on the other side); waves 2, 3: RHS^T = H0^T Ab^T + V^T Gak^T to LDS (fp32);
+//           hi / lo [token][key], V^T [col][token] and the final decay; requests the next
+//           chunk's words.  [barrier]
+//   A       waves 0 .. 3 (token block, value-column block): RHS^T = H0^T Ab^T + V^T Gak^T to
+//           LDS (fp32);
 //           waves 4 .. 7 (one 32 x 32 tile of the fp32 state each): H += Kt^T V, and waves
 //           4 .. 6 one 32 x 32 block of M each, to LDS (fp32).  [barrier]
-//   solve   all waves: value column 8w + m, eight lanes (one per residue of the token
-//           index mod 8) hold its rows; each final row is broadcast to them and added to
-//           the later rows; SA^T to LDS as bf16 hi / lo.  [barrier]
-//   C       waves 0, 1: Y^T += SA^T Grb^T (Grb^T = Bt Rb^T formed in registers), then y;
+//   solve   waves 4 .. 7: value column 16 (w - 4) + m, four lanes (one per residue of the
+//           token index mod 4) hold its rows; each final row is broadcast to them and added
+//           to the later rows; SA^T to LDS as bf16 hi / lo.  Meanwhile, on the matrix cores,
+//           waves 0, 1 (token block 0 / 1) form Y^T = H0^T Rb^T + V^T Grk^T, with the causal
+//           32 x 32 blocks Grk^T = Kt Rb^T formed in registers and used from there (the
+//           accumulator layout is the operand layout, with the token order permuted
+//           alike on the other side), and the blocks Grb^T = Bt Rb^T.  [barrier]
+//   C       waves 0, 1: Y^T += SA^T Grb^T, then y;
 //           waves 4 .. 7: H = D_{L-1} (H + Bt^T SA)
 //           and H^T published as bf16 hi / lo for the next chunk; then every wave starts
 //           the next chunk's stage.
@@ -75,30 +77,28 @@ struct alignas(16) Smem7 {
   uint16_t vt[kHead][RS];      // V^T [col][token]
   uint16_t ht[2][kHead][RS];   // H0^T hi / lo [col][key]
   uint16_t sat[2][kHead][RS];  // SA^T hi / lo [col][token]
-  float rhs[L][kHead];         // RHS [token][col]; with mp: the fp32 state of a direct chunk
-  float mp[L][8][8];           // M[8u + p][s] at [s][p][u] (column s of M for the solve)
+  // fp32 rows padded to 68 floats, so that 32 lanes writing 32 consecutive rows spread over
+  // the banks
+  float rhs[L][SFS];           // RHS [token][col]; with mp: the fp32 state of a direct chunk
+  float mp[L][SFS];            // M[4u + p][s] at [s][16 p + u] (column s of M for the solve)
   float pl[kHead];             // 2^P_{L-1} per key row
   float2 wtot[8][32];          // log2-decay total of each wave, per channel pair
   int direct;
 };
-static_assert(sizeof(float) * kHead * SFS <= sizeof(float) * (L * kHead + L * 64), "direct state fits");
+static_assert(sizeof(float) * kHead * SFS <= sizeof(float) * 2 * L * SFS, "direct state fits");
 
-// Lane (lane & ~7) | q to every lane of its group of 8 (LDS swizzle, bit mode: and 0x18,
-// or q).  q must fold to a constant (the switch goes away in unrolled loops).
+// Lane (lane & ~3) | q to the four lanes of its quad (DPP quad permute); q must fold to a
+// constant.
 template <int Q>
-__device__ __forceinline__ float bcast8_c(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x18 | (Q << 5)));
+__device__ __forceinline__ float bcast4_c(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x55 * Q, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float bcast8(float x, int q) {
+__device__ __forceinline__ float bcast4(float x, int q) {
   switch (q) {
-    case 0: return bcast8_c<0>(x);
-    case 1: return bcast8_c<1>(x);
-    case 2: return bcast8_c<2>(x);
-    case 3: return bcast8_c<3>(x);
-    case 4: return bcast8_c<4>(x);
-    case 5: return bcast8_c<5>(x);
-    case 6: return bcast8_c<6>(x);
-    default: return bcast8_c<7>(x);
+    case 0: return bcast4_c<0>(x);
+    case 1: return bcast4_c<1>(x);
+    case 2: return bcast4_c<2>(x);
+    default: return bcast4_c<3>(x);
   }
 }
 
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   const int tile_c = (wave - 4) & 1;         // value-column block
   const int jcol = 32 * tile_c + l32;
   f32x16 H = {};  // rows 32 tile_r + 8 (e/4) + 4 hh + e%4, column jcol
-  auto publish_state = [&]() {
+  auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t h0, l0, h1, l1;
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) roff[t] = (uint32_t)(((4 * tg + t) * ts + 2 * cp) * 2);
   const unsigned long long row_end = (unsigned long long)(base + (long)(T - 1) * ts + kHead) * 2;
-  auto rsrc_at = [&](const void *ptr, unsigned long long off) {
+  auto rsrc_at = [&](const void *ptr, unsigned long long off) __attribute__((always_inline)) {
     const unsigned long long rem = off < row_end ? row_end - off : 0ull;
     const int n = (int)(rem > 0x7fffffffull ? 0x7fffffffull : rem);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(ptr) + off), 0, n,
@@ -170,7 +170,8 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   };
   enum { LR = 0, LW, LK, LV, LA, LB };
   uint32_t ld[6][4];  // words of r, w, k, v, a, b; rows past the end read as zero
-  auto prefetch = [&](int c) {
+  // The next chunk's words are requested as soon as this chunk's have been staged.
+  auto prefetch = [&](int c) __attribute__((always_inline)) {
     const unsigned long long off = (unsigned long long)uniform64((base + (long)c * L * ts) * 2);
     const void *src[6] = {p.r, p.w, p.k, p.v, p.a, p.b};
 #pragma unroll
@@ -183,7 +184,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   float lam0[4], lam1[4], lower0 = 0.f, lower1 = 0.f;
   const int lane_x32 = (lane ^ 32) << 2;
   // stage, first half: log2 decays and the wave totals (tokens past the end do not decay)
-  auto stage1 = [&](int c) {
+  auto stage1 = [&](int c) __attribute__((always_inline)) {
     const int nvalid = min(L, T - c * L);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -198,7 +199,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
     if (hh) sm.wtot[wave][cp] = make_float2(run0 + lower0, run1 + lower1);
   };
   // stage, second half: prefix, operands, V^T; then the next chunk's loads
-  auto stage2 = [&](int c) {
+  auto stage2 = [&](int c) __attribute__((always_inline)) {
     float pre0 = hh ? lower0 : 0.f, pre1 = hh ? lower1 : 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -268,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   // The next step's operands are requested while this step's products issue (one step of
   // lookahead, so the loads of a pass do not all hold registers at once).
   auto mm_keys = [&](f32x16 &acc, const uint16_t *ah, const uint16_t *al, const uint16_t *bh,
-                     const uint16_t *bl) {
+                     const uint16_t *bl) __attribute__((always_inline)) {
     bf16x8 a0 = ld8(ah + 8 * hh), a1 = ld8(al + 8 * hh), b0 = ld8(bh + 8 * hh), b1 = ld8(bl + 8 * hh);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -287,7 +288,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   // (lane t, rows s): A's row is read in the matching token order (slot 8hh + j of K step
   // ks is token 32 sb + 16 ks + 4 hh + 8 (j / 4) + j % 4).  A exact (al == nullptr: two
   // products) or hi / lo (three).
-  auto mm_g = [&](f32x16 &acc, const uint16_t *ah, const uint16_t *al, const f32x16 &g, int sb) {
+  auto mm_g = [&](f32x16 &acc, const uint16_t *ah, const uint16_t *al, const f32x16 &g, int sb) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int s0 = 32 * sb + 16 * ks + 4 * hh;
@@ -299,12 +300,11 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
       acc = mfma32(a0, gh, acc);
       acc = mfma32(a0, gl, acc);
       if (al) acc = mfma32(ld4x2(al + s0, al + s0 + 8), gh, acc);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // G^T block (sb, tb): rows s = 32 sb + .. of plane pair `zs`, columns t = 32 tb + lane of
   // plane pair `xt`, masked to s < t (strict) or s <= t.
-  auto gram_t = [&](int zs, int xt, int sb, int tb, bool strict) {
+  auto gram_t = [&](int zs, int xt, int sb, int tb, bool strict) __attribute__((always_inline)) {
     f32x16 g = {};
     mm_keys(g, &sm.op[zs][32 * sb + l32][0], &sm.op[zs + 1][32 * sb + l32][0], &sm.op[xt][32 * tb + l32][0],
             &sm.op[xt + 1][32 * tb + l32][0]);
@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
     return g;
   };
   // the transposed key-side operand of the state update: A = Z^T (rows key, K = tokens)
-  auto state_update = [&](int zs, const uint16_t (*bh)[RS], const uint16_t (*bl)[RS]) {
+  auto state_update = [&](int zs, const uint16_t (*bh)[RS], const uint16_t (*bl)[RS]) __attribute__((always_inline)) {
     const int g = lane >> 4;
     const int kcol = 32 * tile_r + 16 * (g & 1) + 4 * (lane & 3);
     const int trow0 = 8 * (g >> 1) + ((lane >> 2) & 3);
@@ -332,16 +332,15 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
       H = mfma32(zh, b0, H);
       H = mfma32(zl, b0, H);
       if (bl) H = mfma32(zh, ld8(&bl[jcol][16 * ks + 8 * hh]), H);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  f32x16 Yt[2];  // output waves: the Y^T tiles of their token block (value-column blocks)
+  f32x16 Yt[2], Gb[2];  // output waves: Y^T tiles of their token block, Grb^T blocks
   constexpr int ESZ = OUTB ? 2 : 4;
 
   // ---------------- one MFMA chunk, phases A .. C (each ends at a workgroup barrier)
   // output waves: token block TB (a compile-time constant, so Gb is indexed statically)
-  auto out_a = [&](auto tb_c) {
+  auto out_a = [&](auto tb_c) __attribute__((always_inline)) {
     constexpr int TB = decltype(tb_c)::value;
     const int trow = 32 * TB + l32;
     Yt[0] = Yt[1] = f32x16{};
@@ -356,15 +355,18 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
       for (int tc = 0; tc < 2; ++tc) mm_g(Yt[tc], &sm.vt[32 * tc + l32][0], nullptr, g, sb);
     }
   };
-  auto out_c = [&](auto tb_c, int c) {
+  auto out_b = [&](auto tb_c) __attribute__((always_inline)) {  // while the state waves solve: the Grb^T blocks
+    constexpr int TB = decltype(tb_c)::value;
+#pragma unroll
+    for (int sb = 0; sb <= TB; ++sb) Gb[sb] = gram_t(BT, RB, sb, TB, false);
+  };
+  auto out_c = [&](auto tb_c, int c) __attribute__((always_inline)) {
     constexpr int TB = decltype(tb_c)::value;
     const int trow = 32 * TB + l32;
 #pragma unroll
-    for (int sb = 0; sb <= TB; ++sb) {
-      const f32x16 g = gram_t(BT, RB, sb, TB, false);  // Grb^T block
+    for (int sb = 0; sb <= TB; ++sb)
 #pragma unroll
-      for (int tc = 0; tc < 2; ++tc) mm_g(Yt[tc], &sm.sat[0][32 * tc + l32][0], &sm.sat[1][32 * tc + l32][0], g, sb);
-    }
+      for (int tc = 0; tc < 2; ++tc) mm_g(Yt[tc], &sm.sat[0][32 * tc + l32][0], &sm.sat[1][32 * tc + l32][0], Gb[sb], sb);
     const int nvalid = min(L, T - c * L);
     if (trow < nvalid) {
       char *yrow = reinterpret_cast<char *>(p.y) + (base + (long)(c * L + trow) * ts + 4 * hh) * ESZ;
@@ -382,32 +384,26 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
     }
   };
 
-  auto phase_a = [&](int c) {
-    if (wave == 0) {
-      out_a(std::integral_constant<int, 0>{});
-    } else if (wave == 1) {
-      out_a(std::integral_constant<int, 1>{});
-    } else if (wave < 4) {
-      const int tb = wave - 2;
-      const int trow = 32 * tb + l32;
-      f32x16 R[2] = {f32x16{}, f32x16{}};
+  // RHS^T tile of token block tb = wave & 1, value-column block tc = 1 - (wave >> 1)
+  // (waves 0 .. 3 share the four tiles; a block's Gak^T is formed by both of its waves)
+  auto rhs_a = [&]() __attribute__((always_inline)) {
+    const int tb = wave & 1, tc = 1 - (wave >> 1);
+    const int trow = 32 * tb + l32;
+    f32x16 R = {};
+    mm_keys(R, &sm.ht[0][32 * tc + l32][0], &sm.ht[1][32 * tc + l32][0], &sm.op[AB][trow][0],
+            &sm.op[AB + 1][trow][0]);
+    for (int sb = 0; sb <= tb; ++sb) {
+      const f32x16 g = gram_t(KT, AB, sb, tb, true);
+      mm_g(R, &sm.vt[32 * tc + l32][0], nullptr, g, sb);
+    }
+    // lane (t, hh) holds RHS[t][32 tc + 8m + 4hh + 0..3] in R[4m .. 4m+3]
 #pragma unroll
-      for (int tc = 0; tc < 2; ++tc)
-        mm_keys(R[tc], &sm.ht[0][32 * tc + l32][0], &sm.ht[1][32 * tc + l32][0], &sm.op[AB][trow][0],
-                &sm.op[AB + 1][trow][0]);
-      for (int sb = 0; sb <= tb; ++sb) {
-        const f32x16 g = gram_t(KT, AB, sb, tb, true);
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc) mm_g(R[tc], &sm.vt[32 * tc + l32][0], nullptr, g, sb);
-      }
-      // lane (t, hh) holds RHS[t][32 tc + 8m + 4hh + 0..3] in R[tc][4m .. 4m+3]
-#pragma unroll
-      for (int tc = 0; tc < 2; ++tc)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          *reinterpret_cast<float4 *>(&sm.rhs[trow][32 * tc + 8 * m + 4 * hh]) =
-              make_float4(R[tc][4 * m], R[tc][4 * m + 1], R[tc][4 * m + 2], R[tc][4 * m + 3]);
-    } else {
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<float4 *>(&sm.rhs[trow][32 * tc + 8 * m + 4 * hh]) =
+          make_float4(R[4 * m], R[4 * m + 1], R[4 * m + 2], R[4 * m + 3]);
+  };
+  auto state_a = [&]() __attribute__((always_inline)) {
+    {
       state_update(KT, sm.vt, nullptr);  // H += Kt^T V
       if (wave < 7) {
         // M block (tb, sb) in {(0,0), (1,0), (1,1)}: C = Ab Bt^T, lane s, rows t
@@ -419,47 +415,57 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int t = 32 * tb + 8 * (e >> 2) + 4 * hh + (e & 3);
-          sm.mp[s][4 * hh + (e & 3)][4 * tb + (e >> 2)] = s < t ? mm[e] : 0.f;  // [s][t % 8][t / 8]
+          sm.mp[s][16 * (e & 3) + 8 * tb + 2 * (e >> 2) + hh] = s < t ? mm[e] : 0.f;  // t % 4, t / 4
         }
       }
     }
   };
 
-  // forward substitution (I - M) SA = RHS, right-looking: lane 8m + p of wave w owns
-  // value column 8w + m and the rows t = 8u + p (u = 0..7), which start as RHS; once row s
-  // is final, the lane that owns it hands SA[s] to its column's eight lanes (an LDS-swizzle
-  // broadcast) and each adds M[t][s] SA[s] to its later rows.
-  auto solve = [&]() {
-    const int p = lane & 7;
-    const int col = 8 * wave + (lane >> 3);
-    float R[8];
+  // forward substitution (I - M) SA = RHS on the four state waves, right-looking: lane
+  // 4m + p of state wave sw owns value column 16 sw + m and the rows t = 4u + p
+  // (u = 0..15), which start as RHS; once row s is final, its owner hands SA[s] to the
+  // column's four lanes (one DPP quad broadcast) and each adds M[t][s] SA[s] to its later
+  // rows.  Column s of M is read kPF steps ahead.
+  auto solve = [&]() __attribute__((always_inline)) {
+    const int p = lane & 3;
+    const int col = 16 * (wave - 4) + (lane >> 2);
+    float R[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) R[u] = sm.rhs[8 * u + p][col];
+    for (int u = 0; u < 16; ++u) R[u] = sm.rhs[4 * u + p][col];
+    constexpr int kPF = 2;
+    float4 mq[kPF][4];
+    auto load_col = [&](int s, float4 *dst) __attribute__((always_inline)) {  // rows 4u + p with u >= s / 4
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (4 * g + 3 >= (s >> 2)) dst[g] = *reinterpret_cast<const float4 *>(&sm.mp[s][16 * p + 4 * g]);
+    };
+#pragma unroll
+    for (int s = 0; s < kPF; ++s) load_col(s, mq[s]);
 #pragma unroll
     for (int s = 0; s < L - 1; ++s) {
-      const int us = s >> 3;
-      const float x = bcast8(R[us], s & 7);
-      const float4 m0 = *reinterpret_cast<const float4 *>(&sm.mp[s][p][0]);
-      const float4 m1 = *reinterpret_cast<const float4 *>(&sm.mp[s][p][4]);
-      const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+      const int us = s >> 2;
+      const float x = bcast4(R[us], s & 3);
+      float mv[16];
 #pragma unroll
-      for (int u = us; u < 8; ++u) R[u] = fmaf(mv[u], x, R[u]);
+      for (int g = 0; g < 4; ++g) {
+        mv[4 * g] = mq[s % kPF][g].x; mv[4 * g + 1] = mq[s % kPF][g].y;
+        mv[4 * g + 2] = mq[s % kPF][g].z; mv[4 * g + 3] = mq[s % kPF][g].w;
+      }
+      if (s + kPF < L - 1) load_col(s + kPF, mq[s % kPF]);
+#pragma unroll
+      for (int u = us; u < 16; ++u) R[u] = fmaf(mv[u], x, R[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const float x = R[u];
       const uint16_t hi = bf16_bits(x);
-      sm.sat[0][col][8 * u + p] = hi;
-      sm.sat[1][col][8 * u + p] = bf16_bits(x - __uint_as_float((uint32_t)hi << 16));
+      sm.sat[0][col][4 * u + p] = hi;
+      sm.sat[1][col][4 * u + p] = bf16_bits(x - __uint_as_float((uint32_t)hi << 16));
     }
   };
 
-  auto phase_c = [&](int c) {
-    if (wave == 0) {
-      out_c(std::integral_constant<int, 0>{}, c);
-    } else if (wave == 1) {
-      out_c(std::integral_constant<int, 1>{}, c);
-    } else if (state_wave) {
+  auto state_c = [&]() __attribute__((always_inline)) {
+    {
       state_update(BT, sm.sat[0], sm.sat[1]);  // H += Bt^T SA
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -474,14 +480,14 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   };
 
   // ---------------- a chunk outside the exponent range: the recurrence token by token
-  auto direct_chunk_a = [&]() {  // state waves: tile layout -> fp32 [key][SFS]
+  auto direct_chunk_a = [&]() __attribute__((always_inline)) {  // state waves: tile layout -> fp32 [key][SFS]
     if (state_wave) {
       float *sf = &sm.rhs[0][0];
 #pragma unroll
       for (int e = 0; e < 16; ++e) sf[(32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3)) * SFS + jcol] = H[e];
     }
   };
-  auto direct_chunk_b = [&](int c) {
+  auto direct_chunk_b = [&](int c) __attribute__((always_inline)) {
     float *sf = &sm.rhs[0][0];
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -552,7 +558,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sf[(8 * q + e) * SFS + col] = s[e];
   };
-  auto direct_chunk_c = [&]() {  // state waves: back to the tile layout, publish
+  auto direct_chunk_c = [&]() __attribute__((always_inline)) {  // state waves: back to the tile layout, publish
     if (state_wave) {
       const float *sf = &sm.rhs[0][0];
 #pragma unroll
@@ -561,35 +567,53 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
     }
   };
 
-  // ---------------- chunk loop
-  prefetch(0);
-  stage1(0);
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();  // wave totals posted; the previous chunk's readers are done
-    stage2(c);
-    __syncthreads();  // operands of chunk c in place
-    const bool direct = __builtin_amdgcn_readfirstlane(sm.direct) != 0;
-    if (!direct) {
-      phase_a(c);
-      __syncthreads();
-      solve();
-      __syncthreads();
-      phase_c(c);
-    } else {
-      direct_chunk_a();
-      __syncthreads();
-      direct_chunk_b(c);
-      __syncthreads();
-      direct_chunk_c();
+  // ---------------- chunk loop.  Each role runs its own copy of the loop (the same
+  // barriers in the same order), so each keeps only its own registers live.
+  // ROLE 0 / 1: output waves of token block 0 / 1; 2: RHS waves; 3: state waves.
+  auto run_chunks = [&](auto role_c) __attribute__((always_inline)) {
+    constexpr int ROLE = decltype(role_c)::value;
+    prefetch(0);
+    stage1(0);
+    for (int c = 0; c < nchunks; ++c) {
+      __syncthreads();  // wave totals posted; the previous chunk's readers are done
+      stage2(c);
+      __syncthreads();  // operands of chunk c in place
+      const bool direct = __builtin_amdgcn_readfirstlane(sm.direct) != 0;
+      const bool more = c + 1 < nchunks;
+      if (!direct) {
+        if constexpr (ROLE < 3) rhs_a();
+        else state_a();
+        __syncthreads();
+        if constexpr (ROLE < 2) {
+          out_a(std::integral_constant<int, ROLE>{});
+          out_b(std::integral_constant<int, ROLE>{});
+        } else if constexpr (ROLE == 3) {
+          solve();
+        }
+        __syncthreads();
+        if constexpr (ROLE < 2) out_c(std::integral_constant<int, ROLE>{}, c);
+        else if constexpr (ROLE == 3) state_c();
+      } else {
+        if constexpr (ROLE == 3) direct_chunk_a();
+        __syncthreads();
+        direct_chunk_b(c);
+        __syncthreads();
+        if constexpr (ROLE == 3) direct_chunk_c();
+      }
+      if (more) stage1(c + 1);
     }
-    if (c + 1 < nchunks) stage1(c + 1);
-  }
-
-  if (state_wave && p.state_out) {
-    float *sp = p.state_out + ((long)b * p.H + h) * (kHead * kHead);
+    if constexpr (ROLE == 3) {
+      if (p.state_out) {
+        float *sp = p.state_out + ((long)b * p.H + h) * (kHead * kHead);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sp[(32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3)) * kHead + jcol] = H[e];
-  }
+        for (int e = 0; e < 16; ++e) sp[(32 * tile_r + 8 * (e >> 2) + 4 * hh + (e & 3)) * kHead + jcol] = H[e];
+      }
+    }
+  };
+  if (wave == 0) run_chunks(std::integral_constant<int, 0>{});
+  else if (wave == 1) run_chunks(std::integral_constant<int, 1>{});
+  else if (wave < 4) run_chunks(std::integral_constant<int, 2>{});
+  else run_chunks(std::integral_constant<int, 3>{});
 }
 
 template <bool OUTB>
