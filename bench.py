@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--H", type=int, default=32)
     ap.add_argument("--budget", type=int, default=128, help="serving: tokens per call")
+    ap.add_argument("--budget-mode", default="total", choices=["total", "slot"],
+                    help="serving: the budget is the call's total, split round-robin over the slots "
+                         "(default), or each slot's own limit per call")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
@@ -482,7 +485,10 @@ def _serving_setup(args, decode_only):
         consumed = np.zeros(Sn, dtype=np.int64)
         rows_all = []
         while True:
-            take = wkv.schedule_round_robin(lengths - consumed, args.budget)
+            if args.budget_mode == "slot":  # every slot with tokens left takes up to `budget` of them
+                take = np.minimum(lengths - consumed, args.budget).astype(np.int32)
+            else:
+                take = wkv.schedule_round_robin(lengths - consumed, args.budget)
             if take.sum() == 0:
                 break
             rows = np.concatenate([np.arange(off[s] + consumed[s], off[s] + consumed[s] + take[s])
@@ -501,6 +507,8 @@ def _serving_setup(args, decode_only):
             act = int((take > 0).sum())
 
             run = wkv.varlen_plan(tk, *a, u, H, state, max_len=mx, y=y_pre[sl], dev_status=status)
+            # calls with max_len above SHORT_MAX run the varlen scan kernel, which hands its slots
+            # of at most SHORT_MAX tokens to the few-token form
             kname = "wkv6_varlen_short_kernel" if mx <= SHORT_MAX else "wkv56_scan_kernel"
             launches.append(("prefill", kname, run, 12 * n * C + 2 * act * H * N * N * 4 + 4 * C,
                              2 * 3 * N * n * C))
@@ -591,15 +599,17 @@ def workload_serving(args, decode_only=False):
                "parallelism": "single GPU"}
         key = f"decode_S{Sn}_H{H}_N64_bf16"
     else:
+        per_slot = args.budget_mode == "slot"
+        split = (f"at most {args.budget} tokens per slot per call" if per_slot else
+                 f"split round-robin at {args.budget} tokens per call")
         metric = (f"WKV6 serving tokens·channels/s, {Sn} slots H={H} N=64: prompts U{{1..2048}} at "
-                  f"{args.budget} tokens/call + {n_dec} decode steps")
-        cfg = {"workload": f"WKV6 varlen serving: {Sn} slots, H={H} N=64, prompts U{{1..2048}} split "
-                           f"round-robin at {args.budget} tokens per call ({st['ncalls']} calls), then "
-                           f"{n_dec} T=1 decode steps", "slots": Sn, "H": H, "N": 64,
-               "prompt_tokens": int(lengths.sum()), "calls": st["ncalls"], "decode_steps": n_dec,
-               "budget": args.budget, "global_batch": Sn, "seq_len": int(lengths.max()),
-               "parallelism": "single GPU"}
-        key = f"serving_S{Sn}_H{H}_N64_bf16_budget{args.budget}"
+                  f"{args.budget} tokens/{'slot/' if per_slot else ''}call + {n_dec} decode steps")
+        cfg = {"workload": f"WKV6 varlen serving: {Sn} slots, H={H} N=64, prompts U{{1..2048}} {split} "
+                           f"({st['ncalls']} calls), then {n_dec} T=1 decode steps", "slots": Sn, "H": H,
+               "N": 64, "prompt_tokens": int(lengths.sum()), "calls": st["ncalls"], "decode_steps": n_dec,
+               "budget": args.budget, "budget_mode": args.budget_mode, "global_batch": Sn,
+               "seq_len": int(lengths.max()), "parallelism": "single GPU"}
+        key = f"serving_S{Sn}_H{H}_N64_bf16_budget{args.budget}" + ("_perslot" if per_slot else "")
     return {"metric": metric, "workload_key": key, "launches": st["launches"], "tc": tc, "dtype": "fp32",
             "compute": "fp32 vector ALU (scan)",
             "data": "synthetic (seeded numpy PCG64; bf16 r,k,v,x; fp32 u; initial states ~ N(0,0.1))",
@@ -651,7 +661,7 @@ def main():
     # every launch, so that each label's time is its own.
     stream = torch.cuda.current_stream()
     nl = len(launches)
-    per_launch_events = len({lab for lab, _, _, _, _ in launches}) > 1
+    per_kind_events = len({(lab, k) for lab, k, _, _, _ in launches}) > 1
     # The timed region holds the launches alone, with one event pair around it.
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
@@ -666,25 +676,34 @@ def main():
     ms_per_step = wall * 1000.0 / args.steps
     region_s = region[0].elapsed_time(region[1]) / 1000.0
     value = W["tc"] / (ms_per_step / 1000.0)
-    ev = None
-    if per_launch_events:
-        # Workloads with several kinds of launch: the per-kind kernel times come from the same
-        # number of steps run again afterwards with an event pair around every launch (outside
-        # the timed region, since the events themselves cost time between launches).
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nl)]
-              for _ in range(args.steps)]
+    seg_s = None
+    if per_kind_events:
+        # Workloads with several kinds of launch (label or kernel): the same steps run again after
+        # the timed region with an event at every change of kind (launches of one kind come in
+        # long runs), so each run of one kind is timed back to back, with no event inside it.
+        bounds = [j for j in range(1, nl) if launches[j][:2] != launches[j - 1][:2]]
+        cuts = [0] + bounds + [nl]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in cuts] for _ in range(args.steps)]
         for i in range(args.steps):
-            for j, (_, _, fn, _, _) in enumerate(launches):
-                ev[i][j][0].record(stream)
-                fn()
-                ev[i][j][1].record(stream)
+            for c in range(len(cuts) - 1):
+                evs[i][c].record(stream)
+                for _, _, fn, _, _ in launches[cuts[c]:cuts[c + 1]]:
+                    fn()
+            evs[i][-1].record(stream)
         torch.cuda.synchronize()
+        seg_s = [[evs[i][c].elapsed_time(evs[i][c + 1]) / 1000.0 for c in range(len(cuts) - 1)]
+                 for i in range(args.steps)]
+        seg_of = {}
+        for c in range(len(cuts) - 1):
+            for j in range(cuts[c], cuts[c + 1]):
+                seg_of[j] = (c, cuts[c + 1] - cuts[c])
 
     # per label: summed algorithmic bytes / flops and kernel time
     per = {}
     for j, (label, kernel, _, nbytes, flops) in enumerate(launches):
-        if per_launch_events:
-            times = [ev[i][j][0].elapsed_time(ev[i][j][1]) / 1000.0 for i in range(args.steps)]
+        if per_kind_events:
+            c, n_in = seg_of[j]
+            times = [seg_s[i][c] / n_in for i in range(args.steps)]  # the segment's mean per launch
         else:
             times = [region_s / (args.steps * nl)] * args.steps
         d = per.setdefault(label, {"kernel": kernel, "launches": 0, "s": 0.0, "bytes": 0, "flops": 0, "times": [],
@@ -695,9 +714,23 @@ def main():
         d["bytes"] += nbytes
         d["flops"] += flops
         d["times"].extend(times)
-    dom = max(per, key=lambda k: per[k]["s"])
-    D = per[dom]
-    D["kernel"] = max(D["kernels"], key=D["kernels"].get)  # the kernel most launches of this label ran
+    # the roofline's kernel: the one with the most kernel time over all labels
+    per_k = {}
+    for j, (label, kernel, _, nbytes, flops) in enumerate(launches):
+        if per_kind_events:
+            c, n_in = seg_of[j]
+            t = float(np.mean([seg_s[i][c] / n_in for i in range(args.steps)]))
+        else:
+            t = region_s / (args.steps * nl)
+        d = per_k.setdefault(kernel, {"s": 0.0, "launches": 0, "bytes": 0, "flops": 0, "labels": set()})
+        d["s"] += t
+        d["launches"] += 1
+        d["bytes"] += nbytes
+        d["flops"] += flops
+        d["labels"].add(label)
+    kdom = max(per_k, key=lambda k: per_k[k]["s"])
+    D = dict(per_k[kdom], kernel=kdom)
+    dom = "+".join(sorted(D["labels"]))
     avg_s = D["s"] / D["launches"]
     bytes_per_launch = D["bytes"] / D["launches"]
     achieved = D["bytes"] / D["s"] / 1e9
@@ -728,9 +761,8 @@ def main():
                     "algorithmic_bytes_per_launch": int(bytes_per_launch)}
     phases = {k: {"launches": d["launches"], "kernel_ms": round(d["s"] * 1000.0, 4),
                   "avg_kernel_us": round(d["s"] / d["launches"] * 1e6, 2),
-                  "min_kernel_us": round(min(d["times"]) * 1e6, 2) if per_launch_events else None,
-                  "median_kernel_us": round(float(np.median(d["times"])) * 1e6, 2) if per_launch_events else None,
-                  "timing": "event pair per launch, in a second run of the same steps after the timed region" if per_launch_events else "event pair around the timed region",
+                  "timing": ("events at each change of launch kind, in a second run of the same steps after "
+                             "the timed region" if per_kind_events else "event pair around the timed region"),
                   "kernels": d["kernels"],
                   "hbm_GBs": round(d["bytes"] / d["s"] / 1e9, 1)} for k, d in per.items()}
 

@@ -7,6 +7,9 @@
 // (the rwkv_ops page's RWKV6_OP call: r, k, v, w, u, init_state, state_map ->
 // y, y_state; the standard RWKV-5/6 recurrence).
 //
+// Varlen calls: workgroups take the slots longest first (up to 256 slots), and a slot
+// that consumes at most kShortMax tokens runs the few-token form on one wave.
+//
 // Work decomposition: one 512-thread workgroup per (head, unit).  Wave w owns
 // key rows 8w..8w+7 of the fp32 state and lane j owns value column j, so the
 // state is read and written as coalesced 256-byte rows and stays in
@@ -33,6 +36,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "varlen_short.hpp"
 #include "wkv.h"
 
 namespace wkv {
@@ -45,6 +49,7 @@ constexpr int kTB = 32;                 // tokens staged per block
 static_assert(4 * kWaves == kTB && 16 * kTB == kThreads, "staging: four tokens per wave; reduce: one (token, quad) per thread");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFrameLog2 = 80.f;  // largest log2 decay of one block the rescaled frame takes
+constexpr int kOrderMax = 256;      // varlen calls with at most this many slots run longest first
 
 struct __align__(16) ScanSmem {
   float rk[2][kTB][kHead];       // rescaled frame operands: [0] = rh, [1] = kh
@@ -57,12 +62,14 @@ struct __align__(16) ScanSmem {
   unsigned long long off_sum;  // varlen: 64-bit sum of the earlier slots' lengths
   int meta[3];
   int frame;                     // 1: the current block takes the direct form
+  int order_unit;                // varlen: the slot this workgroup takes (longest first)
+  int lens[kOrderMax];           // varlen: the slots' lengths, for the order
 };
 
 template <bool V6, bool BF16, bool VARLEN>
 __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   const int h = blockIdx.x;
-  const int unit = blockIdx.y;
+  int unit = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;  // value column j
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // key rows kRows*wave ..
@@ -86,6 +93,24 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
   int row_out;
 
   if constexpr (VARLEN) {
+    // Longest first: workgroup row blockIdx.y takes the slot of rank blockIdx.y in the order
+    // of decreasing length (ties by slot index), so that the longest slots start first and
+    // the short ones fill in behind them instead of leaving a long tail.
+    if (p.units <= kOrderMax) {
+      for (int i = tid; i < p.units; i += kThreads) sm.lens[i] = p.lengths[i];
+      __syncthreads();
+      for (int i = tid; i < p.units; i += kThreads) {
+        const int li = sm.lens[i];
+        int rank = 0;
+        for (int j = 0; j < p.units; ++j) {
+          const int lj = sm.lens[j];
+          rank += (lj > li) | ((lj == li) & (j < i));
+        }
+        if (rank == (int)blockIdx.y) sm.order_unit = i;
+      }
+      __syncthreads();
+      unit = sm.order_unit;
+    }
     // Offset of this slot = sum of earlier lengths; validate the slot.
     // The sum is 64-bit (65535 slots of up to 2^31 - 1 tokens cannot wrap it), and
     // one invalid length anywhere makes every slot's offset meaningless, so every
@@ -121,6 +146,18 @@ __global__ void __launch_bounds__(kThreads) wkv56_scan_kernel(ScanParams p) {
     ntok = my_len;
     row_in = my_row;
     row_out = my_row;
+    // A slot of at most kShortMax tokens takes the few-token form on one wave (the state
+    // column in the lane); the other waves leave.
+    if (ntok <= kShortMax) {
+      if (wave != 0) return;
+      float sc[kHead];
+      const float *sp = p.state_in + ((long)my_row * p.H + h) * (kHead * kHead) + lane;
+#pragma unroll
+      for (int i = 0; i < kHead; ++i) sc[i] = sp[i * kHead];
+      static_assert(sizeof(sm.r) >= sizeof(float) * kShortLdsFloats, "few-token staging fits");
+      short_slot_wave<BF16>(p, h, lane, off, ntok, my_row, sc, &sm.r[0][0]);
+      return;
+    }
   } else {
     tok0 = 0;
     ntok = p.T;

@@ -16,17 +16,13 @@
 // slot offset is a wave reduction.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "varlen_short.hpp"
 #include "wkv.h"
 
 namespace wkv {
 namespace {
 
 __device__ __forceinline__ long wave_sum_l(long x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
-}
-__device__ __forceinline__ float wave_sum_f(float x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
   return x;
@@ -80,53 +76,8 @@ __global__ void __launch_bounds__(64) wkv6_varlen_short_kernel(ScanParams p) {
     if (lane == 0 && p.dev_status) atomicOr(p.dev_status, status);
     return;
   }
-  const int ntok = my_len;
-  const float ui = p.u[h * kHead + lane];
-  // the token's row factors r[i], k[i], d[i], read back by every lane as 16-byte broadcasts
-  __shared__ __align__(16) float s_r[kHead], s_k[kHead], s_d[kHead];
-
-  // token rows one token ahead
-  const long e0 = (long)off * C + h * kHead + lane;
-  float nr = 0.f, nk = 0.f, nv = 0.f, nx = 0.f;
-  if (ntok > 0) {
-    nr = load1<BF16>(p.r, e0); nk = load1<BF16>(p.k, e0); nv = load1<BF16>(p.v, e0); nx = load1<BF16>(p.w, e0);
-  }
-  for (int t = 0; t < ntok; ++t) {
-    const long e = e0 + (long)t * C;
-    const float rj = nr, kj = nk, vj = nv, dj = decay_of(nx);
-    if (t + 1 < ntok) {
-      nr = load1<BF16>(p.r, e + C); nk = load1<BF16>(p.k, e + C); nv = load1<BF16>(p.v, e + C); nx = load1<BF16>(p.w, e + C);
-    }
-    float yj = wave_sum_f(rj * ui * kj) * vj;  // bonus: (r_t . (u * k_t)) v_t[j]
-    s_r[lane] = rj;
-    s_k[lane] = kj;
-    s_d[lane] = dj;
-    __syncthreads();  // one wave: orders the row factors' stores before the broadcast reads
-#pragma unroll
-    for (int i4 = 0; i4 < kHead / 4; ++i4) {
-      const float4 r4 = *reinterpret_cast<const float4 *>(&s_r[4 * i4]);
-      const float4 k4 = *reinterpret_cast<const float4 *>(&s_k[4 * i4]);
-      const float4 d4 = *reinterpret_cast<const float4 *>(&s_d[4 * i4]);
-      const float rr[4] = {r4.x, r4.y, r4.z, r4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // decay in place, then add k v in place: both update the state register itself
-        yj = fmaf(rr[e], s[4 * i4 + e], yj);
-        s[4 * i4 + e] = fmaf(kk[e], vj, s[4 * i4 + e] * dd[e]);
-      }
-    }
-    __syncthreads();  // the reads finish before the next token's factors are stored
-    if (p.y_bf16) static_cast<uint16_t *>(p.y)[e] = bf16_bits(yj);
-    else static_cast<float *>(p.y)[e] = yj;
-  }
-
-  if (p.state_out) {
-    if (ntok == 0 && p.state_out == p.state_in) return;  // empty slot: untouched
-    float *sp = p.state_out + ((long)my_row * p.H + h) * (kHead * kHead) + lane;
-#pragma unroll
-    for (int i = 0; i < kHead; ++i) sp[i * kHead] = s[i];
-  }
+  __shared__ __align__(16) float lds[kShortLdsFloats];
+  short_slot_wave<BF16>(p, h, lane, off, my_len, my_row, s, lds);
 }
 
 }  // namespace

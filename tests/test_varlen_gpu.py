@@ -81,6 +81,39 @@ def test_varlen_few_tokens_many_slots(max_len):
             assert np.array_equal(sh[row], state[row].astype(np.float64)), f"row {row} modified"
 
 
+@pytest.mark.parametrize("S", [40, 300])
+def test_varlen_mixed_lengths_routing_and_order(S):
+    """One call whose slots consume 0, 1 .. 8 and 9 .. 130 tokens (max_len 130): the staged kernel
+    runs the slots of at most 8 tokens in the few-token form and the others staged, taking them
+    longest first when the call has at most 256 slots (S = 40) and in slot order otherwise
+    (S = 300).  Out-of-place states (empty slots copied), a bf16 y that is the fp32 y rounded,
+    every slot against the oracle."""
+    H, N = 2, 64
+    rng = np.random.default_rng(70 + S)
+    kind = rng.integers(0, 3, size=S)
+    lengths = np.where(kind == 0, rng.integers(0, 9, size=S),
+                       np.where(kind == 1, rng.integers(9, 131, size=S), rng.integers(0, 3, size=S)))
+    lengths = lengths.astype(np.int32)
+    lengths[rng.integers(S)] = 130
+    inp = varlen_inputs(S, H, N, seed=71 + S, decode_steps=0, lengths=lengths)
+    sin = dev(inp["state"])
+    sout = torch.full_like(sin, float("nan"))
+    sout_b = torch.full_like(sin, float("nan"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    args = [dev(lengths)] + [dev(inp[n]) for n in ("r", "k", "v", "x")] + [dev(inp["u"]), H, sin]
+    y = wkv.wkv6_forward_varlen(*args, max_len=130, state_out=sout, dev_status=status)
+    yb = wkv.wkv6_forward_varlen(*args, max_len=130, state_out=sout_b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(sin, dev(inp["state"]))
+    assert torch.equal(yb, y.to(torch.bfloat16)) and torch.equal(sout_b, sout)
+    yo, so = oracle.wkv6_varlen(lengths, inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], H, N, inp["state"])
+    assert_bf16(host(y), yo, "mixed varlen y")
+    assert_bf16(host(sout), so, "mixed varlen states")
+    empty = lengths == 0
+    assert torch.equal(sout[torch.from_numpy(empty).cuda()], sin[torch.from_numpy(empty).cuda()])
+
+
 def test_varlen_out_of_place_copies_empty_slots():
     H, N = 1, 64
     lengths = np.array([0, 3], dtype=np.int32)
