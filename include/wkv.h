@@ -255,7 +255,10 @@ WKV_API wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N,
  * written, its du_rows row is zero, and du sums the other rows.
  * All pointers are device pointers owned by the caller; the library
  * allocates nothing.  Outputs are written, not accumulated.  Three
- * token-sequential sweeps plus a small reduction are enqueued on `stream`.
+ * token-sequential sweeps plus a small reduction are enqueued on `stream`;
+ * between the first and the last sweep dw also holds the forward state of
+ * every 256th token (each head in its own columns of the 64 rows before it),
+ * so dw must not alias another argument.
  * N must be 64.  Deterministic (no atomics on data).
  */
 WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,

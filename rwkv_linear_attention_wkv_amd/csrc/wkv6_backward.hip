@@ -16,6 +16,11 @@
 //   dlam_t[i] = sum_{tau > t} r_tau[i] dr~_tau[i] + sum_j dS_T[i][j] S_T[i][j]
 //               - sum_{s >= t} k_s[i] dk~_s[i],       dx_t[i] = -exp(x_t[i]) dlam_t[i]
 // (every pair (s, tau) whose decay path crosses token t, counted once).
+// With E_t[i] = sum_j G_t[i][j] S_t[i][j] this is dlam_t = E_t - k_t dk~_t, and
+// E_{t-1} = E_t - k_t dk~_t + r_t dr~_t, E_{T-1} = sum_j dS_T S_T: the running
+// difference walked backwards.  Its rounding accumulates with the number of
+// steps walked, so the walk restarts from E_t itself every kSpan tokens, with
+// S_t kept by the forward sweep.
 //
 // Each sweep is one state recurrence of the same shape: a 64 x 64 fp32 state
 // X in registers (wave w owns rows 8w..8w+7; lanes 2m and 2m+1 hold the two
@@ -34,7 +39,9 @@
 // are summed through LDS in a fixed order (deterministic).  Of the
 // per-channel sums over time, du is walked by wave 0 one token after the
 // other, and the dlam running sums are a prefix over the block (in-wave sums
-// plus the earlier waves' totals) on a compensated carry.  Inside a block
+// plus the earlier waves' totals) on a compensated carry, reset to E at the
+// span ends (the forward sweep leaves S_t in the dw rows that the dk/dw sweep
+// writes last, so no workspace is needed).  Inside a block
 // the state is carried in a frame rescaled by the block's running decay
 // product, which makes each step two FMAs per state element instead of three
 // (blocks whose decay product underflows the frame take the direct form).
@@ -58,6 +65,10 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kRows = kHead / kWaves;  // state rows per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFrameLog2 = 80.f;  // largest log2 decay of one block the rescaled frame takes
+// Every kSpan tokens the forward sweep leaves the state S in the dw rows of the span's last
+// kHead tokens (of its own head), and the dk/dw sweep restarts its decay-gradient sum there
+// from the exact identity (see the time sums below).  A multiple of both block lengths.
+constexpr int kSpan = 256;
 
 enum Sweep { TFWD = 0, BWD = 1, TBWD = 2 };
 
@@ -78,6 +89,7 @@ struct Smem {
   float tot[kWaves][kHead];            // log2 decay of each staging wave's tokens
   float dend[kHead];                   // decay product of the block per channel
   float bon[KTB];
+  float ek[kWaves][kHead];             // per-wave parts of sum_j G[i][j] S[i][j] at a span end
 };
 
 template <int MODE, bool BF16, int KTB>
@@ -172,9 +184,40 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
       pdr[t4] = MODE == TBWD ? p.dr[e] : 0.f;
     }
   };
+  // Blocks in processing order.  The dk/dw sweep takes the ragged block first, so that its later
+  // blocks start on tokens kSpan * c - 1 (the forward sweep's span ends); the others take it last.
+  const int nb0 = (MODE == TBWD && T % KTB != 0) ? T % KTB : KTB;
+  // dk/dw sweep: the kept state of the next span end, loaded one block ahead (this thread's tile)
+  float ck[4][2];
+  auto fetch_kept = [&](int q1) {
+    if (MODE == TBWD && q1 > 0 && q1 < T && (T - q1) % kSpan == 0) {
+      const long t0 = row0 + (T - q1) - kHead;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float *sv = &p.dw[(t0 + xr0 + a) * C + h * kHead + xc0];  // dw is only 4-byte aligned
+        ck[a][0] = sv[0];
+        ck[a][1] = sv[1];
+      }
+    }
+  };
   if (T > 0) fetch(0);
-  for (int q0 = 0; q0 < T; q0 += KTB) {
-    const int nb = min(KTB, T - q0);
+  fetch_kept(nb0);
+  for (int q0 = 0, nbn = nb0; q0 < T; q0 += nbn, nbn = KTB) {
+    const int nb = min(nbn, T - q0);
+    if (MODE == TBWD && q0 > 0 && (T - q0) % kSpan == 0) {
+      // ck: the state S after token T-1-q0, left by the forward sweep in this head's dw rows of
+      // the kHead tokens up to that one (row j holds S[.][j]), in the same tile layout as X = G^T.
+      // E[i] = sum_j G[i][j] S[i][j] is the exact value of the running difference here.
+      float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        e0 = fmaf(X[a][0], ck[a][0], e0);
+        e1 = fmaf(X[a][1], ck[a][1], e1);
+      }
+      e0 += xor_lane1(e0);
+      e1 += xor_lane1(e1);
+      sm.ek[wave][xc0 + half] = half ? e1 : e0;  // read after the staging barrier below
+    }
     // ---- stage this block (token of step q0 + tt at row tt).  Part 1: the factors that do
     // not depend on the frame, the bonus scalars, and the log2 decays (lam2 = log2 d) with
     // this thread's running sums in processing order (exclusive cex, inclusive cin).
@@ -237,6 +280,13 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
       total += t;
     }
     const bool direct = __any(!(total >= -kFrameLog2));
+    if (MODE == TBWD && q0 > 0 && (T - q0) % kSpan == 0) {  // restart the carry (fixed order)
+      float e = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) e += sm.ek[w][lane];
+      dsum = e;
+      dcomp = 0.f;
+    }
 #pragma unroll
     for (int t4 = 0; t4 < TPW; ++t4) {
       const int tt = TPW * wave + t4;
@@ -256,7 +306,8 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
       }
       if (tt == nb - 1) sm.dend[lane] = __builtin_amdgcn_exp2f(ci);
     }
-    fetch(q0 + KTB);  // in flight during this block
+    fetch(q0 + nb);  // in flight during this block
+    fetch_kept(q0 + nb);
     __syncthreads();
 
     // ---- the recurrence over the block's tokens.  ya, yb: this lane's partial outputs of
@@ -336,6 +387,17 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
     }
     __syncthreads();
 
+    if (MODE == TFWD && (q0 + nb) % kSpan == 0 && q0 + nb < T) {
+      // S after token q0+nb-1 (X = S^T, in plain form at the block end) into this head's dw rows
+      // of the kHead tokens up to that one; the dk/dw sweep reads it before it writes them.
+      const long t0 = row0 + q0 + nb - kHead;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float *sv = &p.dw[(t0 + xr0 + a) * C + h * kHead + xc0];
+        sv[0] = X[a][0];
+        sv[1] = X[a][1];
+      }
+    }
     // ---- sum the wave partials in a fixed order, add the u terms, store
     {
       const int tt = tid / (kHead / CPT), c = CPT * (tid % (kHead / CPT));

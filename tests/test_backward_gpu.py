@@ -5,11 +5,14 @@ The oracle's gradients are pinned to central differences of its forward
 max |g - o| / max(|o|, rms(o)) per gradient.  dr, dk, dv, du and the state
 gradient are single recurrences like the forward (measured about 1e-6 at
 T=4096): bound 1e-4.  The decay gradient is the reverse running difference of
-r * dr~ and k * dk~ over the rest of the sequence; each of those terms carries
-its own fp32 rounding (about 1e-6 relative) and they add up over the
-sequence while the result is a difference, so its relative error grows with
-T over the decay window (measured 1.3e-4 at T=4096 on all 256 units): bound
-1e-3.
+r * dr~ and k * dk~; each of those terms carries its own fp32 rounding (about
+1e-6 relative) and their errors add up over the steps walked while the result
+is a difference.  The walk restarts from its exact value sum_j G S every 256
+tokens (the forward sweep keeps S there), so the error no longer grows with T:
+bound 2e-4, checked up to T=16384 and on the restart edges.  With strong decays
+(x up to 2, d_t down to exp(-7.4)) the difference cancels within one step as
+well: dlam_t = d_t (sum_j G_t S_{t-1}) is small while its two terms are not,
+and dx = -exp(x) dlam scales that error up: bound 1e-3 there.
 """
 import numpy as np
 import pytest
@@ -23,7 +26,8 @@ from wkv_inputs import wkv6_inputs, wkv6_upstream
 pytestmark = pytest.mark.gpu
 
 GRAD_REL = 1e-4
-DW_REL = 1e-3
+DW_REL = 2e-4
+DW_REL_STRONG = 1e-3  # decays down to exp(-exp(2)) per step
 
 
 def _gpu(inp, up, state=None, state_map=None, with_dstate=True):
@@ -37,11 +41,12 @@ def _gpu(inp, up, state=None, state_map=None, with_dstate=True):
                              state_final=S_final if with_dstate else None, d_state=ds)
 
 
-def _check(got, ref, what):
+def _check(got, ref, what, dw_bound=DW_REL):
     names = ("dr", "dk", "dv", "dw", "du", "d_state")
     for name, g, o in zip(names, got, ref):
         e = fp32_relerr(host(g), o)
-        bound = DW_REL if name == "dw" else GRAD_REL
+        bound = dw_bound if name == "dw" else GRAD_REL
+        print(f"{what} {name}: {e:.3e}")
         assert np.all(np.isfinite(host(g))), f"{what} {name}: non-finite"
         assert e <= bound, f"{what} {name}: relative error {e:.3e} > {bound}"
 
@@ -96,7 +101,7 @@ def test_backward_zero_state_and_decay_extremes():
         torch.cuda.synchronize()
         dr, dk, dv, dx, du, _, dS = oracle.wkv6_backward(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], 2, 64,
                                                          up["dy"])
-        _check(got, (dr, dk, dv, dx, du, dS), f"x in {x_range}")
+        _check(got, (dr, dk, dv, dx, du, dS), f"x in {x_range}", DW_REL_STRONG if x_range[1] > 0 else DW_REL)
 
 
 def test_backward_full_shape():
@@ -128,3 +133,31 @@ def test_backward_deterministic_and_empty():
     torch.cuda.synchronize()
     assert torch.equal(out[4], torch.zeros_like(out[4]))
     assert torch.equal(out[5], dev(up0["d_state"]))
+
+
+@pytest.mark.parametrize("T,dtype,x_range", [(256, "bf16", None), (257, "f32", None), (1024, "bf16", None),
+                                             (2100, "f32", (-6.0, 2.0)), (3103, "bf16", None)])
+def test_backward_span_restarts(T, dtype, x_range):
+    """T around multiples of the 256-token span at whose ends the decay-gradient walk restarts
+    from sum_j G S: none (T=256), one right before the last token, several with a ragged first
+    block of the dk/dw sweep, and strong decays (blocks that take the direct form) next to them."""
+    kw = {} if x_range is None else {"x_range": x_range}
+    inp = wkv6_inputs(2, T, 2, 64, seed=500 + T, dtype=dtype, init_state=2, **kw)
+    up = wkv6_upstream(2, T, 2, 64, seed=600 + T)
+    got = _gpu(inp, up, state=inp["state"])
+    torch.cuda.synchronize()
+    dr, dk, dv, dx, du, _, dS = oracle.wkv6_backward(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], 2, 64,
+                                                     up["dy"], state=inp["state"], d_state_out=up["d_state"])
+    _check(got, (dr, dk, dv, dx, du, dS), f"T={T} {dtype}", DW_REL if x_range is None else DW_REL_STRONG)
+
+
+def test_backward_long_sequence_dw():
+    """T=16384 (four times the headline length): the decay gradient stays within 2e-4 (the walk
+    restarts every 256 tokens instead of carrying its rounding over the whole sequence)."""
+    inp = wkv6_inputs(1, 16384, 2, 64, seed=21, init_state=1)
+    up = wkv6_upstream(1, 16384, 2, 64, seed=22)
+    got = _gpu(inp, up, state=inp["state"])
+    torch.cuda.synchronize()
+    ref = oracle.wkv6_backward(inp["r"], inp["k"], inp["v"], inp["x"], inp["u"], 2, 64, up["dy"],
+                               state=inp["state"], d_state_out=up["d_state"])
+    _check(got, (*ref[:5], ref[6]), "T=16384")
