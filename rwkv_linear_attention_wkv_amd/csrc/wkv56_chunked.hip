@@ -50,7 +50,8 @@
 //     adds A V, reading V in the token order the accumulator layout gives.  Four state waves own the
 //     32x32 fp32 state tiles: they read ktil^T with the LDS transpose load,
 //     add ktil^T V, rescale, and publish the state as bf16 hi / lo S^T in a
-//     ping-pong buffer for the next chunk's outputs.
+//     ping-pong buffer for the next chunk's outputs.  The two remaining waves
+//     touch the token rows of chunk i+3 early in the step (they do no math).
 // Operand buffers and the decay totals are double-buffered in LDS.
 #include <atomic>
 #include <type_traits>
@@ -67,6 +68,7 @@ constexpr int L = 64;           // tokens per chunk
 constexpr int kThreads = 1024;  // 16 waves: 8 producers, 8 consumers
 constexpr int RS = 72;          // LDS row stride in bf16 elements (144 bytes)
 constexpr float kMaxLog2 = 100.f;
+constexpr int kWarmAhead = 3;   // chunk distance of the early reads of the idle consumer waves
 
 // A chunk that runs directly keeps the same arrays with other contents:
 // rb_hi = r and rb_lo = k as loaded (bf16), kt_hi / kt_lo = upper / lower 16
@@ -638,6 +640,37 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
         __syncthreads();
       }
     }
+  } else if (cw >= 2 && cw < 4) {
+    // The two consumer waves without output work read one word of each 64-byte half of
+    // every token row of chunk i + kWarmAhead (r, k on one wave, v and the v6 decays on the
+    // other) right after the barrier that opens step i.  The producers issue their own loads
+    // of that chunk only after finishing chunk i + 1 and starting chunk i + 2, late in the
+    // step; by then its lines are in L2 or on their way (measured: 190 instead of 201 us at
+    // B=4 T=4096 H=40, 202-206 instead of 207-237 us at B=8 H=32).  The words are only folded
+    // into a value that is never stored (T is never negative), one step after they were read.
+    const int w2 = cw - 2;
+    const uint32_t wofs0 = (uint32_t)(((lane >> 1) * ts) * 2 + (lane & 1) * 64);
+    const uint32_t wofs1 = wofs0 + (uint32_t)(32 * ts * 2);
+    uint32_t wl[4] = {0u, 0u, 0u, 0u}, acc = 0u;
+    for (int i = -2; i < nchunks; ++i) {
+      if (i >= 0 && is_direct(i)) direct_chunk(i);
+      acc ^= (wl[0] ^ wl[1]) ^ (wl[2] ^ wl[3]);
+      const int cwarm = i + kWarmAhead;
+      if (cwarm < nchunks) {
+        const unsigned long long off = (unsigned long long)uniform64((base + (long)cwarm * L * ts) * 2);
+        const auto ra = rsrc_at(w2 ? p.v : p.r, off);
+        wl[0] = __builtin_amdgcn_raw_buffer_load_b32(ra, (int)wofs0, 0, 0);
+        wl[1] = __builtin_amdgcn_raw_buffer_load_b32(ra, (int)wofs1, 0, 0);
+        if (!w2 || V6) {
+          const auto rb = rsrc_at(w2 ? p.w : p.k, off);
+          wl[2] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)wofs0, 0, 0);
+          wl[3] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)wofs1, 0, 0);
+        }
+      }
+      __syncthreads();
+    }
+    acc ^= (wl[0] ^ wl[1]) ^ (wl[2] ^ wl[3]);
+    if (T < 0) sm.wtot[0][0][0].x = __uint_as_float(acc);
   } else if (y_wave) {
     for (int i = -2; i < nchunks; ++i) {
       if (i >= 0) {
