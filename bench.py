@@ -23,6 +23,10 @@ Other workloads (same JSON layout, not the headline):
 The wkv5 / wkv6 forward also takes --head-first ([B,H,T,N] token arrays) and
 --out-dtype bf16 (y rounded to bf16).
 
+Before the warm-up steps, full steps run untimed for --settle-ms (200 ms by
+default): the core clock moves during the first tens of milliseconds of
+sustained work, and the timed steps are meant to see the sustained clock.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload wkv6] [--algo auto|scan|chunked]
 """
 from __future__ import annotations
@@ -58,6 +62,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20; 200 for the short decode step, 5 for the serving pass)")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed full steps for this long before the warm-up steps, so that the timed "
+                         "steps run at the sustained core clock (0: none)")
     ap.add_argument("--workload", default="wkv6", choices=["wkv6", "wkv5", "wkv4", "decode", "serving", "wkv6_bwd", "wkv7"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunked"])
     ap.add_argument("--head-first", action="store_true",
@@ -652,6 +659,21 @@ def main():
         for _, _, fn, _, _ in launches:
             fn()
 
+    # Clock settle.  The GPU's power management moves the core clock during the first tens of
+    # milliseconds of sustained work: on the chunked B=8 T=4096 H=32 forward, back-to-back launches
+    # 1-8 take about 188 us, launches 9-90 200-280 us, and from there on 186-196 us.  Full steps
+    # run untimed for settle_ms first (synchronizing every four steps, so wall time follows the
+    # GPU), then the warm-up steps; the timed steps see the sustained clock.
+    settle_steps = 0
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1000.0 < args.settle_ms:
+        step()
+        settle_steps += 1
+        if settle_steps % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1000.0
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -769,7 +791,9 @@ def main():
     out = {"metric": W["metric"], "value": value, "unit": TC, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": W["dtype"], "compute": W["compute"], "data": W["data"],
-           "config": W["config"], "roofline": roofline, "phases": phases, "input_gen_s": round(gen_s, 2)}
+           "config": W["config"], "roofline": roofline, "phases": phases, "input_gen_s": round(gen_s, 2),
+           "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
+                      "note": "untimed full steps before the warm-up (core clock settling)"}}
     if not args.no_cpu_baseline:
         cb, parity = W["cpu"](args.cpu_seconds)
         out["cpu_baseline"] = cb
