@@ -50,8 +50,8 @@
 //     adds A V, reading V in the token order the accumulator layout gives.  Four state waves own the
 //     32x32 fp32 state tiles: they read ktil^T with the LDS transpose load,
 //     add ktil^T V, rescale, and publish the state as bf16 hi / lo S^T in a
-//     ping-pong buffer for the next chunk's outputs.  The two remaining waves
-//     touch the token rows of chunk i+3 early in the step (they do no math).
+//     ping-pong buffer for the next chunk's outputs.  The two remaining waves do
+//     no math (they read chunk i+3's rows early in the step; see their loop).
 // Operand buffers and the decay totals are double-buffered in LDS.
 #include <atomic>
 #include <type_traits>
@@ -641,13 +641,17 @@ __global__ void __launch_bounds__(kThreads) wkv56_chunked_kernel(ScanParams p) {
       }
     }
   } else if (cw >= 2 && cw < 4) {
-    // The two consumer waves without output work read one word of each 64-byte half of
-    // every token row of chunk i + kWarmAhead (r, k on one wave, v and the v6 decays on the
-    // other) right after the barrier that opens step i.  The producers issue their own loads
-    // of that chunk only after finishing chunk i + 1 and starting chunk i + 2, late in the
-    // step; by then its lines are in L2 or on their way (measured: 190 instead of 201 us at
-    // B=4 T=4096 H=40, 202-206 instead of 207-237 us at B=8 H=32).  The words are only folded
-    // into a value that is never stored (T is never negative), one step after they were read.
+    // The two consumer waves without output work run their own copy of the chunk loop.  In
+    // it they read one word of each 64-byte half of every token row of chunk i + kWarmAhead
+    // (r, k on one wave, v and the v6 decays on the other) right after the barrier that opens
+    // step i, ahead of the producers' own loads of that chunk late in the step, and fold the
+    // words into a value that is never stored (T is never negative).  Measured sustained at
+    // B=8 T=4096 H=32 and B=4 H=40: 191-193 / 187 us; with these waves in the output waves'
+    // loop, 203 / 198 us; with their own loop but without this code, also 203 / 198 us; with
+    // this code but a distance so large that no read is ever issued, 190 / 187 us.  So the
+    // time this saves comes from how the kernel compiles with this branch in it (the hot
+    // loops of the other roles are the same instructions), not from the reads; the reads cost
+    // nothing in HBM bytes (measured traffic equals the algorithmic).
     const int w2 = cw - 2;
     const uint32_t wofs0 = (uint32_t)(((lane >> 1) * ts) * 2 + (lane & 1) * 64);
     const uint32_t wofs1 = wofs0 + (uint32_t)(32 * ts * 2);
