@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "wkv4_scan_kernel": ["wkv4_scan.hip"],
     "wkv6_varlen_short_kernel": ["wkv6_decode.hip"],
     "wkv6_bwd_sweep_kernel": ["wkv6_backward.hip"],
+    "wkv6_bwd_chunked_kernel": ["wkv6_backward_chunked.hip", "wkv6_backward.hip", "mfma_ops.hpp"],
     "wkv7_scan_kernel": ["wkv7_scan.hip"],
     "wkv7_short_kernel": ["wkv7_scan.hip"],
     "wkv7_chunked_kernel": ["wkv7_chunked.hip", "mfma_ops.hpp"],
@@ -355,9 +356,13 @@ def workload_wkv6_bwd(args):
     # du_rows and the initial-state gradient
     alg_bytes = 8 * tc + 4 * tc + 4 * C + 2 * 4 * B * H * N * N + 16 * tc + 4 * C + 4 * B * C + 4 * B * H * N * N
     flops = 3 * 2 * 3 * N * tc  # three sweeps, each 3 FMA-class ops per state element and token
+    kernel = "wkv6_bwd_chunked_kernel" if (args.algo == "chunked" or (args.algo == "auto" and T >= 64)) \
+        else "wkv6_bwd_sweep_kernel"
+
+    algo = "chunked" if args.algo == "auto" and T >= 64 else ("scan" if args.algo == "auto" else args.algo)
 
     def run():
-        out["g"] = wkv.wkv6_backward(r, k, v, x, u, H, dy, state_final=S_final, d_state=dS)
+        out["g"] = wkv.wkv6_backward(r, k, v, x, u, H, dy, state_final=S_final, d_state=dS, algo=algo)
 
     def cpu(target_s):
         import oracle
@@ -387,14 +392,15 @@ def workload_wkv6_bwd(args):
     return {
         "metric": f"WKV6 backward tokens·channels/s, B={B} T={T} H={H} N={N}",
         "workload_key": f"wkv6bwd_B{B}_T{T}_H{H}_N{N}_bf16",
-        "launches": [("backward", "wkv6_bwd_sweep_kernel", run, alg_bytes, flops)],
+        "launches": [("backward", kernel, run, alg_bytes, flops)],
         "tc": tc,
         "dtype": "fp32",
-        "compute": "fp32 vector ALU (three token-sequential sweeps)",
+        "compute": ("bf16 MFMA on hi/lo-split operands, fp32 accumulation (64-token chunks)"
+                    if kernel == "wkv6_bwd_chunked_kernel" else "fp32 vector ALU (three token-sequential sweeps)"),
         "data": "synthetic (seeded numpy PCG64; bf16 r,k,v,x; fp32 u; fp32 dy ~ N(0,1) and final-state "
                 "gradient ~ N(0,0.1); zero initial state)",
         "config": {"workload": f"WKV6 backward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 gradients",
-                   "B": B, "T": T, "H": H, "N": N, "global_batch": B, "seq_len": T,
+                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
                    "parallelism": "single GPU"},
         "cpu": cpu,
     }

@@ -251,14 +251,15 @@ WKV_API wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N,
  *                state row b started from (rows that share a state_in row are
  *                not summed: the caller adds them)
  * A batch row whose state_map entry is outside [0, n_state) sets
- * WKV_DEV_BAD_STATE_MAP; its rows of dr, dk, dv, dw and d_state_in are not
- * written, its du_rows row is zero, and du sums the other rows.
+ * WKV_DEV_BAD_STATE_MAP; its rows of dr, dk, dv, dw and d_state_in hold no
+ * gradients (not written, apart from the staging described below), its du_rows
+ * row is zero, and du sums the other rows.
  * All pointers are device pointers owned by the caller; the library
- * allocates nothing.  Outputs are written, not accumulated.  Three
- * token-sequential sweeps plus a small reduction are enqueued on `stream`;
- * between the first and the last sweep dw also holds the forward state of
- * every 256th token (each head in its own columns of the 64 rows before it),
- * so dw must not alias another argument.
+ * allocates nothing.  Outputs are written, not accumulated.  The
+ * algorithm is WKV_ALGO_AUTO (see wkv6_backward_ex).  dr and dw also serve as
+ * staging between the launches (chunk start states in dr, the forward state of
+ * every 256th token and a per-unit mark in dw, each head in its own columns), so
+ * neither may alias another argument.
  * N must be 64.  Deterministic (no atomics on data).
  */
 WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
@@ -269,6 +270,32 @@ WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
                          float *dr, float *dk, float *dv, float *dw,
                          float *du, float *du_rows, float *d_state_in,
                          int32_t *dev_status, void *stream);
+
+/* wkv6_backward with a choice of algorithm:
+ *   WKV_ALGO_SCAN     three token-sequential sweeps over the sequence (vector ALUs);
+ *   WKV_ALGO_CHUNKED  64-token chunks on MFMA (bf16 inputs only, else
+ *                     WKV_ERR_UNSUPPORTED): a pass that leaves each chunk's start
+ *                     state in dr, then a reverse pass over the chunks that forms
+ *                     every gradient from matrix products; a (row, head) with a
+ *                     chunk whose decays leave the chunked form's exponent range
+ *                     (a log2-decay total below -100 in some channel, e.g.
+ *                     strong or zero decays) and a rejected state_map row are
+ *                     left to the sweeps, so every input is covered;
+ *   WKV_ALGO_AUTO     CHUNKED for bf16 inputs with T >= 64, else SCAN.
+ * Precision: the sweeps compute in fp32 (dr, dk, dv, du, d_state_in about 1e-6
+ * relative to the largest value, dw about 5e-5, coarser for decays near zero);
+ * the chunked products take every operand that is not an exact bf16 input as
+ * bf16 hi + lo (about 16 bits): about 1e-4 for dr .. d_state_in and 1e-3 for
+ * dw, whose in-chunk running difference does not cancel those roundings.
+ * Every other argument, result and error as wkv6_backward. */
+WKV_API wkv_status wkv6_backward_ex(int B, int T, int H, int N,
+                            const void *r, const void *k, const void *v, const void *w,
+                            wkv_dtype in_dtype, const float *u, const float *dy,
+                            const float *state_in, const int32_t *state_map, int n_state,
+                            const float *state_final, const float *d_state_out,
+                            float *dr, float *dk, float *dv, float *dw,
+                            float *du, float *du_rows, float *d_state_in,
+                            wkv_algo algo, int32_t *dev_status, void *stream);
 
 /*
  * v6 backward for callers that cannot allocate device memory (code under HIP

@@ -195,7 +195,7 @@ def wkv6_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y
 
 
 def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_final=None, d_state=None,
-                  return_d_state=True, dev_status=None, library_scratch=False):
+                  return_d_state=True, dev_status=None, library_scratch=False, algo="auto"):
     """Gradients of :func:`wkv6_forward` (same r, k, v, w, u, H, state, state_map).
 
     ``dy`` [B, T, H*N] fp32 is the gradient of y; ``d_state`` [B, H, N, N] fp32
@@ -206,7 +206,9 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
     started from.  With ``library_scratch`` the call goes to
     ``wkv6_backward_noalloc``, whose du staging is the library's own device
     array (B*H*N <= 1,048,576; calls that overlap on one GPU race) instead of a
-    workspace allocated here.
+    workspace allocated here.  ``algo``: "auto" (chunked on MFMA for bf16 inputs with T >= 64),
+    "scan" (three token-sequential sweeps) or "chunked" (bf16 only); the allocation-free call
+    takes "auto" only.
     """
     B, T, C = r.shape
     if C % H:
@@ -234,11 +236,14 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
     head = (B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r), _ptr(u), _ptr(dy),
             _ptr(state), _ptr(state_map), n_state, _ptr(state_final), _ptr(d_state),
             _ptr(dr), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du))
+    a = _ALGOS[algo] if isinstance(algo, str) else int(algo)
     if library_scratch:
+        if a != WKV_ALGO_AUTO:
+            raise ValueError("the allocation-free backward takes algo='auto' only")
         check(_lib.wkv6_backward_noalloc(*head, _ptr(d_state_in), _ptr(dev_status), _stream(r)))
     else:
         du_rows = torch.empty((B, C), **f32)
-        check(_lib.wkv6_backward(*head, _ptr(du_rows), _ptr(d_state_in), _ptr(dev_status), _stream(r)))
+        check(_lib.wkv6_backward_ex(*head, _ptr(du_rows), _ptr(d_state_in), a, _ptr(dev_status), _stream(r)))
     return dr, dk, dv, dw, du, d_state_in
 
 

@@ -57,9 +57,17 @@ struct BwdParams {
   const float *state_final, *d_state_out;  // [B, H, 64, 64]
   float *dr, *dk, *dv, *dw, *du, *du_rows, *d_state_in;
   int32_t *dev_status;
+  int marked_only;  // sweeps: only the (row, head) units the chunked passes left to them
 };
 
+// The chunked backward's mark on a (row, head) it leaves to the sweeps: a NaN bit pattern in
+// that unit's dw element of the last token and channel 0 (no arithmetic result or widened bf16
+// input has this payload).
+constexpr uint32_t kBwdFallbackMark = 0x7fc0dea1u;
+
 hipError_t launch_wkv6_backward(const BwdParams &p, bool bf16, hipStream_t s);
+// The chunked passes (bf16 inputs); launch_wkv6_backward with marked_only follows them.
+hipError_t launch_wkv6_backward_chunked(const BwdParams &p, hipStream_t s);
 
 // v7 generalized delta rule, token-sequential (dense rows, [B, T, H*64] token arrays).
 struct V7Params {

@@ -120,6 +120,11 @@ __device__ __forceinline__ void sweep(const BwdParams &p, Smem<KTB> &sm, int h, 
 #pragma unroll
   for (int a = 0; a < 4; ++a) X[a][0] = X[a][1] = 0.f;
   const long head_off = (long)h * kHead * kHead;
+  // After the chunked passes: only the units they marked (the mark sits in this unit's dw
+  // element of the last token, which no sweep writes before the dk/dw sweep reads it here).
+  if (p.marked_only && T > 0 &&
+      __float_as_uint(p.dw[(row0 + T - 1) * C + (long)h * kHead]) != kBwdFallbackMark)
+    return;
   // A batch row whose state_map entry is out of range is skipped by all three sweeps
   // alike (its token and state gradients are not written), and its share of du is
   // zero, so du still sums the other rows.

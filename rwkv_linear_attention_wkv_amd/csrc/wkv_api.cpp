@@ -125,9 +125,9 @@ wkv_status backward6(const char *fn, int B, int T, int H, int N, const void *r, 
                      const void *w, wkv_dtype in_dtype, const float *u, const float *dy, const float *state_in,
                      const int32_t *state_map, int n_state, const float *state_final, const float *d_state_out,
                      float *dr, float *dk, float *dv, float *dw, float *du, float *du_rows, bool use_scratch,
-                     float *d_state_in, int32_t *dev_status, void *stream) {
+                     float *d_state_in, wkv_algo algo, int32_t *dev_status, void *stream) {
   wkv_status st = check_dense56(fn, B, T, H, N, r, k, v, w, in_dtype, u, dr, state_in, state_map, n_state,
-                                nullptr, WKV_ALGO_AUTO);
+                                nullptr, algo);
   if (st != WKV_OK) return st;
   if (T > 0) {
     REQUIRE(dy && dk && dv && dw, "%s: dy, dk, dv and dw must be non-NULL", fn);
@@ -162,7 +162,17 @@ wkv_status backward6(const char *fn, int B, int T, int H, int N, const void *r, 
   p.state_final = state_final; p.d_state_out = d_state_out;
   p.dr = dr; p.dk = dk; p.dv = dv; p.dw = dw; p.du = du; p.du_rows = du_rows; p.d_state_in = d_state_in;
   p.dev_status = dev_status;
-  return launched(wkv::launch_wkv6_backward(p, in_dtype == WKV_BF16, static_cast<hipStream_t>(stream)), fn);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  // Chunked passes (AUTO: bf16 inputs, T >= 64), then the sweeps for the units they leave
+  // (decays beyond the chunked form's exponent range, rejected state_map rows).
+  const bool chunked = T > 0 && in_dtype == WKV_BF16 && (int64_t)H * N <= kChunkedMaxRow &&
+                       (algo == WKV_ALGO_CHUNKED || (algo == WKV_ALGO_AUTO && T >= kChunk));
+  if (chunked) {
+    const hipError_t e = wkv::launch_wkv6_backward_chunked(p, hs);
+    if (e != hipSuccess) return launched(e, fn);
+    p.marked_only = 1;
+  }
+  return launched(wkv::launch_wkv6_backward(p, in_dtype == WKV_BF16, hs), fn);
 }
 
 }  // namespace
@@ -368,7 +378,19 @@ wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *
                          const float *d_state_out, float *dr, float *dk, float *dv, float *dw, float *du,
                          float *du_rows, float *d_state_in, int32_t *dev_status, void *stream) {
   return backward6("wkv6_backward", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map, n_state,
-                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, dev_status, stream);
+                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, WKV_ALGO_AUTO,
+                   dev_status, stream);
+}
+
+wkv_status wkv6_backward_ex(int B, int T, int H, int N, const void *r, const void *k, const void *v,
+                            const void *w, wkv_dtype in_dtype, const float *u, const float *dy,
+                            const float *state_in, const int32_t *state_map, int n_state,
+                            const float *state_final, const float *d_state_out, float *dr, float *dk, float *dv,
+                            float *dw, float *du, float *du_rows, float *d_state_in, wkv_algo algo,
+                            int32_t *dev_status, void *stream) {
+  return backward6("wkv6_backward_ex", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map, n_state,
+                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, algo, dev_status,
+                   stream);
 }
 
 wkv_status wkv6_backward_noalloc(int B, int T, int H, int N, const void *r, const void *k, const void *v,
@@ -378,8 +400,8 @@ wkv_status wkv6_backward_noalloc(int B, int T, int H, int N, const void *r, cons
                                  float *dv, float *dw, float *du, float *d_state_in, int32_t *dev_status,
                                  void *stream) {
   return backward6("wkv6_backward_noalloc", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map,
-                   n_state, state_final, d_state_out, dr, dk, dv, dw, du, nullptr, true, d_state_in, dev_status,
-                   stream);
+                   n_state, state_final, d_state_out, dr, dk, dv, dw, du, nullptr, true, d_state_in, WKV_ALGO_AUTO,
+                   dev_status, stream);
 }
 
 wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N, const int32_t *lengths, int max_len,

@@ -1,8 +1,9 @@
 """wkv6_backward_noalloc — the v6 backward for callers that cannot allocate device memory —
 against wkv6_backward (the same kernels with a caller workspace for the du staging).
 
-The two entry points run the same arithmetic in the same order, so their results must be
-bitwise equal (the parity bar for the backward is 1e-4 relative, bitwise is stricter).  Two
+The two entry points run the same arithmetic in the same order (both take the "auto" choice:
+the chunked passes for these bf16 inputs, then the sweeps for the units they leave), so their
+results must be bitwise equal, which is stricter than the backward's parity bars.  Two
 calls in a row go through the library's scratch, the second smaller than the first, so the
 second reads none of the first call's staging.
 """
