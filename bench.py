@@ -32,6 +32,7 @@ sustained work, and the timed steps are meant to see the sustained clock.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -44,7 +45,8 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TFLOPS = 78.6
 KERNEL_SOURCES = {
     "wkv56_scan_kernel": ["wkv56_scan.hip"],
-    "wkv56_chunked_kernel": ["wkv56_chunked.hip", "mfma_ops.hpp"],
+    "wkv56_chunked_kernel": ["wkv56_chunked.hip", "wkv56_chunked.hpp", "mfma_ops.hpp"],
+    "wkv6_fwd_save_kernel": ["wkv6_chunked_save.hip", "wkv56_chunked.hpp", "mfma_ops.hpp"],
     "wkv4_scan_kernel": ["wkv4_scan.hip"],
     "wkv6_varlen_short_kernel": ["wkv6_decode.hip"],
     "wkv6_bwd_sweep_kernel": ["wkv6_backward.hip"],
@@ -83,6 +85,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--saved-states", action="store_true",
+                    help="wkv6: time wkv6_forward_train (the chunked forward that also saves the chunk states); "
+                         "wkv6_bwd: the backward takes the states such a call saved (made before the timed region)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the WKV step, time a plain device-to-device copy of this many bytes "
                          "(the reference kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -226,9 +231,20 @@ def workload_wkv56(args, version):
     in_bytes = (4 if version == 6 else 3) * 2 * tc + (0 if version == 6 else 4 * C)
     alg_bytes = in_bytes + (2 if ybf else 4) * tc + 4 * B * H * N * N + 4 * C  # inputs + y + state_out + u
     flops = 2 * 3 * N * tc  # scan: 3 FMA per state element and token
+    save = args.saved_states
+    if save:
+        if version != 6 or hf or algo != "chunked":
+            raise SystemExit("--saved-states: the v6 chunked forward with [B,T,H,N] rows only")
+        kernel = "wkv6_fwd_save_kernel"
+        cs = torch.empty((B, H, (T + 63) // 64 - 1, N, N), dtype=torch.float32, device="cuda")
+        alg_bytes += 4 * cs.numel()  # the saved states are written once
 
     def run():
-        fwd(r, k, v, x, u, H, algo=algo, y=y, state_out=S, head_first=hf)
+        if save:
+            wkv.wkv6_forward_train(r, k, v, x, u, H, y=y, state_out=S, chunk_states=cs,
+                                   out_dtype=torch.bfloat16 if ybf else torch.float32)
+        else:
+            fwd(r, k, v, x, u, H, algo=algo, y=y, state_out=S, head_first=hf)
 
     def cpu(target_s):
         import oracle
@@ -250,7 +266,7 @@ def workload_wkv56(args, version):
                      "state_max_abs": smax, "state_mean_abs": smean}
 
     name = f"WKV{version}"
-    variant = ("_headfirst" if hf else "") + ("_ybf16" if ybf else "")
+    variant = ("_headfirst" if hf else "") + ("_ybf16" if ybf else "") + ("_save" if save else "")
     layout = "head-first [B,H,T,N]" if hf else "[B,T,H,N]"
     return {
         "metric": f"{name} fwd tokens·channels/s + % HBM peak (rocprof), B={B} T={T} H={H} N={N}",
@@ -265,6 +281,7 @@ def workload_wkv56(args, version):
         "config": {"workload": f"{name} forward B={B} T={T} H={H} N={N}, bf16 inputs {layout}, fp32 state, "
                                f"{'bf16' if ybf else 'fp32'} output",
                    "B": B, "T": T, "H": H, "N": N, "algo": algo, "layout": "BHTN" if hf else "BTHN",
+                   "saved_states": save,
                    "y_dtype": args.out_dtype, "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "cpu": cpu,
     }
@@ -326,7 +343,8 @@ def workload_wkv7(args):
                     if algo == "chunked" else "fp32 vector ALU (token-sequential generalized delta rule)"),
         "data": "synthetic (seeded numpy PCG64; bf16 r,w,k,v,a,b with a = -kappa, b = kappa*beta; initial states ~ N(0,0.1))",
         "config": {"workload": f"WKV7 forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
-                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
+                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "saved_states": bool(saved and algo == "chunked"),
+                   "global_batch": B, "seq_len": T,
                    "parallelism": "single GPU"},
         "cpu": cpu,
     }
@@ -348,7 +366,12 @@ def workload_wkv6_bwd(args):
     u = torch.from_numpy(inp["u"]).cuda()
     dy = torch.from_numpy(up["dy"]).cuda()
     dS = torch.from_numpy(up["d_state"]).cuda()
-    _, S_final = wkv.wkv6_forward(r, k, v, x, u, H)
+    saved = args.saved_states
+    cs = None
+    if saved:
+        _, S_final, cs = wkv.wkv6_forward_train(r, k, v, x, u, H)
+    else:
+        _, S_final = wkv.wkv6_forward(r, k, v, x, u, H)
     torch.cuda.synchronize()
     out = {}
     tc = B * T * C
@@ -362,7 +385,8 @@ def workload_wkv6_bwd(args):
     algo = "chunked" if args.algo == "auto" and T >= 64 else ("scan" if args.algo == "auto" else args.algo)
 
     def run():
-        out["g"] = wkv.wkv6_backward(r, k, v, x, u, H, dy, state_final=S_final, d_state=dS, algo=algo)
+        out["g"] = wkv.wkv6_backward(r, k, v, x, u, H, dy, state_final=S_final, d_state=dS, algo=algo,
+                                     chunk_states=cs)
 
     def cpu(target_s):
         import oracle
@@ -391,7 +415,7 @@ def workload_wkv6_bwd(args):
 
     return {
         "metric": f"WKV6 backward tokens·channels/s, B={B} T={T} H={H} N={N}",
-        "workload_key": f"wkv6bwd_B{B}_T{T}_H{H}_N{N}_bf16",
+        "workload_key": f"wkv6bwd_B{B}_T{T}_H{H}_N{N}_bf16" + ("_saved" if saved and algo == "chunked" else ""),
         "launches": [("backward", kernel, run, alg_bytes, flops)],
         "tc": tc,
         "dtype": "fp32",
@@ -400,7 +424,8 @@ def workload_wkv6_bwd(args):
         "data": "synthetic (seeded numpy PCG64; bf16 r,k,v,x; fp32 u; fp32 dy ~ N(0,1) and final-state "
                 "gradient ~ N(0,0.1); zero initial state)",
         "config": {"workload": f"WKV6 backward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 gradients",
-                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "global_batch": B, "seq_len": T,
+                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "saved_states": bool(saved and algo == "chunked"),
+                   "global_batch": B, "seq_len": T,
                    "parallelism": "single GPU"},
         "cpu": cpu,
     }
@@ -670,6 +695,11 @@ def main():
     # 1-8 take about 188 us, launches 9-90 200-280 us, and from there on 186-196 us.  Full steps
     # run untimed for settle_ms first (synchronizing every four steps, so wall time follows the
     # GPU), then the warm-up steps; the timed steps see the sustained clock.
+    # Python's garbage collector runs before the settle phase and stays off until the timed region
+    # has ended: a collection between the launches stalls them (about 1 ms was seen right before the
+    # timed region) while the events keep counting, and one right before it lets the clock drop.
+    gc.collect()
+    gc.disable()
     settle_steps = 0
     torch.cuda.synchronize()
     t_settle = time.perf_counter()
@@ -701,6 +731,7 @@ def main():
     region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    gc.enable()
     ms_per_step = wall * 1000.0 / args.steps
     region_s = region[0].elapsed_time(region[1]) / 1000.0
     value = W["tc"] / (ms_per_step / 1000.0)

@@ -192,6 +192,27 @@ WKV_API wkv_status wkv6_forward_ex(int B, int T, int H, int N,
                            void *stream);
 
 /*
+ * v6 forward for training: the chunked form (bf16 inputs, [B,T,H*N] rows), which
+ * also saves the state at every chunk boundary for wkv6_backward_ex.  The
+ * rwkv_ops page's RWKV6_OP is the training operator of this recurrence; the
+ * saved states are the ones its forward reaches at the start of each 64-token
+ * chunk.
+ *   chunk_states [B,H,ceil(T/64)-1,N,N] fp32 DEVICE, 16-byte aligned (may be
+ *                NULL when T <= 64): entry c-1 is the state after token 64c-1
+ *                ([key][value], c = 1 .. ceil(T/64)-1), in fp32 as the kernel
+ *                carries it; rows of a rejected state_map entry are not written
+ * Every other argument, result and error as wkv6_forward_ex with layout
+ * WKV_LAYOUT_BTHN and WKV_ALGO_CHUNKED: y and state_out are bitwise those of
+ * that call.  Costs one extra write of the states (16 KiB per chunk and head).
+ */
+WKV_API wkv_status wkv6_forward_train(int B, int T, int H, int N,
+                           const void *r, const void *k, const void *v, const void *w,
+                           wkv_dtype in_dtype, const float *u, void *y, wkv_dtype out_dtype,
+                           const float *state_in, const int32_t *state_map, int n_state,
+                           float *state_out, float *chunk_states, int32_t *dev_status,
+                           void *stream);
+
+/*
  * v6 varlen forward for batched serving.
  *   lengths      [num_slots] int32 DEVICE: tokens slot s consumes this call
  *                (0 = empty slot: no work, its state row is untouched, or
@@ -282,6 +303,11 @@ WKV_API wkv_status wkv6_backward(int B, int T, int H, int N,
  *                     strong or zero decays) and a rejected state_map row are
  *                     left to the sweeps, so every input is covered;
  *   WKV_ALGO_AUTO     CHUNKED for bf16 inputs with T >= 64, else SCAN.
+ *   chunk_states  NULL, or the states wkv6_forward_train saved in the forward
+ *                 call of these inputs ([B,H,ceil(T/64)-1,N,N], 16-byte
+ *                 aligned): the chunked algorithm then reads them instead of
+ *                 computing them (one pass over k, v and w fewer; no state
+ *                 staging in dr).  Ignored by the sweeps.
  * Precision: the sweeps compute in fp32 (dr, dk, dv, du, d_state_in about 1e-6
  * relative to the largest value, dw about 5e-5, coarser for decays near zero);
  * the chunked products take every operand that is not an exact bf16 input as
@@ -295,7 +321,8 @@ WKV_API wkv_status wkv6_backward_ex(int B, int T, int H, int N,
                             const float *state_final, const float *d_state_out,
                             float *dr, float *dk, float *dv, float *dw,
                             float *du, float *du_rows, float *d_state_in,
-                            wkv_algo algo, int32_t *dev_status, void *stream);
+                            const float *chunk_states, wkv_algo algo,
+                            int32_t *dev_status, void *stream);
 
 /*
  * v6 backward for callers that cannot allocate device memory (code under HIP

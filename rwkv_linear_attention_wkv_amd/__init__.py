@@ -28,7 +28,7 @@ _lib = _native.load()
 
 _ALGOS = {"auto": WKV_ALGO_AUTO, "scan": WKV_ALGO_SCAN, "chunked": WKV_ALGO_CHUNKED}
 
-__all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_backward", "wkv6_forward_varlen", "varlen_plan", "VarlenPlan",
+__all__ = ["wkv4_forward", "wkv5_forward", "wkv6_forward", "wkv6_forward_train", "wkv6_backward", "wkv6_forward_varlen", "varlen_plan", "VarlenPlan",
            "wkv7_forward", "wkv7_plan", "Wkv7Plan", "schedule_round_robin", "resolve_algo", "WkvError", "library"]
 
 
@@ -194,8 +194,49 @@ def wkv6_forward(r, k, v, w, u, H, state=None, state_map=None, *, algo="auto", y
                     head_first, out_dtype)
 
 
+
+def wkv6_forward_train(r, k, v, w, u, H, state=None, state_map=None, *, y=None, state_out=None,
+                       return_state=True, dev_status=None, out_dtype=torch.float32, chunk_states=None):
+    """:func:`wkv6_forward` in the chunked form (bf16 [B, T, H*N] inputs) that also saves the
+    state at every 64-token chunk boundary for :func:`wkv6_backward`.
+
+    Returns ``(y, state_out or None, chunk_states [B, H, ceil(T/64) - 1, N, N] fp32)``; y and
+    state_out are bitwise those of ``wkv6_forward(..., algo="chunked")``.
+    """
+    B, T, C = r.shape
+    if C % H:
+        raise ValueError(f"C={C} is not a multiple of H={H}")
+    N = C // H
+    _same_dtype([("r", r), ("k", k), ("v", v), ("w", w)])
+    for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
+        _dev(t, name, shape=(B, T, C))
+    _dev(u.reshape(-1) if u.dim() == 2 else u, "u", torch.float32, (C,))
+    n_state = 0
+    if state is not None:
+        _dev(state, "state", torch.float32)
+        if state.dim() != 4 or tuple(state.shape[1:]) != (H, N, N):
+            raise ValueError(f"state must be [n_state, {H}, {N}, {N}], got {tuple(state.shape)}")
+        n_state = state.shape[0]
+    _dev(state_map, "state_map", torch.int32, (B,))
+    oc, odt = _out_code(y, out_dtype)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=odt, device=r.device)
+    _dev(y, "y", odt, (B, T, C))
+    if return_state and state_out is None:
+        state_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    _dev(state_out, "state_out", torch.float32, (B, H, N, N))
+    _dev(dev_status, "dev_status", torch.int32, (1,))
+    nsave = max((T + 63) // 64 - 1, 0)
+    if chunk_states is None:
+        chunk_states = torch.empty((B, H, nsave, N, N), dtype=torch.float32, device=r.device)
+    _dev(chunk_states, "chunk_states", torch.float32, (B, H, nsave, N, N))
+    check(_lib.wkv6_forward_train(B, T, H, N, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _dtype_code(r), _ptr(u),
+                                  _ptr(y), oc, _ptr(state), _ptr(state_map), n_state, _ptr(state_out),
+                                  _ptr(chunk_states) if nsave else None, _ptr(dev_status), _stream(r)))
+    return y, state_out, chunk_states
+
 def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_final=None, d_state=None,
-                  return_d_state=True, dev_status=None, library_scratch=False, algo="auto"):
+                  return_d_state=True, dev_status=None, library_scratch=False, algo="auto", chunk_states=None):
     """Gradients of :func:`wkv6_forward` (same r, k, v, w, u, H, state, state_map).
 
     ``dy`` [B, T, H*N] fp32 is the gradient of y; ``d_state`` [B, H, N, N] fp32
@@ -208,7 +249,9 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
     array (B*H*N <= 1,048,576; calls that overlap on one GPU race) instead of a
     workspace allocated here.  ``algo``: "auto" (chunked on MFMA for bf16 inputs with T >= 64),
     "scan" (three token-sequential sweeps) or "chunked" (bf16 only); the allocation-free call
-    takes "auto" only.
+    takes "auto" only.  ``chunk_states``: the states :func:`wkv6_forward_train` saved for these
+    inputs; the chunked algorithm then skips its own pass over k, v and w (the sweeps ignore
+    them).
     """
     B, T, C = r.shape
     if C % H:
@@ -229,6 +272,7 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
     _dev(d_state, "d_state", torch.float32, (B, H, N, N))
     _dev(state_final, "state_final", torch.float32, (B, H, N, N))
     _dev(dev_status, "dev_status", torch.int32, (1,))
+    _dev(chunk_states, "chunk_states", torch.float32, (B, H, max((T + 63) // 64 - 1, 0), N, N))
     f32 = dict(dtype=torch.float32, device=r.device)
     dr, dk, dv, dw = (torch.empty((B, T, C), **f32) for _ in range(4))
     du = torch.empty((C,), **f32)
@@ -238,12 +282,13 @@ def wkv6_backward(r, k, v, w, u, H, dy, state=None, state_map=None, *, state_fin
             _ptr(dr), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du))
     a = _ALGOS[algo] if isinstance(algo, str) else int(algo)
     if library_scratch:
-        if a != WKV_ALGO_AUTO:
-            raise ValueError("the allocation-free backward takes algo='auto' only")
+        if a != WKV_ALGO_AUTO or chunk_states is not None:
+            raise ValueError("the allocation-free backward takes algo='auto' and no chunk_states only")
         check(_lib.wkv6_backward_noalloc(*head, _ptr(d_state_in), _ptr(dev_status), _stream(r)))
     else:
         du_rows = torch.empty((B, C), **f32)
-        check(_lib.wkv6_backward_ex(*head, _ptr(du_rows), _ptr(d_state_in), a, _ptr(dev_status), _stream(r)))
+        cs = _ptr(chunk_states) if chunk_states is not None and chunk_states.numel() else None
+        check(_lib.wkv6_backward_ex(*head, _ptr(du_rows), _ptr(d_state_in), cs, a, _ptr(dev_status), _stream(r)))
     return dr, dk, dv, dw, du, d_state_in
 
 

@@ -37,7 +37,9 @@ SIGNATURES = {
     "wkv6_backward": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp,
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "wkv6_backward_ex": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp,
-                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp]),
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp]),
+    "wkv6_forward_train": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
+                                _vp, _vp]),
     "wkv6_backward_noalloc": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "wkv6_forward_varlen": (_i, [_i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i,

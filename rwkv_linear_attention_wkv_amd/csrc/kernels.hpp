@@ -33,6 +33,9 @@ struct ScanParams {
   const int32_t *lengths;
   int max_len;
   int total_tokens;
+  // chunked v6 with saved states only: [units, H, ceil(T/64) - 1, 64, 64], the state at the
+  // start of chunks 1 .. ceil(T/64) - 1 (after tokens 64c - 1), [key][value]
+  float *chunk_states;
 };
 
 hipError_t launch_wkv56_scan(const ScanParams &p, bool v6, bool bf16, bool varlen, hipStream_t s);
@@ -44,6 +47,8 @@ hipError_t launch_wkv6_varlen_short(const ScanParams &p, bool bf16, hipStream_t 
 
 // v5 / v6 64-token chunked form with MFMA contractions (dense rows only).
 hipError_t launch_wkv56_chunked(const ScanParams &p, bool v6, bool bf16, hipStream_t s);
+// The v6 chunked form that also writes p.chunk_states (bf16 inputs, [B, T, H*64] rows).
+hipError_t launch_wkv6_chunked_save(const ScanParams &p, hipStream_t s);
 
 // v6 backward: three token-sequential sweeps (dr and du, dk and dw, dv and the
 // initial-state gradient) and the sum of du over the batch.
@@ -58,6 +63,9 @@ struct BwdParams {
   float *dr, *dk, *dv, *dw, *du, *du_rows, *d_state_in;
   int32_t *dev_status;
   int marked_only;  // sweeps: only the (row, head) units the chunked passes left to them
+  // chunked: the chunk start states saved by the forward ([B, H, ceil(T/64) - 1, 64, 64]);
+  // NULL: the state pass computes them into dr
+  const float *chunk_states;
 };
 
 // The chunked backward's mark on a (row, head) it leaves to the sweeps: a NaN bit pattern in
@@ -66,7 +74,8 @@ struct BwdParams {
 constexpr uint32_t kBwdFallbackMark = 0x7fc0dea1u;
 
 hipError_t launch_wkv6_backward(const BwdParams &p, bool bf16, hipStream_t s);
-// The chunked passes (bf16 inputs); launch_wkv6_backward with marked_only follows them.
+// The chunked passes (bf16 inputs; the state pass only without p.chunk_states);
+// launch_wkv6_backward with marked_only follows them.
 hipError_t launch_wkv6_backward_chunked(const BwdParams &p, hipStream_t s);
 
 // v7 generalized delta rule, token-sequential (dense rows, [B, T, H*64] token arrays).

@@ -23,13 +23,18 @@
 // Two launches.  Pass 1 walks each (row, head) forward and leaves the chunk start states
 // S_1 .. S_{n-1} in that head's dr rows of the chunk before (64 token rows x 64 channels,
 // exactly one state), which pass 2 reads before it writes those rows; no workspace.  Pass 2
-// walks the chunks in reverse with one 512-thread workgroup per (row, head).
+// walks the chunks in reverse with one 512-thread workgroup per (row, head).  When the caller
+// hands over the states the chunked forward saved (wkv6_forward_train), pass 1 is skipped and
+// pass 2 reads them there.
 //
 // Range.  kt carries exp(-Lam_s) >= 1.  Pass 1 checks every chunk's log2-decay total (the
 // same arithmetic as pass 2); a (row, head) with a chunk below -kMaxLog2 in some channel (or
 // an out-of-range state_map entry) is marked, by a NaN with a payload no arithmetic or bf16
 // input produces, in its dw element of the last token and channel 0, and left to the
 // token-sequential sweeps, which are launched next and skip every unit that is not marked.
+// Without pass 1, pass 2 makes the same checks as it reaches each chunk and, at the first that
+// fails, stores the mark (after the real dw value it may have stored there) and stops; the
+// sweeps then redo the whole unit.
 //
 // Precision.  Operands that are not exact bf16 inputs are split into bf16 hi + lo and each
 // product is hi*hi + hi*lo + lo*hi (two products against the exact v), fp32 accumulation.
@@ -363,9 +368,27 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
   const int cp = tid & 31, tg = tid >> 5, hh = lane >> 5, l32 = lane & 31;
   const int T = p.T, nch = (T + L - 1) / L;
   const long C = (long)p.H * kHead;
-  if (__float_as_uint(*mark_of(p, b, h)) == kBwdFallbackMark) return;  // the sweeps take this unit
+  // With the forward's saved states there is no state pass: this pass itself leaves a unit to
+  // the sweeps (a rejected state_map row, a chunk out of the exponent range), by storing the
+  // mark from the thread that stores that dw element in the chunk loop (its store came first).
+  const bool saved = p.chunk_states != nullptr;
+  if (!saved && __float_as_uint(*mark_of(p, b, h)) == kBwdFallbackMark) return;  // the sweeps take this unit
+  const int tlast = (T - 1) - (nch - 1) * L;  // the last token's place in its chunk
+  auto leave_to_sweeps = [&]() {
+    if (wave == (tlast >> 3) && lane == 0) {
+      __threadfence();
+      *reinterpret_cast<uint32_t *>(mark_of(p, b, h)) = kBwdFallbackMark;
+    }
+  };
   const int row_in = p.state_in ? (p.state_map ? p.state_map[b] : (p.n_state == 1 ? 0 : b)) : -1;
+  if (saved && p.state_in && (row_in < 0 || row_in >= p.n_state)) {
+    leave_to_sweeps();
+    return;
+  }
   const long base = ((long)b * T) * C + (long)h * kHead;
+  // S_c (c >= 1): the saved states, or the dr rows of chunk c - 1 where the state pass left them
+  const float *sbase = saved ? p.chunk_states + ((long)b * p.H + h) * (long)(nch - 1) * (kHead * kHead) : p.dr + base;
+  const long schunk = saved ? (long)(kHead * kHead) : (long)L * C, srow = saved ? (long)kHead : C;
   const long head_off = ((long)b * p.H + h) * (kHead * kHead);
   const unsigned long long row_end2 = (unsigned long long)(base + (long)(T - 1) * C + kHead) * 2;
   const unsigned long long row_end4 = row_end2 * 2;
@@ -397,8 +420,8 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
       dy0[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)roff4[t], 0, 0));  // dy: 4-byte aligned
       dy1[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)roff4[t] + 4, 0, 0));
     }
-    if (c >= 1) {  // S_c, left by pass 1 in the dr rows of chunk c - 1
-      const float *s = p.dr + base + ((long)(c - 1) * L + sci) * C + scj;
+    if (c >= 1) {
+      const float *s = sbase + (long)(c - 1) * schunk + sci * srow + scj;
       const float4 a = *reinterpret_cast<const float4 *>(s), q = *reinterpret_cast<const float4 *>(s + 4);
       sc[0] = a.x; sc[1] = a.y; sc[2] = a.z; sc[3] = a.w; sc[4] = q.x; sc[5] = q.y; sc[6] = q.z; sc[7] = q.w;
     } else if (row_in >= 0) {
@@ -429,7 +452,7 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
 
   // Each role runs its own copy of the chunk loop (the same barriers in the same order), so
   // that only its own registers stay live.  ROLE 0: dV waves, 1: dkt waves, 2: drb waves, 3: G.
-  auto run_chunks = [&](auto role_c) __attribute__((always_inline)) {
+  auto run_chunks = [&](auto role_c) __attribute__((always_inline)) -> bool {
   constexpr int ROLE = decltype(role_c)::value;
   // G waves: the gradient of the state at the current chunk end, tiles (key block gi, value
   // blocks 0 / 1)
@@ -494,7 +517,11 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
     // ---------- stage B: prefix, rb and kt hi / lo, P, the chunk decay
     {
       float pre0, pre1, tot0, tot1;
-      stage_prefix(st, sm.wtot, wave, cp, lane, pre0, pre1, tot0, tot1);  // in range: pass 1 checked
+      // in range when the state pass ran (it checked every chunk); else checked here
+      if (stage_prefix(st, sm.wtot, wave, cp, lane, pre0, pre1, tot0, tot1) && saved) {
+        leave_to_sweeps();
+        return true;
+      }
       if (wave == 0 && !hh)
         *reinterpret_cast<float2 *>(&sm.dl[2 * cp]) = make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
       float c0 = pre0, c1 = pre1;
@@ -721,11 +748,14 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
             g[(32 * gi + 8 * (e >> 2) + 4 * hh + (e & 3)) * kHead + 32 * jb + l32] = G[jb][e];
       }
     }
+    return false;
   };
-  if (wave < 2) run_chunks(std::integral_constant<int, 0>{});
-  else if (wave < 4) run_chunks(std::integral_constant<int, 1>{});
-  else if (wave < 6) run_chunks(std::integral_constant<int, 2>{});
-  else run_chunks(std::integral_constant<int, 3>{});
+  bool left;  // the same in every wave (a workgroup-uniform decision at the same point)
+  if (wave < 2) left = run_chunks(std::integral_constant<int, 0>{});
+  else if (wave < 4) left = run_chunks(std::integral_constant<int, 1>{});
+  else if (wave < 6) left = run_chunks(std::integral_constant<int, 2>{});
+  else left = run_chunks(std::integral_constant<int, 3>{});
+  if (left) return;
 
   __syncthreads();  // the P plane is free: reduce du over the 16 token groups
   *reinterpret_cast<float2 *>(&sm.P[tg][2 * cp]) = make_float2(du0, du1);
@@ -752,9 +782,11 @@ hipError_t launch_wkv6_backward_chunked(const BwdParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL(wkv6_bwdc_state_kernel, dim3(p.H, p.B), dim3(kThreads), sizeof(Smem1), s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!p.chunk_states) {
+    hipLaunchKernelGGL(wkv6_bwdc_state_kernel, dim3(p.H, p.B), dim3(kThreads), sizeof(Smem1), s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(wkv6_bwdc_kernel, dim3(p.H, p.B), dim3(kThreads), sizeof(Smem2), s, p);
   return hipGetLastError();
 }

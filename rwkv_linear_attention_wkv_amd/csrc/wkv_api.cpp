@@ -125,7 +125,8 @@ wkv_status backward6(const char *fn, int B, int T, int H, int N, const void *r, 
                      const void *w, wkv_dtype in_dtype, const float *u, const float *dy, const float *state_in,
                      const int32_t *state_map, int n_state, const float *state_final, const float *d_state_out,
                      float *dr, float *dk, float *dv, float *dw, float *du, float *du_rows, bool use_scratch,
-                     float *d_state_in, wkv_algo algo, int32_t *dev_status, void *stream) {
+                     float *d_state_in, const float *chunk_states, wkv_algo algo, int32_t *dev_status,
+                     void *stream) {
   wkv_status st = check_dense56(fn, B, T, H, N, r, k, v, w, in_dtype, u, dr, state_in, state_map, n_state,
                                 nullptr, algo);
   if (st != WKV_OK) return st;
@@ -167,6 +168,10 @@ wkv_status backward6(const char *fn, int B, int T, int H, int N, const void *r, 
   // (decays beyond the chunked form's exponent range, rejected state_map rows).
   const bool chunked = T > 0 && in_dtype == WKV_BF16 && (int64_t)H * N <= kChunkedMaxRow &&
                        (algo == WKV_ALGO_CHUNKED || (algo == WKV_ALGO_AUTO && T >= kChunk));
+  if (chunked && T > kChunk && chunk_states) {
+    REQUIRE(aligned(chunk_states, 16), "%s: chunk_states must be 16-byte aligned", fn);
+    p.chunk_states = chunk_states;  // the forward's saved states: no state pass
+  }
   if (chunked) {
     const hipError_t e = wkv::launch_wkv6_backward_chunked(p, hs);
     if (e != hipSuccess) return launched(e, fn);
@@ -302,6 +307,41 @@ wkv_status wkv6_forward(int B, int T, int H, int N, const void *r, const void *k
                  n_state, state_out, algo, dev_status, stream);
 }
 
+wkv_status wkv6_forward_train(int B, int T, int H, int N, const void *r, const void *k, const void *v,
+                              const void *w, wkv_dtype in_dtype, const float *u, void *y, wkv_dtype out_dtype,
+                              const float *state_in, const int32_t *state_map, int n_state, float *state_out,
+                              float *chunk_states, int32_t *dev_status, void *stream) {
+  const char *fn = "wkv6_forward_train";
+  wkv_status st = check_dense56(fn, B, T, H, N, r, k, v, w, in_dtype, u, y, state_in, state_map, n_state,
+                                state_out, WKV_ALGO_CHUNKED);
+  if (st != WKV_OK) return st;
+  if (!dtype_ok(out_dtype)) return fail(WKV_ERR_UNSUPPORTED, "%s: unknown output dtype %d", fn, out_dtype);
+  REQUIRE(!dev_status || aligned(dev_status, 4), "%s: dev_status must be 4-byte aligned", fn);
+  if (T > kChunk)
+    REQUIRE(chunk_states && aligned(chunk_states, 16),
+            "%s: chunk_states must be a non-NULL, 16-byte aligned device array (T > %d)", fn, kChunk);
+  if (T == 0)  // no tokens, no chunk states: the plain forward (state_out from state_in)
+    return dense56(6, B, T, H, N, r, k, v, w, in_dtype, WKV_LAYOUT_BTHN, u, y, out_dtype, state_in, state_map,
+                   n_state, state_out, WKV_ALGO_AUTO, dev_status, stream);
+  wkv::ScanParams p{};
+  p.units = B;
+  p.T = T;
+  p.H = H;
+  p.r = r; p.k = k; p.v = v; p.w = w;
+  p.u = u;
+  p.y = y;
+  p.y_bf16 = out_dtype == WKV_BF16;
+  const long C = (long)H * N;
+  p.row_stride = (long)T * C; p.tok_stride = C; p.head_stride = N;
+  p.state_in = state_in;
+  p.state_map = state_map;
+  p.n_state = n_state;
+  p.state_out = state_out;
+  p.dev_status = dev_status;
+  p.chunk_states = chunk_states;
+  return launched(wkv::launch_wkv6_chunked_save(p, static_cast<hipStream_t>(stream)), fn);
+}
+
 wkv_status wkv7_forward_ex(int B, int T, int H, int N, const void *r, const void *w, const void *k, const void *v,
                            const void *a, const void *b, wkv_dtype in_dtype, wkv_layout layout, void *y,
                            wkv_dtype out_dtype, const float *state_in, const int32_t *state_map, int n_state,
@@ -378,19 +418,19 @@ wkv_status wkv6_backward(int B, int T, int H, int N, const void *r, const void *
                          const float *d_state_out, float *dr, float *dk, float *dv, float *dw, float *du,
                          float *du_rows, float *d_state_in, int32_t *dev_status, void *stream) {
   return backward6("wkv6_backward", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map, n_state,
-                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, WKV_ALGO_AUTO,
-                   dev_status, stream);
+                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, nullptr,
+                   WKV_ALGO_AUTO, dev_status, stream);
 }
 
 wkv_status wkv6_backward_ex(int B, int T, int H, int N, const void *r, const void *k, const void *v,
                             const void *w, wkv_dtype in_dtype, const float *u, const float *dy,
                             const float *state_in, const int32_t *state_map, int n_state,
                             const float *state_final, const float *d_state_out, float *dr, float *dk, float *dv,
-                            float *dw, float *du, float *du_rows, float *d_state_in, wkv_algo algo,
-                            int32_t *dev_status, void *stream) {
+                            float *dw, float *du, float *du_rows, float *d_state_in,
+                            const float *chunk_states, wkv_algo algo, int32_t *dev_status, void *stream) {
   return backward6("wkv6_backward_ex", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map, n_state,
-                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, algo, dev_status,
-                   stream);
+                   state_final, d_state_out, dr, dk, dv, dw, du, du_rows, false, d_state_in, chunk_states, algo,
+                   dev_status, stream);
 }
 
 wkv_status wkv6_backward_noalloc(int B, int T, int H, int N, const void *r, const void *k, const void *v,
@@ -400,8 +440,8 @@ wkv_status wkv6_backward_noalloc(int B, int T, int H, int N, const void *r, cons
                                  float *dv, float *dw, float *du, float *d_state_in, int32_t *dev_status,
                                  void *stream) {
   return backward6("wkv6_backward_noalloc", B, T, H, N, r, k, v, w, in_dtype, u, dy, state_in, state_map,
-                   n_state, state_final, d_state_out, dr, dk, dv, dw, du, nullptr, true, d_state_in, WKV_ALGO_AUTO,
-                   dev_status, stream);
+                   n_state, state_final, d_state_out, dr, dk, dv, dw, du, nullptr, true, d_state_in, nullptr,
+                   WKV_ALGO_AUTO, dev_status, stream);
 }
 
 wkv_status wkv6_forward_varlen_ex(int num_slots, int H, int N, const int32_t *lengths, int max_len,

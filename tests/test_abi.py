@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(nat.SIGNATURES)
