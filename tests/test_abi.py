@@ -278,3 +278,28 @@ def test_v6_backward_validation(lib):
     assert b"state_final" in lib.wkv_last_error()
     assert bwd(lib, sm=P) == 1                 # state_map without state_in
     assert bwd(lib, si=P, ns=3) == 1           # n_state must be 1 or B without a map
+
+
+def test_train_forward_and_saved_states_validation(lib):
+    """wkv6_forward_train needs bf16 inputs and, past one chunk, an aligned chunk_states array;
+    wkv6_backward_ex checks the alignment of the saved states it is handed (host only)."""
+    E, U = nat.WKV_ERR_INVALID_ARG, nat.WKV_ERR_UNSUPPORTED
+
+    def train(B=2, T=100, H=2, N=64, dt=1, y=P, odt=0, cs=P):
+        return lib.wkv6_forward_train(B, T, H, N, P, P, P, P, dt, P, y, odt, None, None, 0, None, cs, None, None)
+
+    assert train(dt=0) == U and b"bf16" in lib.wkv_last_error()
+    assert train(cs=None) == E and b"chunk_states" in lib.wkv_last_error()
+    assert train(cs=MIS) == E and b"chunk_states" in lib.wkv_last_error()
+    assert train(odt=5) == U and b"output dtype" in lib.wkv_last_error()
+    assert train(N=32) == U and b"head size" in lib.wkv_last_error()
+    assert train(y=MIS) == E
+    assert train(T=0, cs=None) == nat.WKV_OK  # no tokens, no states to save
+
+    def bwd(T=100, dt=1, cs=P, algo=nat.WKV_ALGO_AUTO):
+        return lib.wkv6_backward_ex(2, T, 2, 64, P, P, P, P, dt, P, P, None, None, 0, None, None, P, P, P, P, P, P,
+                                    None, cs, algo, None, None)
+
+    assert bwd(cs=MIS) == E and b"chunk_states" in lib.wkv_last_error()
+    assert bwd(algo=7) == U and b"algorithm" in lib.wkv_last_error()
+    assert bwd(dt=0, algo=nat.WKV_ALGO_CHUNKED) == U and b"bf16" in lib.wkv_last_error()
