@@ -549,6 +549,7 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
     __syncthreads();  // B2
     // ---------- phase 3a: products that do not need Gh; the G waves form Gh
     f32x16 acc[2] = {f32x16{}, f32x16{}};  // the wave's output blocks (value or key blocks 0 / 1)
+    float sv[2][16];  // G waves: S_c at their G tile elements, in fp32, for E_c
     if constexpr (ROLE == 0) {
       const int sb = wave;
       // A[t][s] = rb_t . kt_s (s < t), blocks tb >= sb; dV += A^T dY
@@ -599,6 +600,27 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int l32 = ln & 31, hh = ln >> 5;
+      // S_c at the G tile's elements for E_c in phase 3b, loaded in fp32 from where the
+      // prefetch took it (the saved states, the dr rows of the chunk before, or state_in) while
+      // this role has little else to do: two-byte reads of its hi / lo planes in 3b cost more
+      {
+        const float *sp = nullptr;
+        long sr = 0;
+        if (c >= 1) {
+          sp = sbase + (long)(c - 1) * schunk;
+          sr = srow;
+        } else if (row_in >= 0) {
+          sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead);
+          sr = kHead;
+        }
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = 32 * gi + 8 * (e >> 2) + 4 * hh + (e & 3), col = 32 * jb + l32;
+            sv[jb][e] = sp ? sp[row * sr + col] : 0.f;
+          }
+      }
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -637,7 +659,7 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = 32 * gi + 8 * (e >> 2) + 4 * hh + (e & 3), col = 32 * jb + l32;
-          const float s = bf16_lo(sm.pl[SCH][row][col]) + bf16_lo(sm.pl[SCL][row][col]);
+          const float s = sv[jb][e];
           ep[e] = fmaf(s, G[jb][e], ep[e]);
         }
       }
@@ -704,8 +726,6 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
             }
             stg[row * PFS + col] = val;
           }
-          // four elements' LDS reads in flight at a time (more would hold registers for all 32)
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
