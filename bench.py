@@ -343,7 +343,7 @@ def workload_wkv7(args):
                     if algo == "chunked" else "fp32 vector ALU (token-sequential generalized delta rule)"),
         "data": "synthetic (seeded numpy PCG64; bf16 r,w,k,v,a,b with a = -kappa, b = kappa*beta; initial states ~ N(0,0.1))",
         "config": {"workload": f"WKV7 forward B={B} T={T} H={H} N={N}, bf16 inputs, fp32 state and output",
-                   "B": B, "T": T, "H": H, "N": N, "algo": algo, "saved_states": bool(saved and algo == "chunked"),
+                   "B": B, "T": T, "H": H, "N": N, "algo": algo,
                    "global_batch": B, "seq_len": T,
                    "parallelism": "single GPU"},
         "cpu": cpu,
