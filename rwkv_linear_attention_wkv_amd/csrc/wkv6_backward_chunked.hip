@@ -37,7 +37,8 @@
 // sweeps then redo the whole unit.
 //
 // Precision.  Operands that are not exact bf16 inputs are split into bf16 hi + lo and each
-// product is hi*hi + hi*lo + lo*hi (two products against the exact v), fp32 accumulation.
+// product is hi*hi + hi*lo + lo*hi (two products against the exact v), fp32 accumulation;
+// E_c is formed in fp32 from the state as stored.
 #include <atomic>
 #include <type_traits>
 
@@ -51,7 +52,7 @@ namespace {
 
 constexpr int L = 64;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// Cache policy of the gradient stores: non-temporal (streamed past the caches; 5% faster than
+// Cache policy of the gradient stores: non-temporal (streamed past the caches; 3-4% faster than
 // default stores on B=8 T=4096 H=32, which compete with the next chunk's loads).
 constexpr int kStoreNT = 2;
 constexpr int kThreads = 512;
@@ -74,7 +75,8 @@ struct alignas(16) Smem2 {
   float2 wtot[8][32];    // log2-decay total of each wave's tokens, per channel pair
   float dlt[8][kHead];   // dlam: each wave's token-group total
 };
-// the dlam terms of a chunk reuse the S_c and Gh planes (free by then)
+// In phases 4 and 5 the dlam terms of a chunk reuse the S_c and Gh planes, and the staged dr,
+// dk, dv the rb, kt and dy planes (free by then), each as one fp32 plane of stride PFS
 static_assert(sizeof(float) * L * PFS <= 2 * sizeof(uint16_t) * L * RS, "fp32 plane fits two bf16 planes");
 
 struct alignas(16) Smem1 {
