@@ -89,10 +89,12 @@ def test_forward_train_rejects_what_it_cannot_save():
     assert b"chunk_states" in wkv._lib.wkv_last_error()
 
 
-@pytest.mark.parametrize("B,T,H,seed", [(2, 65, 2, 1), (2, 300, 2, 2), (3, 1000, 2, 3), (8, 4096, 32, 0)])
+@pytest.mark.parametrize("B,T,H,seed", [(2, 65, 2, 1), (2, 128, 2, 4), (2, 300, 2, 2), (3, 1000, 2, 3),
+                                        (1, 4097, 3, 5), (64, 128, 8, 6), (8, 4096, 32, 0)])
 def test_backward_with_saved_states(B, T, H, seed):
-    """Every unit against the oracle, and close to the backward that computes the states itself
-    (B=8 T=4096 H=32 is the headline shape)."""
+    """Every unit against the oracle, and close to the backward that computes the states itself:
+    two whole chunks, ragged last chunks (one token at T=4097), 512 (row, head) units at B=64
+    H=8, and B=8 T=4096 H=32 (the headline shape)."""
     inp = wkv6_inputs(B, T, H, 64, seed=seed, init_state=B if seed else None)
     up = wkv6_upstream(B, T, H, 64, seed=seed + 100)
     args = _args(inp)
