@@ -173,3 +173,20 @@ def test_backward_with_saved_states_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_backward_wide_rows():
+    """H=256 (C=16384 channels, 64 KiB per bf16 token row): the chunked passes' row strides and
+    store offsets at a width far past the headline's, with and without saved states."""
+    inp = wkv6_inputs(1, 130, 256, 64, seed=91, init_state=1)
+    up = wkv6_upstream(1, 130, 256, 64, seed=92)
+    args = _args(inp)
+    st = dev(inp["state"])
+    _, S, cs = wkv.wkv6_forward_train(*args, state=st)
+    ds = dev(up["d_state"])
+    own = wkv.wkv6_backward(*args, dev(up["dy"]), state=st, state_final=S, d_state=ds)
+    got = wkv.wkv6_backward(*args, dev(up["dy"]), state=st, state_final=S, d_state=ds, chunk_states=cs)
+    torch.cuda.synchronize()
+    ref = _oracle_bwd(inp, up, state=inp["state"])
+    _check(own, ref, "H=256 own states")
+    _check(got, ref, "H=256 saved states")
