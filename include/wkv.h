@@ -193,10 +193,10 @@ WKV_API wkv_status wkv6_forward_ex(int B, int T, int H, int N,
 
 /*
  * v6 forward for training: the chunked form (bf16 inputs, [B,T,H*N] rows), which
- * also saves the state at every chunk boundary for wkv6_backward_ex.  The
- * rwkv_ops page's RWKV6_OP is the training operator of this recurrence; the
- * saved states are the ones its forward reaches at the start of each 64-token
- * chunk.
+ * also saves the state at every chunk boundary for wkv6_backward_ex.  (The
+ * rwkv_ops page's RWKV6_OP is the gradient-capable operator of this recurrence;
+ * handing the forward's chunk-start states to the backward is this library's
+ * own arrangement, so that the backward need not recompute them.)
  *   chunk_states [B,H,ceil(T/64)-1,N,N] fp32 DEVICE, 16-byte aligned (may be
  *                NULL when T <= 64): entry c-1 is the state after token 64c-1
  *                ([key][value], c = 1 .. ceil(T/64)-1), in fp32 as the kernel
