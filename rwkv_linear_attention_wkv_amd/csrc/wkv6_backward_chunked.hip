@@ -198,11 +198,16 @@ __device__ __forceinline__ void mm_za(f32x16 &acc, const f32x16 &z, const uint16
 // satisfy row > col (keep_row_gt) or row < col, zero elsewhere.
 template <bool ROW_GT>
 __device__ __forceinline__ void mask_diag(f32x16 &z, int lane) {
-  const int col = lane & 31, h = lane >> 5;
+  // Element e holds row - 4h = 8 (e / 4) + e % 4 (an immediate) against dd = col - 4h.  dd comes
+  // from an opaque copy of the lane index, so the 16 conditions are formed here, in every chunk,
+  // instead of being held across the chunk loop in scalar register pairs.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int dd = (ln & 31) - 4 * (ln >> 5);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int row = 8 * (e >> 2) + 4 * h + (e & 3);
-    const bool keep = ROW_GT ? row > col : row < col;
+    const int ce = 8 * (e >> 2) + (e & 3);
+    const bool keep = ROW_GT ? ce > dd : ce < dd;
     z[e] = keep ? z[e] : 0.f;
   }
 }
@@ -561,11 +566,15 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
         f32x16 Z = {};
         mm_nn(Z, sm.pl[RBH], sm.pl[RBL], sm.pl[KTH], sm.pl[KTL], 32 * tb, 32 * sb, lane);
         if (tb == sb) {  // keep s < t; the bonus r_t . (u * k_t) on s == t gives dV its b_s dy_s
-          const int col = lane & 31, h2 = lane >> 5;
+          // (the conditions as in mask_diag; on the diagonal row == col, one bonus read per lane)
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          const int col = ln & 31, dd = col - 4 * (ln >> 5);
+          const float bonc = sm.bon[32 * tb + col];
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int row = 8 * (e >> 2) + 4 * h2 + (e & 3);
-            Z[e] = row > col ? Z[e] : (row == col ? sm.bon[32 * tb + row] : 0.f);
+            const int ce = 8 * (e >> 2) + (e & 3);
+            Z[e] = ce > dd ? Z[e] : (ce == dd ? bonc : 0.f);
           }
         }
 #pragma unroll
@@ -606,21 +615,30 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
       // prefetch took it (the saved states, the dr rows of the chunk before, or state_in) while
       // this role has little else to do: two-byte reads of its hi / lo planes in 3b cost more
       {
-        const float *sp = nullptr;
+        const float *sp = p.dr;  // no state (c == 0 without state_in): a resource with no records
         long sr = 0;
+        int nrec = 0;
         if (c >= 1) {
           sp = sbase + (long)(c - 1) * schunk;
           sr = srow;
+          nrec = 0x7fffffff;
         } else if (row_in >= 0) {
           sp = p.state_in + ((long)row_in * p.H + h) * (kHead * kHead);
           sr = kHead;
+          nrec = 0x7fffffff;
         }
+        // One buffer resource at the state (reads past no records return zero), the lane's row
+        // and column as the vector offset, each element's row step as a scalar offset: no
+        // per-element 64-bit address arithmetic.  Offsets stay below 64 rows of the state.
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char *>(uniform64(reinterpret_cast<long>(sp))), 0,
+                                                          nrec, 0x00020000);
+        const int vo = (int)(((32 * gi + 4 * hh) * sr + l32) * 4);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int row = 32 * gi + 8 * (e >> 2) + 4 * hh + (e & 3), col = 32 * jb + l32;
-            sv[jb][e] = sp ? sp[row * sr + col] : 0.f;
+            const int so = __builtin_amdgcn_readfirstlane((int)((8 * (e >> 2) + (e & 3)) * sr * 4));
+            sv[jb][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo + 128 * jb, so, 0));
           }
       }
 #pragma unroll
@@ -703,12 +721,32 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
         const int col = 32 * ob + l32;
         const float uc = ob ? uh2 : ul;
         const uint32_t *rk = rkplane(sm);
+        // All of the column block's operands are read before any result is written: the
+        // compiler cannot tell the planes written below from the planes read, so reads
+        // interleaved with the writes would each wait for the LDS round trip in turn.
+        uint32_t wv[16];
+        float pv[16], dbv[16];
+        if constexpr (ROLE != 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row0 = 32 * blk + 8 * q + 4 * hh;  // rows row0 .. row0 + 3 of elements 4q .. 4q+3
+            const float4 db4 = *reinterpret_cast<const float4 *>(&sm.dbon[row0]);
+            dbv[4 * q] = db4.x;
+            dbv[4 * q + 1] = db4.y;
+            dbv[4 * q + 2] = db4.z;
+            dbv[4 * q + 3] = db4.w;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const int row = row0 + m;
+              wv[4 * q + m] = rk[row * RS + col];
+              // dk needs P_s, dr needs P_{t-1} (0 before the chunk's first token)
+              pv[4 * q + m] = ROLE == 1 ? sm.P[row][col] : sm.P[row ? row - 1 : 0][col];
+            }
+          }
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int row0 = 32 * blk + 8 * q + 4 * hh;  // rows row0 .. row0 + 3 of elements 4q .. 4q+3
-          float4 db4 = make_float4(0.f, 0.f, 0.f, 0.f);
-          if constexpr (ROLE != 0) db4 = *reinterpret_cast<const float4 *>(&sm.dbon[row0]);
-          const float dbv[4] = {db4.x, db4.y, db4.z, db4.w};
+          const int row0 = 32 * blk + 8 * q + 4 * hh;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const int e = 4 * q + m, row = row0 + m;
@@ -716,15 +754,13 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
             if constexpr (ROLE == 0) {  // dv (the bonus b_s dy_s is on A's diagonal)
               val = acc[ob][e];
             } else if constexpr (ROLE == 1) {  // dk = 2^-P_s dkt + u r_s db_s
-              const uint32_t w = rk[row * RS + col];
-              const float dkt = acc[ob][e] * __builtin_amdgcn_exp2f(-sm.P[row][col]);
-              val = fmaf(uc * bf16_lo(w), dbv[m], dkt);
-              T2[row * PFS + col] = bf16_hi(w) * dkt;
+              const float dkt = acc[ob][e] * __builtin_amdgcn_exp2f(-pv[e]);
+              val = fmaf(uc * bf16_lo(wv[e]), dbv[e], dkt);
+              T2[row * PFS + col] = bf16_hi(wv[e]) * dkt;
             } else {  // dr = 2^P_{t-1} drb + u k_t db_t
-              const uint32_t w = rk[row * RS + col];
-              const float drb = acc[ob][e] * __builtin_amdgcn_exp2f(row ? sm.P[row - 1][col] : 0.f);
-              val = fmaf(uc * bf16_hi(w), dbv[m], drb);
-              T1[row * PFS + col] = bf16_lo(w) * drb;
+              const float drb = acc[ob][e] * __builtin_amdgcn_exp2f(row ? pv[e] : 0.f);
+              val = fmaf(uc * bf16_hi(wv[e]), dbv[e], drb);
+              T1[row * PFS + col] = bf16_lo(wv[e]) * drb;
             }
             stg[row * PFS + col] = val;
           }
@@ -736,13 +772,21 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
     {
       int i = lane;
       asm volatile("" : "+v"(i));
+      // the token rows from an opaque vector copy of the wave index: one base address plus
+      // immediate offsets, where uniform per-token row addresses would each hold a scalar
+      // register (more than there are) across the chunk loop
+      int wv = wave;
+      asm volatile("" : "+v"(wv));
       const float Eend = sm.E[(c + 1) & 1][i];
       float s[8], xv[8];
       float run = 0.f;
 #pragma unroll
       for (int q = 7; q >= 0; --q) {
-        const int t = 8 * wave + q;
-        const float t1 = t < L - 1 ? T1[(t + 1) * PFS + i] : Eend;
+        const int t = 8 * wv + q;
+        // row t + 1 = 64 (read for the last token, then not used) is still inside the two
+        // bf16 planes that hold T1
+        const float t1n = T1[(t + 1) * PFS + i];
+        const float t1 = t < L - 1 ? t1n : Eend;
         run += t1 - T2[t * PFS + i];
         s[q] = run;
         xv[q] = bf16_lo(sm.pl[XR][t][i]);
