@@ -479,6 +479,10 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
     }
   }
   prefetch(nch - 1);
+  // Wait for the first chunk's words here, once: otherwise this path into the loop (the
+  // prefetch the newest memory operation) makes the compiler's merged waits at the top of the
+  // loop wait for everything in flight, the previous chunk's stores included, in every chunk.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   Stage st;
   for (int c = nch - 1; c >= 0; --c) {
     const int nvalid = min(L, T - c * L);
@@ -500,21 +504,25 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
       bn[t] = fmaf(r1 * u1, k1, r0 * u0 * k0);
       db[t] = fmaf(dy1[t], bf16_hi(vw[t]), dy0[t] * bf16_lo(vw[t]));
     }
+    {  // Sums over the 32 channel pairs of the half-wave, of all eight values at once: each of
+       // three exchange steps keeps half of the lane's values and adds the other lane's matching
+       // half, so lane group g = (lane / 4) % 8 ends with value g (the bonus of token g for g < 4,
+       // dy . v of token g - 4 above), and two DPP steps finish the sums.
+      // (lane bits from an opaque copy: formed here, not held across the loop as masks)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      float w4[4], w2[2];
+      const bool b4 = ln & 16, b3 = ln & 8, b2 = ln & 4;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {  // sums over the 32 channel pairs of the half-wave
-      bn[t] += xor1(bn[t]); db[t] += xor1(db[t]);
-      bn[t] += xor2(bn[t]); db[t] += xor2(db[t]);
-      bn[t] += xor_swz<4>(bn[t]); db[t] += xor_swz<4>(db[t]);
-      bn[t] += xor_swz<8>(bn[t]); db[t] += xor_swz<8>(db[t]);
-      bn[t] += xor_swz<16>(bn[t]); db[t] += xor_swz<16>(db[t]);
-      du0 = fmaf(bf16_lo(rw[t]) * bf16_lo(kw[t]), db[t], du0);
-      du1 = fmaf(bf16_hi(rw[t]) * bf16_hi(kw[t]), db[t], du1);
-    }
-    if (l32 == 0) {
+      for (int j = 0; j < 4; ++j) w4[j] = (b4 ? db[j] : bn[j]) + xor_swz<16>(b4 ? bn[j] : db[j]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        sm.bon[4 * tg + t] = bn[t];
-        sm.dbon[4 * tg + t] = db[t];
+      for (int j = 0; j < 2; ++j) w2[j] = (b3 ? w4[2 + j] : w4[j]) + xor_swz<8>(b3 ? w4[j] : w4[2 + j]);
+      float w1 = (b2 ? w2[1] : w2[0]) + xor_swz<4>(b2 ? w2[0] : w2[1]);
+      w1 += xor2(w1);
+      w1 += xor1(w1);
+      if ((ln & 3) == 0) {
+        const int g = (ln >> 2) & 7;
+        (g < 4 ? sm.bon : sm.dbon)[4 * tg + (g & 3)] = w1;
       }
     }
 #pragma unroll
@@ -535,6 +543,15 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
       }
       if (wave == 0 && !hh)
         *reinterpret_cast<float2 *>(&sm.dl[2 * cp]) = make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
+      {  // du += r k (dy . v) over the thread's tokens, the dy . v sums as stage A left them
+        const float4 d4 = *reinterpret_cast<const float4 *>(&sm.dbon[4 * tg]);
+        const float dbt[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          du0 = fmaf(bf16_lo(rw[t]) * bf16_lo(kw[t]), dbt[t], du0);
+          du1 = fmaf(bf16_hi(rw[t]) * bf16_hi(kw[t]), dbt[t], du1);
+        }
+      }
       float c0 = pre0, c1 = pre1;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -800,11 +817,11 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
           float *outp = pk == 0 ? p.dr : (pk == 1 ? p.dk : p.dv);
           const int row = 32 * (k6 & 1) + (tid >> 4), c4 = tid & 15;
           const float4 v = *reinterpret_cast<const float4 *>(&stg[row * PFS + 4 * c4]);
-          const auto ro = __builtin_amdgcn_make_buffer_rsrc(outp + uniform64(tok0), 0, 0x7fffffff, 0x00020000);
+          // (rows past the chunk's last valid token lie past the resource's records: dropped)
+          const auto ro = __builtin_amdgcn_make_buffer_rsrc(outp + uniform64(tok0), 0,
+                                                            (int)((uint32_t)(nvalid - 1) * C4 + 4u * kHead), 0x00020000);
           const u32x4 w4 = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-          if (row < nvalid)
-            __builtin_amdgcn_raw_buffer_store_b128(w4, ro, (int)((uint32_t)row * C4 + 16u * (uint32_t)c4), 0,
-                                                   kStoreNT);
+          __builtin_amdgcn_raw_buffer_store_b128(w4, ro, (int)((uint32_t)row * C4 + 16u * (uint32_t)c4), 0, kStoreNT);
         }
       }
       sm.dlt[wave][i] = run;
@@ -812,13 +829,17 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
       float carry = 0.f;
 #pragma unroll
       for (int w = 7; w > 0; --w) carry += w > wave ? sm.dlt[w][i] : 0.f;
-      const auto rw2 = __builtin_amdgcn_make_buffer_rsrc(p.dw + uniform64(tok0), 0, 0x7fffffff, 0x00020000);
+      // The resource ends at the chunk's last valid token row, so the stores of rows past it are
+      // dropped and every path issues the same eight stores: with a branch per token, the
+      // compiler's count of memory operations in flight would make the next chunk's first waits
+      // for its prefetched words wait for these stores as well.
+      const auto rw2 = __builtin_amdgcn_make_buffer_rsrc(p.dw + uniform64(tok0), 0,
+                                                         (int)((uint32_t)(nvalid - 1) * C4 + 4u * kHead), 0x00020000);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int t = 8 * wave + q;
-        if (t < nvalid)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-fast_exp(xv[q]) * (s[q] + carry)), rw2, i * 4,
-                                                (int)((uint32_t)t * C4), kStoreNT);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-fast_exp(xv[q]) * (s[q] + carry)), rw2, i * 4,
+                                              (int)((uint32_t)t * C4), kStoreNT);
       }
     }
   }
