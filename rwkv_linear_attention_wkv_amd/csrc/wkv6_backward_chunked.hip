@@ -569,7 +569,6 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
         *reinterpret_cast<uint32_t *>(&sm.pl[KTL][tau][2 * cp]) = lo;
       }
     }
-    if (c > 0) prefetch(c - 1);  // in flight during the products
     __syncthreads();  // B2
     // ---------- phase 3a: products that do not need Gh; the G waves form Gh
     f32x16 acc[2] = {f32x16{}, f32x16{}};  // the wave's output blocks (value or key blocks 0 / 1)
@@ -674,6 +673,14 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
         }
     }
     __syncthreads();  // B3
+    // The next chunk's rows.  Issuing a wave's 28 loads blocks it for a few thousand cycles while
+    // the requests queue (all eight waves issuing them at the end of stage B took about 3,500
+    // cycles of every chunk), so each role issues them where it would otherwise wait: the dkt
+    // and drb waves here (the drb waves have no work in 3b), the dV and G waves after B4.  They
+    // arrive during phases 4 and 5, and the registers they land in are free in 3a.
+    if constexpr (ROLE == 1 || ROLE == 2) {
+      if (c > 0) prefetch(c - 1);
+    }
     // ---------- phase 3b: the products with Gh; G_c and E_c
     if constexpr (ROLE == 0) {
       const int sb = wave;
@@ -716,6 +723,9 @@ __global__ void __launch_bounds__(kThreads) wkv6_bwdc_kernel(BwdParams p) {
       }
     }
     __syncthreads();  // B4
+    if constexpr (ROLE == 0 || ROLE == 3) {
+      if (c > 0) prefetch(c - 1);
+    }
     // ---------- phase 4: outputs and the dlam terms (T1 = rb drb in the Gh planes, T2 = kt dkt in
     // the S_c planes, both fp32 [token][key])
     float *T1 = fplane(sm, GHH), *T2 = fplane(sm, SCH);
