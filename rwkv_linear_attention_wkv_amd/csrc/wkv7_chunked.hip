@@ -170,12 +170,13 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   };
   enum { LR = 0, LW, LK, LV, LA, LB };
   uint32_t ld[6][4];  // words of r, w, k, v, a, b; rows past the end read as zero
-  // The next chunk's words are requested as soon as this chunk's have been staged.
-  auto prefetch = [&](int c) __attribute__((always_inline)) {
+  // The next chunk's words of arrays n0 .. n1 - 1 (the chunk loop issues them where each role
+  // can wait: see there).
+  auto prefetch = [&](int c, int n0, int n1) __attribute__((always_inline)) {
     const unsigned long long off = (unsigned long long)uniform64((base + (long)c * L * ts) * 2);
     const void *src[6] = {p.r, p.w, p.k, p.v, p.a, p.b};
 #pragma unroll
-    for (int n = 0; n < 6; ++n) {
+    for (int n = n0; n < n1; ++n) {
       const auto rs = rsrc_at(src[n], off);
 #pragma unroll
       for (int t = 0; t < 4; ++t) ld[n][t] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)roff[t], 0, 0);
@@ -198,7 +199,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
     lower1 = __int_as_float(__builtin_amdgcn_ds_bpermute(lane_x32, __float_as_int(run1)));
     if (hh) sm.wtot[wave][cp] = make_float2(run0 + lower0, run1 + lower1);
   };
-  // stage, second half: prefix, operands, V^T; then the next chunk's loads
+  // stage, second half: prefix, operands, V^T
   auto stage2 = [&](int c) __attribute__((always_inline)) {
     float pre0 = hh ? lower0 : 0.f, pre1 = hh ? lower1 : 0.f, tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
@@ -261,7 +262,6 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
         __builtin_amdgcn_perm(vw[1], vw[0], 0x05040100u), __builtin_amdgcn_perm(vw[3], vw[2], 0x05040100u));
     *reinterpret_cast<uint2 *>(&sm.vt[2 * cp + 1][4 * tg]) = make_uint2(
         __builtin_amdgcn_perm(vw[1], vw[0], 0x07060302u), __builtin_amdgcn_perm(vw[3], vw[2], 0x07060302u));
-    if (c + 1 < nchunks) prefetch(c + 1);
   };
 
   // ---------------- MFMA building blocks
@@ -572,18 +572,32 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   // ROLE 0 / 1: output waves of token block 0 / 1; 2: RHS waves; 3: state waves.
   auto run_chunks = [&](auto role_c) __attribute__((always_inline)) {
     constexpr int ROLE = decltype(role_c)::value;
-    prefetch(0);
+    prefetch(0, 0, 6);
     stage1(0);
     for (int c = 0; c < nchunks; ++c) {
       __syncthreads();  // wave totals posted; the previous chunk's readers are done
       stage2(c);
+      // The next chunk's 24 words per thread.  Issuing loads blocks a wave for as long as the
+      // requests queue (about 1,300 cycles per chunk with every wave issuing all of them here),
+      // so each role issues them where it has time: the output and RHS waves after the third
+      // barrier, where the state waves solve and they wait; the state waves, busy in every
+      // phase, half here and half at the end of their next phase.
+      const bool more = c + 1 < nchunks;
+      if constexpr (ROLE == 3) {
+        if (more) prefetch(c + 1, 0, 3);
+      }
       __syncthreads();  // operands of chunk c in place
       const bool direct = __builtin_amdgcn_readfirstlane(sm.direct) != 0;
-      const bool more = c + 1 < nchunks;
       if (!direct) {
         if constexpr (ROLE < 3) rhs_a();
         else state_a();
+        if constexpr (ROLE == 3) {
+          if (more) prefetch(c + 1, 3, 6);
+        }
         __syncthreads();
+        if constexpr (ROLE < 3) {
+          if (more) prefetch(c + 1, 0, 6);
+        }
         if constexpr (ROLE < 2) {
           out_a(std::integral_constant<int, ROLE>{});
           out_b(std::integral_constant<int, ROLE>{});
@@ -594,6 +608,11 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
         if constexpr (ROLE < 2) out_c(std::integral_constant<int, ROLE>{}, c);
         else if constexpr (ROLE == 3) state_c();
       } else {
+        if constexpr (ROLE < 3) {
+          if (more) prefetch(c + 1, 0, 6);
+        } else {
+          if (more) prefetch(c + 1, 3, 6);
+        }
         if constexpr (ROLE == 3) direct_chunk_a();
         __syncthreads();
         direct_chunk_b(c);
