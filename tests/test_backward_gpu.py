@@ -259,3 +259,43 @@ def test_backward_long_sequence_dw(algo):
     got = _gpu(inp, up, state=inp["state"], algo=algo)
     torch.cuda.synchronize()
     _check(got, _oracle(inp, up, state=inp["state"]), f"T=16384 {algo}", _bounds(algo, "bf16", 16384))
+
+
+@pytest.mark.parametrize("T,algo,saved", [(100, "auto", False), (100, "auto", True), (130, "auto", True),
+                                          (65, "auto", False), (100, "scan", False)])
+def test_backward_writes_stay_inside_the_outputs(T, algo, saved):
+    """The chunked backward stores a ragged last chunk's rows through buffer resources that end at
+    its last token (the rows past it are dropped, not branched around).  The last batch row's
+    padding rows lie past the end of dr, dk, dv and dw, so each output is handed over at the head
+    of a larger buffer whose tail holds a canary: the tail must come back untouched and the
+    gradients bitwise equal to the same call on exactly sized outputs."""
+    B, H, N = 2, 2, 64
+    C = H * N
+    inp = wkv6_inputs(B, T, H, N, seed=900 + T, dtype="bf16", init_state=B)
+    up = wkv6_upstream(B, T, H, N, seed=950 + T)
+    r, k, v, x = (dev(inp[n]) for n in ("r", "k", "v", "x"))
+    u, st, dy, dS = dev(inp["u"]), dev(inp["state"]), dev(up["dy"]), dev(up["d_state"])
+    cs = None
+    if saved:
+        _, S_final, cs = wkv.wkv6_forward_train(r, k, v, x, u, H, state=st)
+    else:
+        _, S_final = wkv.wkv6_forward(r, k, v, x, u, H, state=st, algo="scan")
+    ref = wkv.wkv6_backward(r, k, v, x, u, H, dy, state=st, state_final=S_final, d_state=dS, algo=algo,
+                            chunk_states=cs)
+    n, tail = B * T * C, CHUNK * C  # a whole chunk of rows past the end
+    canary = 0x7FBADBAD
+    bufs = [torch.full((n + tail,), canary, dtype=torch.int32, device="cuda").view(torch.float32) for _ in range(4)]
+    du = torch.empty((C,), dtype=torch.float32, device="cuda")
+    du_rows = torch.empty((B, C), dtype=torch.float32, device="cuda")
+    d_state_in = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
+    p = wkv._ptr
+    wkv.check(wkv._lib.wkv6_backward_ex(
+        B, T, H, N, p(r), p(k), p(v), p(x), wkv._dtype_code(r), p(u), p(dy), p(st), None, B, p(S_final), p(dS),
+        *(p(b) for b in bufs), p(du), p(du_rows), p(d_state_in), p(cs) if cs is not None else None,
+        wkv._ALGOS[algo], None, wkv._stream(r)))
+    torch.cuda.synchronize()
+    for name, b, g in zip(("dr", "dk", "dv", "dw"), bufs, ref[:4]):
+        t = b[n:].view(torch.int32)
+        assert bool((t == canary).all()), f"{name}: {int((t != canary).sum())} elements past the output written"
+        assert torch.equal(b[:n].view(B, T, C), g), f"{name}: differs from the exactly sized call"
+    assert torch.equal(du, ref[4]) and torch.equal(d_state_in, ref[5])
