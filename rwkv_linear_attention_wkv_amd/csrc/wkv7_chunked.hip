@@ -40,10 +40,11 @@
 //           LDS (fp32);
 //           waves 4 .. 7 (one 32 x 32 tile of the fp32 state each): H += Kt^T V, and waves
 //           4 .. 6 one 32 x 32 block of M each, to LDS (fp32).  [barrier]
-//   solve   waves 4 .. 7: value columns 16 (w - 4) + 2m, +1, eight lanes (one per residue
-//           of the token index mod 8) hold their rows; each final row is broadcast to them
-//           and added to the later rows; SA^T to LDS as bf16 hi / lo.  Meanwhile, on the matrix cores,
-//           waves 0, 1 (token block 0 / 1) form Y^T = H0^T Rb^T + V^T Grk^T, with the causal
+//   solve   waves 4 .. 7: value columns 16 (w - 4) + 4g .. +3, sixteen lanes (one per
+//           residue of the token index mod 16) hold their rows; each final row is broadcast
+//           to them and added to the later rows; SA^T to LDS as bf16 hi / lo.
+//           Meanwhile, on the matrix cores, waves 0, 1 (token block 0 / 1) form
+//           Y^T = H0^T Rb^T + V^T Grk^T, with the causal
 //           32 x 32 blocks Grk^T = Kt Rb^T formed in registers and used from there (the
 //           accumulator layout is the operand layout, with the token order permuted
 //           alike on the other side), and the blocks Grb^T = Bt Rb^T.  [barrier]
@@ -80,7 +81,7 @@ struct alignas(16) Smem7 {
   // fp32 rows padded to 68 floats, so that 32 lanes writing 32 consecutive rows spread over
   // the banks
   float rhs[L][SFS];           // RHS [token][col]; with mp: the fp32 state of a direct chunk
-  float mp[L][SFS];            // M[8u + p][s] at [s][8 p + u] (column s of M for the solve)
+  float mp[L][SFS];            // M[16u + p][s] at [s][4 p + u] (column s of M for the solve)
   float pl[kHead];             // 2^P_{L-1} per key row
   float2 wtot[8][32];          // log2-decay total of each wave, per channel pair
   int direct;
@@ -100,6 +101,12 @@ __device__ __forceinline__ float bcast4(float x, int q) {
     case 2: return bcast4_c<2>(x);
     default: return bcast4_c<3>(x);
   }
+}
+
+// Lane Q of each row of 16 lanes to the whole row (DPP row_newbcast).
+template <int Q>
+__device__ __forceinline__ float bcast16_c(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + Q, 0xF, 0xF, false));
 }
 
 // f(integral_constant<int, I>) for I = I0 .. N - 1, so that every step's indices are
@@ -425,78 +432,62 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int t = 32 * tb + 8 * (e >> 2) + 4 * hh + (e & 3);
-          sm.mp[s][8 * (4 * hh + (e & 3)) + 4 * tb + (e >> 2)] = s < t ? mm[e] : 0.f;  // t % 8, t / 8
+          sm.mp[s][4 * (t & 15) + (t >> 4)] = s < t ? mm[e] : 0.f;
         }
       }
     }
   };
 
   // forward substitution (I - M) SA = RHS on the four state waves, right-looking: lane
-  // 8m + p of state wave sw owns value columns 16 sw + 2m and 16 sw + 2m + 1 and the rows
-  // t = 8u + p (u = 0..7), which start as RHS; once row s is final, its owner hands SA[s]
-  // to the column pair's eight lanes and each adds M[t][s] SA[s] to its later rows.
-  // Holding two columns per lane halves the M values each lane reads per step (the
-  // lanes of one row residue all read the same column of M), which had kept the LDS busy
-  // for most of the solve.  Column s of M is read kPF steps ahead.
+  // 16g + p of state wave sw owns value columns 16 sw + 4g .. +3 and the rows t = 16u + p
+  // (u = 0..3), which start as RHS; once row s is final, its owner hands SA[s] to the
+  // sixteen lanes of its DPP row in one broadcast per column, and each adds M[t][s] SA[s]
+  // to its later rows.  The lanes of one row residue read the same column of M, four
+  // values per step.  Column s of M is read kPF steps ahead.
   auto solve = [&]() __attribute__((always_inline)) {
-    const bool upper_quad = lane & 4;
     // Per-lane bases formed here from an opaque copy of the lane index: every access below
     // is one of them plus a constant offset.  (With the plain indices the compiler hoisted
     // the 63 column addresses of M, which lie past the 64 KiB reach of the offset field,
     // out of the chunk loop, and spilled.)
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int pq = ln & 7, cq = 16 * (wave - 4) + 2 * (ln >> 3);
-    const float *mcol = &sm.mp[0][0] + 8 * pq;      // + s * SFS + 4g: M[8u + p][s], u = 4g .. 4g + 3
-    const float *rrow = &sm.rhs[0][0] + pq * SFS + cq;  // + 8u * SFS: RHS[8u + p][col, col + 1]
+    const int pq = ln & 15, cq = 16 * (wave - 4) + 4 * (ln >> 4);
+    const float *mcol = &sm.mp[0][0] + 4 * pq;          // + s * SFS: M[16u + p][s], u = 0..3
+    const float *rrow = &sm.rhs[0][0] + pq * SFS + cq;  // + 16u * SFS: RHS[16u + p][col .. col + 3]
     uint16_t *shi = &sm.sat[0][0][0] + cq * RS + pq, *slo = &sm.sat[1][0][0] + cq * RS + pq;
-    float R0[8], R1[8];  // columns col, col + 1 of rows 8u + p
+    float R[4][4];  // [u][c]: row 16u + p, column col + c
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float2 r2 = *reinterpret_cast<const float2 *>(rrow + 8 * u * SFS);
-      R0[u] = r2.x;
-      R1[u] = r2.y;
+    for (int u = 0; u < 4; ++u) {
+      const float4 r4 = *reinterpret_cast<const float4 *>(rrow + 16 * u * SFS);
+      R[u][0] = r4.x; R[u][1] = r4.y; R[u][2] = r4.z; R[u][3] = r4.w;
     }
     constexpr int kPF = 2;
-    float4 mq[kPF][2];
-    auto load_col = [&](auto s_c, float4 *dst) __attribute__((always_inline)) {  // rows 8u + p, u >= s / 8
+    float4 mq[kPF];
+    static_for<0, kPF>([&](auto s_c) __attribute__((always_inline)) {
       constexpr int s = decltype(s_c)::value;
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-        if (4 * g + 3 >= (s >> 3)) dst[g] = *reinterpret_cast<const float4 *>(mcol + s * SFS + 4 * g);
-    };
-    static_for<0, kPF>([&](auto s_c) __attribute__((always_inline)) { load_col(s_c, mq[decltype(s_c)::value]); });
+      mq[s] = *reinterpret_cast<const float4 *>(mcol + s * SFS);
+    });
     static_for<0, L - 1>([&](auto s_c) __attribute__((always_inline)) {
-      constexpr int s = decltype(s_c)::value, us = s >> 3, q = s & 7;
-      // row s reaches lanes 8m .. 8m + 7 from lane 8m + q: a quad broadcast inside each quad,
-      // then the other quad takes the mirrored lane's copy
-      const float v0 = bcast4_c<q & 3>(R0[us]), v1 = bcast4_c<q & 3>(R1[us]);
-      const float w0 = mirror8(v0), w1 = mirror8(v1);
-      const bool own = upper_quad == (q >= 4);
-      const float x0 = own ? v0 : w0, x1 = own ? v1 : w1;
-      float mv[8];
+      constexpr int s = decltype(s_c)::value, us = s >> 4, q = s & 15;
+      float x[4];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        mv[4 * g] = mq[s % kPF][g].x; mv[4 * g + 1] = mq[s % kPF][g].y;
-        mv[4 * g + 2] = mq[s % kPF][g].z; mv[4 * g + 3] = mq[s % kPF][g].w;
-      }
-      if constexpr (s + kPF < L - 1) load_col(std::integral_constant<int, s + kPF>{}, mq[s % kPF]);
+      for (int c = 0; c < 4; ++c) x[c] = bcast16_c<q>(R[us][c]);
+      const float4 m4 = mq[s % kPF];
+      const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+      if constexpr (s + kPF < L - 1) mq[s % kPF] = *reinterpret_cast<const float4 *>(mcol + (s + kPF) * SFS);
 #pragma unroll
-      for (int u = us; u < 8; ++u) {
-        R0[u] = fmaf(mv[u], x0, R0[u]);
-        R1[u] = fmaf(mv[u], x1, R1[u]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = us; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) R[u][c] = fmaf(mv[u], x[c], R[u][c]);
     });
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // SA^T[col (+1)][8u + p] as bf16 hi / lo
-      uint16_t hi = bf16_bits(R0[u]);
-      shi[8 * u] = hi;
-      slo[8 * u] = bf16_bits(R0[u] - __uint_as_float((uint32_t)hi << 16));
-      hi = bf16_bits(R1[u]);
-      shi[RS + 8 * u] = hi;
-      slo[RS + 8 * u] = bf16_bits(R1[u] - __uint_as_float((uint32_t)hi << 16));
-    }
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {  // SA^T[col + c][16u + p] as bf16 hi / lo
+        const uint16_t hi = bf16_bits(R[u][c]);
+        shi[c * RS + 16 * u] = hi;
+        slo[c * RS + 16 * u] = bf16_bits(R[u][c] - __uint_as_float((uint32_t)hi << 16));
+      }
   };
 
   auto state_c = [&]() __attribute__((always_inline)) {
