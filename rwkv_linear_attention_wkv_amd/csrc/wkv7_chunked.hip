@@ -82,11 +82,13 @@ struct alignas(16) Smem7 {
   // the banks
   float rhs[L][SFS];           // RHS [token][col]; with mp: the fp32 state of a direct chunk
   float mp[L][SFS];            // M[16u + p][s] at [s][4 p + u] (column s of M for the solve)
+  uint16_t mlo[2][32][40];     // M[32 + t][s], s < 32, as bf16 hi / lo [t][s]
   float pl[kHead];             // 2^P_{L-1} per key row
   float2 wtot[8][32];          // log2-decay total of each wave, per channel pair
   int direct;
 };
 static_assert(sizeof(float) * kHead * SFS <= sizeof(float) * 2 * L * SFS, "direct state fits");
+static_assert(sizeof(Smem7) <= 160 * 1024, "one workgroup's LDS");
 
 // Lane (lane & ~3) | q to the four lanes of its quad (DPP quad permute); q must fold to a
 // constant.
@@ -429,10 +431,20 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
         mm_keys(mm, &sm.op[AB][32 * tb + l32][0], &sm.op[AB + 1][32 * tb + l32][0], &sm.op[BT][32 * sb + l32][0],
                 &sm.op[BT + 1][32 * sb + l32][0]);
         const int s = 32 * sb + l32;
+        if (wave != 5) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int t = 32 * tb + 8 * (e >> 2) + 4 * hh + (e & 3);
-          sm.mp[s][4 * (t & 15) + (t >> 4)] = s < t ? mm[e] : 0.f;
+          for (int e = 0; e < 16; ++e) {
+            const int t = 32 * tb + 8 * (e >> 2) + 4 * hh + (e & 3);
+            sm.mp[s][4 * (t & 15) + (t >> 4)] = s < t ? mm[e] : 0.f;
+          }
+        } else {  // block (1, 0) as bf16 hi / lo only: the solve adds it on the matrix cores
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int t = 8 * (e >> 2) + 4 * hh + (e & 3);
+            const uint16_t hi = bf16_bits(mm[e]);
+            sm.mlo[0][t][l32] = hi;
+            sm.mlo[1][t][l32] = bf16_bits(mm[e] - __uint_as_float((uint32_t)hi << 16));
+          }
         }
       }
     }
@@ -443,7 +455,9 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
   // (u = 0..3), which start as RHS; once row s is final, its owner hands SA[s] to the
   // sixteen lanes of its DPP row in one broadcast per column, and each adds M[t][s] SA[s]
   // to its later rows.  The lanes of one row residue read the same column of M, four
-  // values per step.  Column s of M is read kPF steps ahead.
+  // values per step; column s is read kPF steps ahead.  In two halves: rows 0..31 first,
+  // then rows 32..63 receive the sum over s < 32 as one product on the matrix cores
+  // (M's block below the diagonal as bf16 hi / lo against SA^T), then rows 32..63.
   auto solve = [&]() __attribute__((always_inline)) {
     // Per-lane bases formed here from an opaque copy of the lane index: every access below
     // is one of them plus a constant offset.  (With the plain indices the compiler hoisted
@@ -451,9 +465,10 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
     // out of the chunk loop, and spilled.)
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int pq = ln & 15, cq = 16 * (wave - 4) + 4 * (ln >> 4);
+    const int sw = wave - 4;
+    const int pq = ln & 15, cq = 16 * sw + 4 * (ln >> 4);
     const float *mcol = &sm.mp[0][0] + 4 * pq;          // + s * SFS: M[16u + p][s], u = 0..3
-    const float *rrow = &sm.rhs[0][0] + pq * SFS + cq;  // + 16u * SFS: RHS[16u + p][col .. col + 3]
+    float *rrow = &sm.rhs[0][0] + pq * SFS + cq;        // + 16u * SFS: RHS[16u + p][col .. col + 3]
     uint16_t *shi = &sm.sat[0][0][0] + cq * RS + pq, *slo = &sm.sat[1][0][0] + cq * RS + pq;
     float R[4][4];  // [u][c]: row 16u + p, column col + c
 #pragma unroll
@@ -463,31 +478,67 @@ __global__ void __launch_bounds__(kThreads) wkv7_chunked_kernel(V7Params p) {
     }
     constexpr int kPF = 2;
     float4 mq[kPF];
-    static_for<0, kPF>([&](auto s_c) __attribute__((always_inline)) {
-      constexpr int s = decltype(s_c)::value;
-      mq[s] = *reinterpret_cast<const float4 *>(mcol + s * SFS);
-    });
-    static_for<0, L - 1>([&](auto s_c) __attribute__((always_inline)) {
-      constexpr int s = decltype(s_c)::value, us = s >> 4, q = s & 15;
-      float x[4];
+    auto steps = [&](auto s0_c, auto s1_c) __attribute__((always_inline)) {  // rows s0 .. s1 - 1 final
+      constexpr int S0 = decltype(s0_c)::value, S1 = decltype(s1_c)::value, UE = (S1 + 15) / 16;
+      static_for<S0, S0 + kPF>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int s = decltype(s_c)::value;
+        mq[s % kPF] = *reinterpret_cast<const float4 *>(mcol + s * SFS);
+      });
+      static_for<S0, S1>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int s = decltype(s_c)::value, us = s >> 4, q = s & 15;
+        float x[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) x[c] = bcast16_c<q>(R[us][c]);
-      const float4 m4 = mq[s % kPF];
-      const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
-      if constexpr (s + kPF < L - 1) mq[s % kPF] = *reinterpret_cast<const float4 *>(mcol + (s + kPF) * SFS);
+        for (int c = 0; c < 4; ++c) x[c] = bcast16_c<q>(R[us][c]);
+        const float4 m4 = mq[s % kPF];
+        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+        if constexpr (s + kPF < S1) mq[s % kPF] = *reinterpret_cast<const float4 *>(mcol + (s + kPF) * SFS);
 #pragma unroll
-      for (int u = us; u < 4; ++u)
+        for (int u = us; u < UE; ++u)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) R[u][c] = fmaf(mv[u], x[c], R[u][c]);
-    });
+          for (int c = 0; c < 4; ++c) R[u][c] = fmaf(mv[u], x[c], R[u][c]);
+      });
+    };
+    auto store_rows = [&](int u0) __attribute__((always_inline)) {  // SA^T[col + c][16u + p], u = u0, u0 + 1
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = u0; u < u0 + 2; ++u)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {  // SA^T[col + c][16u + p] as bf16 hi / lo
-        const uint16_t hi = bf16_bits(R[u][c]);
-        shi[c * RS + 16 * u] = hi;
-        slo[c * RS + 16 * u] = bf16_bits(R[u][c] - __uint_as_float((uint32_t)hi << 16));
+        for (int c = 0; c < 4; ++c) {
+          const uint16_t hi = bf16_bits(R[u][c]);
+          shi[c * RS + 16 * u] = hi;
+          slo[c * RS + 16 * u] = bf16_bits(R[u][c] - __uint_as_float((uint32_t)hi << 16));
+        }
+    };
+    steps(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{});
+    store_rows(0);
+    asm volatile("" ::: "memory");  // the product below reads those rows
+    {
+      // rows 32..63 += M[32.., 0..31] SA[0..31] for the 32 columns 32 (sw / 2) .. +31 (the
+      // other wave's 16 of them are not final yet and are dropped); through this wave's own
+      // columns of the RHS rows 32..63 back to the solve layout
+      const int cb = 32 * (sw >> 1);
+      f32x16 acc = {};
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int k = 16 * kq + 8 * hh;
+        const bf16x8 ah = ld8(&sm.mlo[0][l32][k]), al = ld8(&sm.mlo[1][l32][k]);
+        const bf16x8 bh = ld8(&sm.sat[0][cb + l32][k]), bl = ld8(&sm.sat[1][cb + l32][k]);
+        acc = mfma32(ah, bh, acc);
+        acc = mfma32(al, bh, acc);
+        acc = mfma32(ah, bl, acc);
       }
+      if ((l32 >> 4) == (sw & 1)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sm.rhs[32 + 8 * (e >> 2) + 4 * hh + (e & 3)][cb + l32] = acc[e];
+      }
+      asm volatile("" ::: "memory");  // one wave's LDS accesses complete in order
+#pragma unroll
+      for (int u = 2; u < 4; ++u) {
+        const float4 r4 = *reinterpret_cast<const float4 *>(rrow + 16 * u * SFS);
+        R[u][0] += r4.x; R[u][1] += r4.y; R[u][2] += r4.z; R[u][3] += r4.w;
+      }
+    }
+    steps(std::integral_constant<int, 32>{}, std::integral_constant<int, L - 1>{});
+    store_rows(2);
   };
 
   auto state_c = [&]() __attribute__((always_inline)) {
